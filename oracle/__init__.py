@@ -1,0 +1,206 @@
+"""Python binding of the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this module. The HIP product path never does, and this module imports nothing from
+the product package.
+
+Inputs are CPU tensors or numpy arrays holding bf16 bit patterns (uint16) or float32 tables;
+outputs are float64 numpy arrays, unrounded, plus the encoders that turn them into bf16 bits and
+OCP E4M3 codes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCE = os.path.join(_HERE, "oracle.c")
+
+NORM_MODES = {"none": 0, "per_head": 1, "across_heads": 2}
+TABLE_BF16, TABLE_F32, TABLE_F64 = 0, 1, 2
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (portable x86-64, OpenMP)."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+           "-o", tmp, SOURCE, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.oracle_run_table.argtypes = [P, P, P, P, P, I, D, I64, I, I, I, I, I, I,
+                                       I64, I64, I64, P, P]
+        L.oracle_run_table.restype = I
+        L.oracle_run_3d.argtypes = [P, P, P, I64, I64, I, I, I, I, I, I, I, I, I, I,
+                                    D, D, I, D, D, D, D, I, P, P, P]
+        L.oracle_run_3d.restype = I
+        L.oracle_bf16_encode.argtypes = [D]
+        L.oracle_bf16_encode.restype = ctypes.c_uint16
+        L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_decode.restype = D
+        L.oracle_e4m3_encode.argtypes = [D]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = D
+        L.oracle_encode_bf16_array.argtypes = [P, I64, P]
+        L.oracle_encode_bf16_array.restype = None
+        L.oracle_quantize_e4m3_array.argtypes = [P, I64, D, P]
+        L.oracle_quantize_e4m3_array.restype = None
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = I
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+# --- array helpers -----------------------------------------------------------------------------
+
+def _bits16(x) -> np.ndarray:
+    """bf16 bit patterns as a C-contiguous uint16 array (accepts torch bf16 or numpy uint16)."""
+    if hasattr(x, "detach"):                       # torch tensor
+        import torch
+        x = x.detach()
+        if x.dtype != torch.bfloat16:
+            raise TypeError(f"expected a bfloat16 tensor, got {x.dtype}")
+        x = x.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError(f"expected uint16 bf16 bits, got {x.dtype}")
+    return x
+
+
+def _table(x):
+    """(array, dtype code) for a rope table: torch bf16/fp32, numpy uint16/float32/float64."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().cpu().contiguous()
+        if x.dtype == torch.float32:
+            return np.ascontiguousarray(x.numpy()), TABLE_F32
+        return _bits16(x), TABLE_BF16
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float64:
+        return x, TABLE_F64
+    if x.dtype == np.float32:
+        return x, TABLE_F32
+    return _bits16(x), TABLE_BF16
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --- the two forms -----------------------------------------------------------------------------
+
+def run_table(q, k, q_weight, k_weight, rope_table, eps, *, rotary_dim=None,
+              interleaved=False, norm_mode="per_head"):
+    """fp64 table form. q [T,Hq,D], k [T,Hk,D] bf16; table [T,R]. Returns (q_out, k_out) fp64."""
+    qb, kb = _bits16(q), _bits16(k)
+    if qb.ndim != 3 or kb.ndim != 3:
+        raise ValueError("q and k must be [tokens, heads, head_dim]")
+    T, Hq, D = qb.shape
+    Hk = kb.shape[1]
+    tab, tdt = _table(rope_table)
+    R = tab.shape[1] if rotary_dim is None else rotary_dim
+    wq = _bits16(q_weight) if q_weight is not None else np.zeros(1, np.uint16)
+    wk = _bits16(k_weight) if k_weight is not None else np.zeros(1, np.uint16)
+    qo = np.empty((T, Hq, D), np.float64)
+    ko = np.empty((T, Hk, D), np.float64)
+    rc = lib().oracle_run_table(_ptr(qb), _ptr(kb), _ptr(wq), _ptr(wk), _ptr(tab), tdt,
+                                float(eps), T, Hq, Hk, D, R, int(bool(interleaved)),
+                                NORM_MODES[norm_mode], Hq * D, Hk * D, tab.shape[1],
+                                _ptr(qo), _ptr(ko))
+    if rc != 0:
+        raise ValueError(f"oracle_run_table rejected its arguments (code {rc})")
+    return qo, ko
+
+
+def run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
+           num_height_channels, num_width_channels, num_heads_q, num_heads_k, num_heads_v,
+           head_dim, eps=1e-6, base=10000.0, interleave=True, factor=1.0, low=0.0, high=0.0,
+           attention_factor=1.0, is_qk_norm=True, token_offset=0):
+    """fp64 3D form over rows of packed qkv. Returns (q, k, v) fp64 [T, H, D], unrounded.
+
+    qkv may be [T, row] or [B, S, row]; token_offset is the flattened index of its first row.
+    """
+    x = _bits16(qkv)
+    row = (num_heads_q + num_heads_k + num_heads_v) * head_dim
+    x = x.reshape(-1, row)
+    T = x.shape[0]
+    D = head_dim
+    wq = _bits16(q_weight) if q_weight is not None else np.zeros(1, np.uint16)
+    wk = _bits16(k_weight) if k_weight is not None else np.zeros(1, np.uint16)
+    qo = np.empty((T, num_heads_q, D), np.float64)
+    ko = np.empty((T, num_heads_k, D), np.float64)
+    vo = np.empty((T, num_heads_v, D), np.float64)
+    rc = lib().oracle_run_3d(_ptr(x), _ptr(wq), _ptr(wk), T, int(token_offset), ppf, pph, ppw,
+                             num_frame_channels, num_height_channels, num_width_channels,
+                             num_heads_q, num_heads_k, num_heads_v, D, float(eps), float(base),
+                             int(bool(interleave)), float(factor), float(low), float(high),
+                             float(attention_factor), int(bool(is_qk_norm)),
+                             _ptr(qo), _ptr(ko), _ptr(vo))
+    if rc != 0:
+        raise ValueError(f"oracle_run_3d rejected its arguments (code {rc})")
+    return qo, ko, vo
+
+
+def run_3d_workload(w, qkv, q_weight, k_weight, token_offset=0):
+    """run_3d with the parameters of a 3D workload description (any object with those fields)."""
+    return run_3d(qkv, q_weight, k_weight, ppf=w.ppf, pph=w.pph, ppw=w.ppw,
+                  num_frame_channels=w.num_frame_channels,
+                  num_height_channels=w.num_height_channels,
+                  num_width_channels=w.num_width_channels, num_heads_q=w.num_heads_q,
+                  num_heads_k=w.num_heads_k, num_heads_v=w.num_heads_v, head_dim=w.head_dim,
+                  eps=w.eps, base=w.base, interleave=w.interleave, factor=w.factor, low=w.low,
+                  high=w.high, attention_factor=w.attention_factor, is_qk_norm=w.is_qk_norm,
+                  token_offset=token_offset)
+
+
+# --- encoders ----------------------------------------------------------------------------------
+
+def bf16_encode(x) -> np.ndarray:
+    """Round-to-nearest-even bf16 bit patterns of an fp64 array."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, np.uint16)
+    lib().oracle_encode_bf16_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def bf16_decode(bits) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e4m3_encode(x, scale: float = 1.0) -> np.ndarray:
+    """OCP E4M3 codes of x*scale (RNE, saturating to +-448, NaN kept)."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, np.uint8)
+    lib().oracle_quantize_e4m3_array(_ptr(a), a.size, float(scale), _ptr(out))
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    f = lib().oracle_e4m3_decode
+    table = np.array([f(i) for i in range(256)], dtype=np.float64)
+    return table[c]

@@ -1,0 +1,364 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for the fused QK-RMSNorm + RoPE (+ V) prologue.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the benchmark's
+ * CPU-baseline leg load this library. It shares no code, header, table or helper with the HIP
+ * path, and the HIP path never calls it.
+ *
+ * What it follows (the pages, cited by title and section):
+ *   [table form] vLLM-Omni API docs, "vllm_omni.diffusion.layers.fused_qk_norm_rope",
+ *       module contract: q/k are [tokens, heads, head_dim]; the norm weights are [head_dim];
+ *       rope_table is [tokens, rotary_dim] holding [cos(theta) | sin(theta)], theta of width
+ *       rotary_dim/2, in the activation dtype or float32; interleaved=False rotates the pairs
+ *       (d, d + rotary_dim/2), interleaved=True the adjacent pairs (2i, 2i+1) by theta_i.
+ *       The fused path materialises no normalised or rotated intermediates.
+ *   [3D form] FlashInfer API docs, "flashinfer.norm.fused_qk_rmsnorm_rope", description and
+ *       parameter list: across-heads RMSNorm of Q and K (weights [heads*head_dim]); RoPE with a
+ *       frame/height/width decomposition (seq_len = ppf*pph*ppw, channel counts per axis that
+ *       sum to head_dim, frequency base); interleave=True for adjacent pairs, False for NeoX;
+ *       YaRN factor/low/high and an attention factor applied to cos and sin; is_qk_norm=False
+ *       skips the norm; V is copied out of packed QKV; optional FP8 E4M3 outputs with one scale
+ *       for Q and K and one for V.
+ *
+ * Where the pages leave a step open, the reading taken is stated next to the code:
+ *   - RMSNorm: n = x * (mean(x^2) + eps)^(-1/2) * w, eps inside the root, w multiplied directly.
+ *   - rotation by +theta: a' = a*cos - b*sin, b' = b*cos + a*sin.
+ *   - dims at or beyond rotary_dim are normalised but not rotated.
+ *   - 3D positions are frame-major (width fastest); token t of a flattened batch is position
+ *     t mod seq_len. The frequency vector of length head_dim/2 is the concatenation of the frame,
+ *     height and width blocks; block pair j has omega = base^(-2j/C_axis). NeoX pairs (k, k+D/2)
+ *     across that whole vector.
+ *   - YaRN: per axis, ramp rho = clamp((j - low)/(high - low), 0, 1) over the block pair index,
+ *     omega' = (omega/factor)*rho + omega*(1 - rho) (the published YaRN blend of interpolated and
+ *     original frequencies); cos and sin are then multiplied by attention_factor.
+ *   - FP8: OCP E4M3 (bias 7, max 448, no infinities, NaN = S.1111.111), round to nearest even,
+ *     value multiplied by its scale, finite overflow saturates to +-448.
+ *
+ * Everything is computed in double from the exact decoded inputs and rounded once at the output.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_OK = 0, ORACLE_BAD_ARG = 1, ORACLE_NO_MEMORY = 2 };
+enum { ORACLE_NORM_NONE = 0, ORACLE_NORM_PER_HEAD = 1, ORACLE_NORM_ACROSS_HEADS = 2 };
+/* Table dtypes: the pages allow the activation dtype (bf16) or float32. F64 is a test-only
+ * extension that lets the table form be compared exactly with the 3D form. */
+enum { ORACLE_TABLE_BF16 = 0, ORACLE_TABLE_F32 = 1, ORACLE_TABLE_F64 = 2 };
+
+/* ---------------------------------------------------------------------------------------------
+ * Number formats.
+ * bf16 is the upper half of an IEEE-754 binary32; decoding is exact.
+ * ------------------------------------------------------------------------------------------- */
+double oracle_bf16_decode(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+double oracle_f32_decode(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round |a| (finite, > 0) to a binary grid with `prec` significant bits whose smallest normal
+ * binade starts at 2^emin (below it the quantum stays 2^(emin - prec + 1)). Ties go to even:
+ * rint() runs in the default round-to-nearest-even mode, and a/quantum is exact because the
+ * quantum is a power of two. */
+static double round_to_grid(double a, int prec, int emin)
+{
+    int e;
+    frexp(a, &e);               /* a = m * 2^e, m in [0.5, 1): leading bit has weight 2^(e-1) */
+    int lead = e - 1;
+    if (lead < emin) lead = emin;
+    double quantum = ldexp(1.0, lead - (prec - 1));
+    return rint(a / quantum) * quantum;
+}
+
+/* bf16 round-to-nearest-even of an fp64 value (8 significant bits, exponent range of binary32).
+ * Overflow rounds to infinity; NaN becomes a quiet NaN with its sign. */
+uint16_t oracle_bf16_encode(double x)
+{
+    if (isnan(x)) return signbit(x) ? 0xFFC0 : 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    double r = round_to_grid(a, 8, -126);
+    double max_finite = ldexp(255.0, 120);          /* (2 - 2^-7) * 2^127 */
+    if (r > max_finite) return sign | 0x7F80;
+    float f = (float)r;                             /* exact: r is on the bf16 grid */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; normal binades
+ * 2^-6 .. 2^8, subnormal quantum 2^-9, largest finite 448 = 1.75 * 2^8, no infinities, and
+ * S.1111.111 is NaN. */
+uint8_t oracle_e4m3_encode(double x)
+{
+    if (isnan(x)) return signbit(x) ? 0xFF : 0x7F;
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a > 448.0) a = 448.0;                       /* saturate (also maps +-inf to +-448) */
+    if (a == 0.0) return sign;
+    double r = round_to_grid(a, 4, -6);
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -6)) {                       /* subnormal: mantissa counts 2^-9 steps */
+        return (uint8_t)(sign | (int)(r / ldexp(1.0, -9)));
+    }
+    int e;
+    frexp(r, &e);
+    int lead = e - 1;                               /* r in [2^lead, 2^(lead+1)) */
+    int mant = (int)((r / ldexp(1.0, lead) - 1.0) * 8.0);
+    return (uint8_t)(sign | ((lead + 7) << 3) | mant);
+}
+
+double oracle_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7, E = (c >> 3) & 15, M = c & 7;
+    double v;
+    if (E == 15 && M == 7) return s ? -NAN : NAN;
+    if (E == 0) v = ldexp((double)M, -9);
+    else v = ldexp(1.0 + M / 8.0, E - 7);
+    return s ? -v : v;
+}
+
+void oracle_encode_bf16_array(const double *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_encode(x[i]);
+}
+
+/* FP8 output of the 3D form: code = e4m3(value * scale). */
+void oracle_quantize_e4m3_array(const double *x, int64_t n, double scale, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i] * scale);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * RMSNorm: the reciprocal root mean square of n values, (mean(x^2) + eps)^(-1/2).
+ * ------------------------------------------------------------------------------------------- */
+static double inv_rms(const double *x, int64_t n, double eps)
+{
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; ++i) sum += x[i] * x[i];
+    return 1.0 / sqrt(sum / (double)n + eps);
+}
+
+/* Normalise one token's [H, D] block x in place. PER_HEAD: one scale per head, weight w[d].
+ * ACROSS_HEADS: one scale for the whole H*D row, weight w[h*D + d]. NONE: unchanged. */
+static void normalise_token(double *x, int H, int D, int norm_mode, const uint16_t *w, double eps)
+{
+    if (norm_mode == ORACLE_NORM_PER_HEAD) {
+        for (int h = 0; h < H; ++h) {
+            double r = inv_rms(x + (int64_t)h * D, D, eps);
+            for (int d = 0; d < D; ++d)
+                x[h * D + d] = x[h * D + d] * r * oracle_bf16_decode(w[d]);
+        }
+    } else if (norm_mode == ORACLE_NORM_ACROSS_HEADS) {
+        double r = inv_rms(x, (int64_t)H * D, eps);
+        for (int i = 0; i < H * D; ++i)
+            x[i] = x[i] * r * oracle_bf16_decode(w[i]);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Table form.
+ * q: [T, Hq, D] bf16 with token stride q_stride (elements); k likewise. rope_table: [T, R]
+ * with token stride table_stride, dtype bf16, f32 (or f64 for tests). Outputs: fp64 [T, H, D], unrounded.
+ * norm_mode PER_HEAD is the pages' contract ([head_dim] weights); NONE and ACROSS_HEADS
+ * (weights [H*D]) are extensions used to relate the table form to the 3D form.
+ * ------------------------------------------------------------------------------------------- */
+static double table_value(const void *table, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_TABLE_F64) return ((const double *)table)[idx];
+    if (dtype == ORACLE_TABLE_F32) return oracle_f32_decode(((const uint32_t *)table)[idx]);
+    return oracle_bf16_decode(((const uint16_t *)table)[idx]);
+}
+
+static void table_token(const uint16_t *src, int H, int D, int R, int interleaved,
+                        int norm_mode, const uint16_t *w, double eps,
+                        const void *table, int dtype, int64_t trow, double *out, double *n)
+{
+    for (int i = 0; i < H * D; ++i) n[i] = oracle_bf16_decode(src[i]);
+    normalise_token(n, H, D, norm_mode, w, eps);
+    for (int h = 0; h < H; ++h) {
+        const double *nh = n + (int64_t)h * D;
+        double *oh = out + (int64_t)h * D;
+        for (int d = 0; d < D; ++d) oh[d] = nh[d];            /* dims >= R pass through */
+        for (int i = 0; i < R / 2; ++i) {
+            double c = table_value(table, dtype, trow + i);
+            double s = table_value(table, dtype, trow + R / 2 + i);
+            int a = interleaved ? 2 * i : i;
+            int b = interleaved ? 2 * i + 1 : i + R / 2;
+            oh[a] = nh[a] * c - nh[b] * s;
+            oh[b] = nh[b] * c + nh[a] * s;
+        }
+    }
+}
+
+int oracle_run_table(const uint16_t *q, const uint16_t *k,
+                     const uint16_t *q_weight, const uint16_t *k_weight,
+                     const void *rope_table, int table_dtype, double eps,
+                     int64_t num_tokens, int num_heads_q, int num_heads_k, int head_dim,
+                     int rotary_dim, int interleaved, int norm_mode,
+                     int64_t q_stride, int64_t k_stride, int64_t table_stride,
+                     double *q_out, double *k_out)
+{
+    if (num_tokens < 0 || num_heads_q < 0 || num_heads_k < 0 || head_dim <= 0) return ORACLE_BAD_ARG;
+    if (rotary_dim < 0 || rotary_dim > head_dim || rotary_dim % 2) return ORACLE_BAD_ARG;
+    if (norm_mode < 0 || norm_mode > 2) return ORACLE_BAD_ARG;
+    if (table_dtype != ORACLE_TABLE_BF16 && table_dtype != ORACLE_TABLE_F32 &&
+        table_dtype != ORACLE_TABLE_F64)
+        return ORACLE_BAD_ARG;
+    int D = head_dim, R = rotary_dim;
+    int Hmax = num_heads_q > num_heads_k ? num_heads_q : num_heads_k;
+    int64_t T = num_tokens;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *scratch = (double *)malloc(sizeof(double) * ((size_t)Hmax * D + 1));
+        if (!scratch) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            if (!scratch) continue;
+            table_token(q + t * q_stride, num_heads_q, D, R, interleaved, norm_mode, q_weight,
+                        eps, rope_table, table_dtype, t * table_stride,
+                        q_out + t * num_heads_q * D, scratch);
+            table_token(k + t * k_stride, num_heads_k, D, R, interleaved, norm_mode, k_weight,
+                        eps, rope_table, table_dtype, t * table_stride,
+                        k_out + t * num_heads_k * D, scratch);
+        }
+        free(scratch);
+    }
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * 3D form.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Position of sequence index s on the (frame, height, width) grid, frame-major. */
+static void grid_position(int64_t s, int pph, int ppw, int64_t pos[3])
+{
+    pos[0] = s / ((int64_t)pph * ppw);
+    pos[1] = (s / ppw) % pph;
+    pos[2] = s % ppw;
+}
+
+/* cos/sin (times attention_factor) of pair k of the head_dim/2-long frequency vector. */
+static void pair_angle(int k, const int64_t pos[3], const int C[3], double base, double factor,
+                       double low, double high, double attention_factor, double *c, double *s)
+{
+    int axis = 0, j = k;
+    while (j >= C[axis] / 2) {          /* blocks: frame C[0]/2 pairs, height, then width */
+        j -= C[axis] / 2;
+        ++axis;
+    }
+    double omega = pow(base, -2.0 * j / (double)C[axis]);
+    if (factor != 1.0) {
+        double rho = (j - low) / (high - low);
+        if (rho < 0.0) rho = 0.0;
+        if (rho > 1.0) rho = 1.0;
+        omega = (omega / factor) * rho + omega * (1.0 - rho);
+    }
+    double theta = (double)pos[axis] * omega;
+    *c = cos(theta) * attention_factor;
+    *s = sin(theta) * attention_factor;
+}
+
+static void rope3d_region(const uint16_t *src, int H, int D, int interleave, int norm,
+                          const uint16_t *w, double eps, const double *cs_c, const double *cs_s,
+                          double *out, double *n)
+{
+    for (int i = 0; i < H * D; ++i) n[i] = oracle_bf16_decode(src[i]);
+    normalise_token(n, H, D, norm ? ORACLE_NORM_ACROSS_HEADS : ORACLE_NORM_NONE, w, eps);
+    for (int h = 0; h < H; ++h) {
+        const double *nh = n + (int64_t)h * D;
+        double *oh = out + (int64_t)h * D;
+        for (int k = 0; k < D / 2; ++k) {
+            int a = interleave ? 2 * k : k;
+            int b = interleave ? 2 * k + 1 : k + D / 2;
+            oh[a] = nh[a] * cs_c[k] - nh[b] * cs_s[k];
+            oh[b] = nh[b] * cs_c[k] + nh[a] * cs_s[k];
+        }
+    }
+}
+
+/* qkv: rows of (Hq+Hk+Hv)*D bf16 for tokens token_offset .. token_offset+num_tokens-1 of a
+ * flattened [B*S] sequence (the offset lets a caller check a slice of a long input). Outputs are
+ * fp64 [num_tokens, H, D], unrounded; V is the decoded input. */
+int oracle_run_3d(const uint16_t *qkv, const uint16_t *q_weight, const uint16_t *k_weight,
+                  int64_t num_tokens, int64_t token_offset,
+                  int ppf, int pph, int ppw,
+                  int num_frame_channels, int num_height_channels, int num_width_channels,
+                  int num_heads_q, int num_heads_k, int num_heads_v, int head_dim,
+                  double eps, double base, int interleave, double factor, double low,
+                  double high, double attention_factor, int is_qk_norm,
+                  double *q_out, double *k_out, double *v_out)
+{
+    int C[3] = {num_frame_channels, num_height_channels, num_width_channels};
+    int D = head_dim;
+    if (ppf <= 0 || pph <= 0 || ppw <= 0 || D <= 0 || D % 2) return ORACLE_BAD_ARG;
+    if (num_tokens < 0 || token_offset < 0) return ORACLE_BAD_ARG;
+    for (int a = 0; a < 3; ++a)
+        if (C[a] < 0 || C[a] % 2) return ORACLE_BAD_ARG;
+    if (C[0] + C[1] + C[2] != D) return ORACLE_BAD_ARG;
+    if (factor != 1.0 && !(high > low)) return ORACLE_BAD_ARG;
+    if (factor == 1.0 && attention_factor != 1.0) return ORACLE_BAD_ARG;
+    int Hq = num_heads_q, Hk = num_heads_k, Hv = num_heads_v;
+    int64_t row = (int64_t)(Hq + Hk + Hv) * D;
+    int64_t S = (int64_t)ppf * pph * ppw;
+    int Hmax = Hq > Hk ? Hq : Hk;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *scratch = (double *)malloc(sizeof(double) * ((size_t)Hmax * D + (size_t)D + 2));
+        if (!scratch) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        double *cs_c = scratch ? scratch + (size_t)Hmax * D : NULL;
+        double *cs_s = scratch ? cs_c + D / 2 + 1 : NULL;
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < num_tokens; ++i) {
+            if (!scratch) continue;
+            int64_t pos[3];
+            grid_position((token_offset + i) % S, pph, ppw, pos);
+            for (int k = 0; k < D / 2; ++k)
+                pair_angle(k, pos, C, base, factor, low, high, attention_factor,
+                           &cs_c[k], &cs_s[k]);
+            const uint16_t *src = qkv + i * row;
+            rope3d_region(src, Hq, D, interleave, is_qk_norm, q_weight, eps, cs_c, cs_s,
+                          q_out + i * Hq * D, scratch);
+            rope3d_region(src + (int64_t)Hq * D, Hk, D, interleave, is_qk_norm, k_weight, eps,
+                          cs_c, cs_s, k_out + i * Hk * D, scratch);
+            for (int64_t e = 0; e < (int64_t)Hv * D; ++e)
+                v_out[i * Hv * D + e] = oracle_bf16_decode(src[(int64_t)(Hq + Hk) * D + e]);
+        }
+        free(scratch);
+    }
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* Threads an OpenMP parallel region of this library will use. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,203 @@
+"""Seeded synthetic workloads for the fused QK-RMSNorm + RoPE (+ V) prologue.
+
+This module only draws inputs: shapes, seeds and value distributions. It holds none of the
+prologue's arithmetic (no normalisation, no rotation, no quantisation), so the HIP path and the
+fp64 oracle can both consume its arrays without sharing any method code.
+
+Workload shapes follow the two API pages the prologue is built from:
+  * vLLM-Omni "vllm_omni.diffusion.layers.fused_qk_norm_rope" (table form): q and k are
+    [tokens, heads, head_dim], norm weights are [head_dim], the rope table is
+    [tokens, rotary_dim] holding [cos(theta) | sin(theta)] in the activation dtype or float32.
+  * FlashInfer "flashinfer.norm.fused_qk_rmsnorm_rope" (3D form): packed bf16 QKV
+    [batch, seq_len, (Hq+Hk+Hv)*head_dim] with seq_len = ppf*pph*ppw, weights [H*head_dim].
+
+Value recipe (stated once, used everywhere):
+  * activations: numpy PCG64(seed).standard_normal in float32, times sigma, rounded to bf16 (RNE);
+  * norm weights: 1 + 0.1*N(0,1) drawn in float64, rounded to float32 then bf16 (RNE);
+  * rope table (table form only): theta_i = t * base**(-2i/rotary_dim) for token t, cos/sin taken
+    in float64 and rounded to float32 (and then to bf16 for a bf16 table). The table is an input
+    of the table form; the pages leave its contents to the caller.
+Every array is dense and contiguous, with no padding and no special values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+SEED_BASE = 20261203
+_CHUNK = 1 << 24  # elements drawn per PCG64 call when filling large activations
+
+# Role offsets added to a workload's seed, so each input has its own stream.
+ROLE_QKV = 0   # packed qkv (3D form) or q (table form)
+ROLE_K = 1     # k (table form)
+ROLE_WQ = 2
+ROLE_WK = 3
+
+
+@dataclass(frozen=True)
+class TableWorkload:
+    """Table-form problem: q, k [T, H, D] bf16; table [T, R] fp32 or bf16."""
+    name: str
+    num_tokens: int
+    num_heads_q: int
+    num_heads_k: int
+    head_dim: int
+    rotary_dim: int
+    interleaved: bool
+    table_dtype: str          # "f32" or "bf16"
+    seed: int
+    eps: float = 1e-6
+    base: float = 10000.0
+    sigma: float = 1.0
+    norm_mode: str = "per_head"   # "none" | "per_head" | "across_heads"
+
+    def with_(self, **kw) -> "TableWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclass(frozen=True)
+class Rope3DWorkload:
+    """3D-form problem: packed bf16 qkv [B, S, (Hq+Hk+Hv)*D], S = ppf*pph*ppw."""
+    name: str
+    batch: int
+    ppf: int
+    pph: int
+    ppw: int
+    num_frame_channels: int
+    num_height_channels: int
+    num_width_channels: int
+    num_heads_q: int
+    num_heads_k: int
+    num_heads_v: int
+    head_dim: int
+    seed: int
+    eps: float = 1e-6
+    base: float = 10000.0
+    interleave: bool = True
+    factor: float = 1.0
+    low: float = 0.0
+    high: float = 0.0
+    attention_factor: float = 1.0
+    is_qk_norm: bool = True
+    output_fp8: bool = False
+    output_quant_scale: float = 1.0
+    v_quant_scale: float = 1.0
+    sigma: float = 1.0
+
+    @property
+    def seq_len(self) -> int:
+        return self.ppf * self.pph * self.ppw
+
+    @property
+    def num_tokens(self) -> int:
+        return self.batch * self.seq_len
+
+    @property
+    def row_elems(self) -> int:
+        return (self.num_heads_q + self.num_heads_k + self.num_heads_v) * self.head_dim
+
+    def with_(self, **kw) -> "Rope3DWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# --- the five named workloads ------------------------------------------------------------------
+
+# MiniMax-H3 geometry of the table form's half-split kernel (head_dim 128, rotary_dim 96).
+TABLE_HALFSPLIT_T256 = TableWorkload(
+    name="table_halfsplit_t256_h4_d128_r96_f32table", num_tokens=256, num_heads_q=4,
+    num_heads_k=4, head_dim=128, rotary_dim=96, interleaved=False, table_dtype="f32",
+    seed=SEED_BASE + 10)
+
+# Boogu-Image style interleaved table form.
+TABLE_INTERLEAVED_T4096 = TableWorkload(
+    name="table_interleaved_t4096_h24_d128_bf16table", num_tokens=4096, num_heads_q=24,
+    num_heads_k=24, head_dim=128, rotary_dim=128, interleaved=True, table_dtype="bf16",
+    seed=SEED_BASE + 20)
+
+# LTX-2 video self-attention shape: 15360 tokens, 32 heads of 128.
+ROPE3D_ACROSS_S15360 = Rope3DWorkload(
+    name="rope3d_across_interleaved_s15360_h32_d128", batch=1, ppf=16, pph=24, ppw=40,
+    num_frame_channels=16, num_height_channels=56, num_width_channels=56,
+    num_heads_q=32, num_heads_k=32, num_heads_v=32, head_dim=128, seed=SEED_BASE + 30)
+
+# SANA-WM's 18480-token grid, NeoX pairing, FP8 E4M3 outputs.
+ROPE3D_NEOX_FP8_S18480 = Rope3DWorkload(
+    name="rope3d_neox_fp8_b2_s18480_h20_d64", batch=2, ppf=20, pph=33, ppw=28,
+    num_frame_channels=16, num_height_channels=24, num_width_channels=24,
+    num_heads_q=20, num_heads_k=20, num_heads_v=20, head_dim=64, seed=SEED_BASE + 40,
+    interleave=False, output_fp8=True, output_quant_scale=0.5, v_quant_scale=0.25, sigma=2.0)
+
+# Long-video YaRN, RoPE only.
+ROPE3D_YARN_S122880 = Rope3DWorkload(
+    name="rope3d_yarn_nonorm_s122880_h16_d256", batch=1, ppf=32, pph=48, ppw=80,
+    num_frame_channels=64, num_height_channels=96, num_width_channels=96,
+    num_heads_q=16, num_heads_k=16, num_heads_v=16, head_dim=256, seed=SEED_BASE + 50,
+    factor=4.0, low=1.0, high=32.0, attention_factor=1.0 + 0.1 * float(np.log(4.0)),
+    is_qk_norm=False)
+
+WORKLOADS = {w.name: w for w in (TABLE_HALFSPLIT_T256, TABLE_INTERLEAVED_T4096,
+                                 ROPE3D_ACROSS_S15360, ROPE3D_NEOX_FP8_S18480,
+                                 ROPE3D_YARN_S122880)}
+
+
+# --- drawing -----------------------------------------------------------------------------------
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def bf16_normal(seed: int, n: int, sigma: float = 1.0) -> torch.Tensor:
+    """n draws of sigma*N(0,1) as a flat CPU bfloat16 tensor (float32 draws, RNE to bf16)."""
+    rng = _rng(seed)
+    out = torch.empty(n, dtype=torch.bfloat16)
+    for start in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - start)
+        chunk = rng.standard_normal(m, dtype=np.float32)
+        if sigma != 1.0:
+            chunk *= np.float32(sigma)
+        out[start:start + m] = torch.from_numpy(chunk).to(torch.bfloat16)
+    return out
+
+
+def bf16_weights(seed: int, n: int) -> torch.Tensor:
+    """Norm weights 1 + 0.1*N(0,1), drawn in float64, as a CPU bfloat16 tensor."""
+    w = 1.0 + 0.1 * _rng(seed).standard_normal(n)
+    return torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16)
+
+
+def rope_table(num_tokens: int, rotary_dim: int, base: float, dtype: str) -> torch.Tensor:
+    """[T, R] table: row t = [cos(theta_0..theta_{R/2-1}) | sin(...)], theta_i = t*base^(-2i/R)."""
+    half = rotary_dim // 2
+    inv = base ** (-(2.0 * np.arange(half, dtype=np.float64)) / rotary_dim)
+    theta = np.arange(num_tokens, dtype=np.float64)[:, None] * inv[None, :]
+    tab = np.concatenate([np.cos(theta), np.sin(theta)], axis=1).astype(np.float32)
+    t = torch.from_numpy(np.ascontiguousarray(tab))
+    if dtype == "f32":
+        return t
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    raise ValueError(f"table dtype {dtype!r}")
+
+
+def table_inputs(w: TableWorkload) -> dict:
+    """CPU tensors for a table-form workload: q, k [T,H,D] bf16; weights; table."""
+    T, D = w.num_tokens, w.head_dim
+    q = bf16_normal(w.seed + ROLE_QKV, T * w.num_heads_q * D, w.sigma).view(T, w.num_heads_q, D)
+    k = bf16_normal(w.seed + ROLE_K, T * w.num_heads_k * D, w.sigma).view(T, w.num_heads_k, D)
+    wlen_q = D if w.norm_mode != "across_heads" else w.num_heads_q * D
+    wlen_k = D if w.norm_mode != "across_heads" else w.num_heads_k * D
+    return dict(q=q, k=k,
+                q_weight=bf16_weights(w.seed + ROLE_WQ, wlen_q),
+                k_weight=bf16_weights(w.seed + ROLE_WK, wlen_k),
+                rope_table=rope_table(T, w.rotary_dim, w.base, w.table_dtype))
+
+
+def rope3d_inputs(w: Rope3DWorkload) -> dict:
+    """CPU tensors for a 3D workload: qkv [B, S, (Hq+Hk+Hv)*D] bf16 and the two weights."""
+    qkv = bf16_normal(w.seed + ROLE_QKV, w.num_tokens * w.row_elems, w.sigma)
+    return dict(qkv=qkv.view(w.batch, w.seq_len, w.row_elems),
+                q_weight=bf16_weights(w.seed + ROLE_WQ, w.num_heads_q * w.head_dim),
+                k_weight=bf16_weights(w.seed + ROLE_WK, w.num_heads_k * w.head_dim))
