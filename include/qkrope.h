@@ -1,0 +1,152 @@
+/*
+ * qkrope.h -- C ABI of the fused QK-RMSNorm + RoPE (+ V) attention prologue for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library computes, in one kernel launch per call, the attention prologue of video and
+ * diffusion transformers as two API pages define it:
+ *
+ *   [table form] vLLM-Omni "vllm_omni.diffusion.layers.fused_qk_norm_rope", module contract and
+ *       the fused_qk_norm_rope signature: Q/K RMSNorm with [head_dim] weights, then RoPE from a
+ *       [tokens, rotary_dim] table holding [cos(theta) | sin(theta)] (theta of width
+ *       rotary_dim/2), half-split pairs (d, d + rotary_dim/2) or interleaved pairs (2i, 2i+1).
+ *   [3D form] FlashInfer "flashinfer.norm.fused_qk_rmsnorm_rope", description and parameters:
+ *       across-heads RMSNorm of Q and K, RoPE computed from a frame/height/width decomposition of
+ *       the token index (optionally YaRN-scaled), V copied out of the packed QKV input, and
+ *       optional FP8 E4M3 outputs.
+ *
+ * Conventions shared by every entry point:
+ *   - All functions return a qkrope_status. On any status other than QKROPE_OK nothing has been
+ *     launched, and qkrope_last_error() returns a message for the calling thread.
+ *   - Tensor pointers are DEVICE pointers, owned by the caller. The library never allocates,
+ *     frees, or synchronises on them; it only enqueues work on `stream` (a hipStream_t; NULL is
+ *     the default stream) and returns. A kernel fault therefore surfaces at the caller's next
+ *     synchronisation with that stream.
+ *   - Activations are bf16 (raw 16-bit patterns). Every tensor pointer must be 16-byte aligned
+ *     and every token stride a multiple of 8 elements (one 16-byte chunk), else
+ *     QKROPE_ERR_UNSUPPORTED.
+ *   - Arithmetic is fp32 on the GPU; each output element is rounded once (bf16 round-to-nearest-
+ *     even, or OCP E4M3 round-to-nearest-even with saturation to +-448).
+ *   - A handle is immutable after qkrope_create, so calls on different streams may run
+ *     concurrently from several host threads.
+ */
+#ifndef QKROPE_H
+#define QKROPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qkrope_status {
+    QKROPE_OK = 0,
+    QKROPE_ERR_INVALID = 1,      /* arguments break the pages' contract (shape, divisibility...) */
+    QKROPE_ERR_UNSUPPORTED = 2,  /* valid per the pages but outside this library's kernels
+                                    (alignment, head_dim or head-count limits) */
+    QKROPE_ERR_DEVICE = 3,       /* HIP runtime error: device query, wrong architecture, launch */
+    QKROPE_ERR_ALLOC = 4         /* host memory for the handle could not be allocated */
+} qkrope_status;
+
+/* rope_table element types for qkrope_run_table: the table form's page allows the activation
+ * dtype (bf16) or float32. */
+enum { QKROPE_TABLE_BF16 = 0, QKROPE_TABLE_F32 = 1 };
+
+/* Norm modes for qkrope_run_table. PER_HEAD is the table form's contract (weights [head_dim],
+ * one RMS per head). ACROSS_HEADS (weights [heads*head_dim], one RMS over the token's whole Q or
+ * K row, as in the 3D form) and NONE (RoPE only) extend the table form so it covers every norm
+ * the 3D form has. */
+enum { QKROPE_NORM_NONE = 0, QKROPE_NORM_PER_HEAD = 1, QKROPE_NORM_ACROSS_HEADS = 2 };
+
+typedef struct qkrope_ctx *qkrope_handle;
+
+/* Create a handle bound to HIP device `device_ordinal` (made current for the query). Fails with
+ * QKROPE_ERR_DEVICE if the device is not a gfx950 part. *out receives the handle. */
+int qkrope_create(int device_ordinal, qkrope_handle *out);
+
+/* Release a handle. NULL is accepted and ignored. No device work is pending on a handle (it holds
+ * only a snapshot of device properties), so this never blocks. */
+int qkrope_destroy(qkrope_handle h);
+
+/* Static text for a status code. */
+const char *qkrope_status_str(int status);
+
+/* Detail of the last error on the calling thread ("" after a successful call). */
+const char *qkrope_last_error(void);
+
+/*
+ * Table form (vLLM-Omni fused_qk_norm_rope).
+ *
+ *   q          [num_tokens, num_heads_q, head_dim] bf16; token t starts at q + t*q_token_stride
+ *              (elements); heads and dims are contiguous inside a token.
+ *   k          [num_tokens, num_heads_k, head_dim] bf16, token stride k_token_stride.
+ *   q_weight,  norm weights, bf16: [head_dim] for PER_HEAD, [num_heads*head_dim] for
+ *   k_weight   ACROSS_HEADS, ignored (may be NULL) for NONE.
+ *   rope_table [num_tokens, rotary_dim], token stride table_token_stride (elements), dtype
+ *              table_dtype. Row t holds cos(theta_t,i) for i < rotary_dim/2, then sin(theta_t,i).
+ *              Row t rotates token t.
+ *   eps        RMSNorm epsilon: n = x * (mean(x^2) + eps)^(-1/2) * w.
+ *   rotary_dim even, 0 < rotary_dim <= head_dim; dims >= rotary_dim are normalised, not rotated.
+ *   interleaved 0: half-split pairs (i, i + rotary_dim/2); 1: adjacent pairs (2i, 2i + 1).
+ *   q_out,     outputs with the inputs' shapes, bf16, token strides *_out_token_stride.
+ *   k_out      q_out == q (with equal strides) works in place, likewise k_out == k; any other
+ *              overlap between an output and an input is QKROPE_ERR_INVALID.
+ *
+ * Limits (else QKROPE_ERR_UNSUPPORTED): head_dim a multiple of 8 and <= 256; half-split needs
+ * head_dim and rotary_dim multiples of 16; num_tokens < 2^31.
+ * num_tokens == 0 (or zero heads) is a valid no-op.
+ */
+int qkrope_run_table(qkrope_handle h,
+                     const void *q, const void *k, const void *q_weight, const void *k_weight,
+                     const void *rope_table, int table_dtype, double eps,
+                     int64_t num_tokens, int num_heads_q, int num_heads_k, int head_dim,
+                     int rotary_dim, int interleaved, int norm_mode,
+                     int64_t q_token_stride, int64_t k_token_stride, int64_t table_token_stride,
+                     void *q_out, void *k_out,
+                     int64_t q_out_token_stride, int64_t k_out_token_stride,
+                     void *stream);
+
+/*
+ * 3D form (FlashInfer fused_qk_rmsnorm_rope).
+ *
+ *   qkv        [num_tokens, (num_heads_q + num_heads_k + num_heads_v) * head_dim] bf16,
+ *              contiguous; each row holds the token's Q heads, then K heads, then V heads.
+ *              num_tokens = batch * seq_len must be a multiple of seq_len = ppf*pph*ppw; token t
+ *              sits at grid position s = t mod seq_len, frame-major:
+ *              f = s / (pph*ppw), h = (s / ppw) mod pph, w = s mod ppw.
+ *   q_weight,  RMSNorm weights [num_heads_q*head_dim] and [num_heads_k*head_dim], bf16, used
+ *   k_weight   when is_qk_norm != 0 (one RMS over each token's whole Q, resp. K, row);
+ *              ignored (may be NULL) otherwise.
+ *   num_*_channels  even, summing to head_dim. The head_dim/2 rotation pairs take their
+ *              frequency from the concatenation [frame | height | width]: pair j of an axis with
+ *              C channels has omega_j = base^(-2j/C) and angle pos_axis * omega'_j.
+ *   head_dim   64, 128 or 256.
+ *   interleave 1: pairs (2k, 2k+1); 0: NeoX pairs (k, k + head_dim/2).
+ *   factor, low, high, attention_factor  YaRN. factor == 1 disables it and then
+ *              attention_factor must be 1. Otherwise high > low and, per axis pair index j,
+ *              rho = clamp((j - low)/(high - low), 0, 1),
+ *              omega'_j = (omega_j/factor)*rho + omega_j*(1 - rho); cos and sin are multiplied by
+ *              attention_factor.
+ *   output_fp8 0: q_out/k_out/v_out are bf16; V is a bit copy.
+ *              1: they are OCP E4M3 bytes: Q/K = e4m3(y * output_quant_scale),
+ *              V = e4m3(v * v_quant_scale); scales must be finite and > 0.
+ *   q_out, k_out, v_out  [num_tokens, num_heads_x, head_dim], contiguous, and must not overlap
+ *              qkv or each other.
+ *
+ * Limits (else QKROPE_ERR_UNSUPPORTED): num_tokens < 2^31; (Hq+Hk+Hv)*head_dim/8 <= 8192.
+ * num_tokens == 0 is a valid no-op.
+ */
+int qkrope_run_3d(qkrope_handle h,
+                  const void *qkv, const void *q_weight, const void *k_weight, int64_t num_tokens,
+                  int ppf, int pph, int ppw,
+                  int num_frame_channels, int num_height_channels, int num_width_channels,
+                  int num_heads_q, int num_heads_k, int num_heads_v, int head_dim,
+                  double eps, double base, int interleave, double factor, double low,
+                  double high, double attention_factor, int is_qk_norm, int output_fp8,
+                  double output_quant_scale, double v_quant_scale,
+                  void *q_out, void *k_out, void *v_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKROPE_H */

@@ -1,0 +1,261 @@
+"""Fused QK-RMSNorm + RoPE (+ V) attention prologue for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/qkrope.h (libqkrope.so, built by build.py). The
+binding only marshals arguments: every step of the computation runs in the library's HIP
+kernels. PyTorch provides device memory and the current stream.
+
+Entry points, with the names of the C ABI:
+  qkrope_create / qkrope_destroy / qkrope_run_table / qkrope_run_3d
+and the two page-shaped conveniences that allocate outputs:
+  fused_qk_norm_rope      -- vLLM-Omni "vllm_omni.diffusion.layers.fused_qk_norm_rope"
+  fused_qk_rmsnorm_rope   -- FlashInfer "flashinfer.norm.fused_qk_rmsnorm_rope"
+
+There is no fallback: if the library is missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # imported before the library so both share torch's HIP runtime
+
+from .workloads import WORKLOADS  # noqa: F401  (re-exported for convenience)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqkrope.so")
+
+QKROPE_OK, QKROPE_ERR_INVALID, QKROPE_ERR_UNSUPPORTED, QKROPE_ERR_DEVICE, QKROPE_ERR_ALLOC = range(5)
+QKROPE_TABLE_BF16, QKROPE_TABLE_F32 = 0, 1
+NORM_MODES = {"none": 0, "per_head": 1, "across_heads": 2}
+
+_lock = threading.Lock()
+_lib = None
+_handles: dict[int, int] = {}
+
+
+class QkropeError(RuntimeError):
+    """A device-side failure reported by the library (status QKROPE_ERR_DEVICE / _ALLOC)."""
+
+
+def _hip_runtimes_loaded() -> set[str]:
+    with open("/proc/self/maps") as f:
+        return {l.split()[-1] for l in f if "libamdhip64" in l}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqkrope.so (once). Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'` "
+                               "or `python qk_rmsnorm_rope_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.qkrope_create.argtypes = [I, ctypes.POINTER(P)]
+        L.qkrope_create.restype = I
+        L.qkrope_destroy.argtypes = [P]
+        L.qkrope_destroy.restype = I
+        L.qkrope_status_str.argtypes = [I]
+        L.qkrope_status_str.restype = ctypes.c_char_p
+        L.qkrope_last_error.argtypes = []
+        L.qkrope_last_error.restype = ctypes.c_char_p
+        L.qkrope_run_table.argtypes = [P, P, P, P, P, P, I, D, I64, I, I, I, I, I, I,
+                                       I64, I64, I64, P, P, I64, I64, P]
+        L.qkrope_run_table.restype = I
+        L.qkrope_run_3d.argtypes = [P, P, P, P, I64, I, I, I, I, I, I, I, I, I, I,
+                                    D, D, I, D, D, D, D, I, I, D, D, P, P, P, P]
+        L.qkrope_run_3d.restype = I
+        runtimes = _hip_runtimes_loaded()
+        if len(runtimes) > 1:
+            raise RuntimeError(f"two HIP runtimes are loaded ({sorted(runtimes)}); "
+                               "libqkrope.so must share torch's")
+        _lib = L
+        return L
+
+
+def _check(status: int, what: str) -> None:
+    if status == QKROPE_OK:
+        return
+    L = lib()
+    msg = f"{what}: {L.qkrope_status_str(status).decode()}: {L.qkrope_last_error().decode()}"
+    if status in (QKROPE_ERR_INVALID, QKROPE_ERR_UNSUPPORTED):
+        raise ValueError(msg)
+    raise QkropeError(msg)
+
+
+# --- the C entry points ------------------------------------------------------------------------
+
+def qkrope_create(device: int = 0) -> int:
+    """Create a library handle for HIP device `device`; returns the opaque handle."""
+    h = ctypes.c_void_p()
+    _check(lib().qkrope_create(int(device), ctypes.byref(h)), "qkrope_create")
+    return h.value
+
+
+def qkrope_destroy(handle) -> None:
+    _check(lib().qkrope_destroy(handle), "qkrope_destroy")
+
+
+def _handle_for(device: torch.device) -> int:
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    with _lock:
+        h = _handles.get(idx)
+    if h is None:
+        h = qkrope_create(idx)
+        with _lock:
+            _handles.setdefault(idx, h)
+            h = _handles[idx]
+    return h
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _rows(t: torch.Tensor, heads: int, head_dim: int, name: str) -> int:
+    """Token stride (elements) of a [T, H, D] (or [T, H*D]) view with contiguous heads/dims."""
+    if t.dim() == 3:
+        ok = t.shape[1] == heads and t.shape[2] == head_dim and \
+            (t.shape[1] <= 1 or t.stride(1) == head_dim) and (t.shape[2] <= 1 or t.stride(2) == 1)
+    elif t.dim() == 2:
+        ok = t.shape[1] == heads * head_dim and (t.shape[1] <= 1 or t.stride(1) == 1)
+    else:
+        ok = False
+    if not ok:
+        raise ValueError(f"{name} must be [tokens, heads, head_dim] with contiguous heads and dims")
+    return t.stride(0) if t.shape[0] > 1 else heads * head_dim
+
+
+def qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, *, q_out, k_out,
+                     head_dim=None, rotary_dim=None, interleaved=False, norm_mode="per_head",
+                     stream=None) -> None:
+    """Table form into caller-provided outputs (q_out may be q, k_out may be k)."""
+    for name, t in (("q", q), ("k", k), ("q_out", q_out), ("k_out", k_out)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError(f"{name} must be a bfloat16 GPU tensor")
+    D = head_dim if head_dim is not None else q.shape[-1]
+    Hq = q.shape[1] if q.dim() == 3 else q.shape[1] // D
+    Hk = k.shape[1] if k.dim() == 3 else k.shape[1] // D
+    T = q.shape[0]
+    if k.shape[0] != T or q_out.shape[0] != T or k_out.shape[0] != T:
+        raise ValueError("q, k and outputs must have the same number of tokens")
+    R = rotary_dim if rotary_dim is not None else rope_table.shape[-1]
+    if rope_table.dtype == torch.float32:
+        tdt = QKROPE_TABLE_F32
+    elif rope_table.dtype == torch.bfloat16:
+        tdt = QKROPE_TABLE_BF16
+    else:
+        raise ValueError("rope_table must be float32 or bfloat16")
+    if rope_table.dim() != 2 or rope_table.shape[0] != T or rope_table.shape[1] < R or \
+            (R > 0 and rope_table.stride(1) != 1) or not rope_table.is_cuda:
+        raise ValueError("rope_table must be a GPU [tokens, >= rotary_dim] tensor whose "
+                         "columns are contiguous (unit stride along the last dim)")
+    ts = rope_table.stride(0) if T > 1 else rope_table.shape[1]
+    for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+        if norm_mode != "none" and (w is None or w.dtype != torch.bfloat16 or not w.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    s = lib().qkrope_run_table(
+        _handle_for(q.device), _ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight), _ptr(rope_table),
+        tdt, float(eps), T, Hq, Hk, D, R, int(bool(interleaved)), NORM_MODES[norm_mode],
+        _rows(q, Hq, D, "q"), _rows(k, Hk, D, "k"), ts, _ptr(q_out), _ptr(k_out),
+        _rows(q_out, Hq, D, "q_out"), _rows(k_out, Hk, D, "k_out"), _stream(q.device, stream))
+    _check(s, "qkrope_run_table")
+
+
+def qkrope_run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
+                  num_height_channels, num_width_channels, num_heads_q, num_heads_k,
+                  num_heads_v, head_dim, q_out, k_out, v_out, eps=1e-6, base=10000.0,
+                  interleave=True, factor=1.0, low=0.0, high=0.0, attention_factor=1.0,
+                  is_qk_norm=True, output_fp8=False, output_quant_scale=1.0, v_quant_scale=1.0,
+                  stream=None) -> None:
+    """3D form into caller-provided contiguous outputs."""
+    if qkv.dtype != torch.bfloat16 or not qkv.is_cuda or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous bfloat16 GPU tensor")
+    row = (num_heads_q + num_heads_k + num_heads_v) * head_dim
+    if qkv.dim() not in (2, 3) or qkv.shape[-1] != row:
+        raise ValueError(f"qkv must be [tokens, {row}] or [batch, seq_len, {row}]")
+    T = qkv.numel() // row
+    odt = torch.float8_e4m3fn if output_fp8 else torch.bfloat16
+    for name, o, H in (("q_out", q_out, num_heads_q), ("k_out", k_out, num_heads_k),
+                       ("v_out", v_out, num_heads_v)):
+        if o.dtype != odt or not o.is_contiguous() or o.numel() != T * H * head_dim or not o.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {odt} GPU tensor of {T}x{H}x{head_dim}")
+    if is_qk_norm:
+        for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+            if w is None or w.dtype != torch.bfloat16 or not w.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    s = lib().qkrope_run_3d(
+        _handle_for(qkv.device), _ptr(qkv), _ptr(q_weight) if is_qk_norm else None,
+        _ptr(k_weight) if is_qk_norm else None, T, ppf, pph, ppw, num_frame_channels,
+        num_height_channels, num_width_channels, num_heads_q, num_heads_k, num_heads_v, head_dim,
+        float(eps), float(base), int(bool(interleave)), float(factor), float(low), float(high),
+        float(attention_factor), int(bool(is_qk_norm)), int(bool(output_fp8)),
+        float(output_quant_scale), float(v_quant_scale), _ptr(q_out), _ptr(k_out), _ptr(v_out),
+        _stream(qkv.device, stream))
+    _check(s, "qkrope_run_3d")
+
+
+# --- the pages' Python signatures --------------------------------------------------------------
+
+def fused_qk_norm_rope(q, k, q_weight, k_weight, rope_table, eps, *, head_dim=None,
+                       rotary_dim=None, interleaved=False):
+    """Q/K RMSNorm (per head, [head_dim] weights) then RoPE from a [tokens, rotary_dim] table.
+
+    Signature of vLLM-Omni's fused_qk_norm_rope. Returns new (q, k) with the inputs' shapes.
+    """
+    q_out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    k_out = torch.empty(k.shape, dtype=k.dtype, device=k.device)
+    qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, q_out=q_out, k_out=k_out,
+                     head_dim=head_dim, rotary_dim=rotary_dim, interleaved=interleaved)
+    return q_out, k_out
+
+
+def fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
+                          num_height_channels, num_width_channels, num_heads_q, num_heads_k,
+                          num_heads_v, head_dim, eps=1e-6, base=10000.0, interleave=True,
+                          factor=1.0, low=0.0, high=0.0, attention_factor=1.0, is_qk_norm=True,
+                          output_fp8=False, output_quant_scale=1.0, v_quant_scale=1.0,
+                          q_out=None, k_out=None, v_out=None):
+    """Across-heads QK RMSNorm + 3D RoPE + V copy (+ FP8), FlashInfer's signature.
+
+    Returns (q_out, k_out, v_out), each [B, S, H, D] for a 3D qkv or [T, H, D] for a 2D one;
+    pre-allocated outputs are used when given (destination-passing style).
+    """
+    lead = tuple(qkv.shape[:-1])
+    odt = torch.float8_e4m3fn if output_fp8 else torch.bfloat16
+    outs = []
+    for o, H in ((q_out, num_heads_q), (k_out, num_heads_k), (v_out, num_heads_v)):
+        outs.append(o if o is not None else
+                    torch.empty(lead + (H, head_dim), dtype=odt, device=qkv.device))
+    qkrope_run_3d(qkv, q_weight, k_weight, ppf=ppf, pph=pph, ppw=ppw,
+                  num_frame_channels=num_frame_channels, num_height_channels=num_height_channels,
+                  num_width_channels=num_width_channels, num_heads_q=num_heads_q,
+                  num_heads_k=num_heads_k, num_heads_v=num_heads_v, head_dim=head_dim,
+                  q_out=outs[0], k_out=outs[1], v_out=outs[2], eps=eps, base=base,
+                  interleave=interleave, factor=factor, low=low, high=high,
+                  attention_factor=attention_factor, is_qk_norm=is_qk_norm,
+                  output_fp8=output_fp8, output_quant_scale=output_quant_scale,
+                  v_quant_scale=v_quant_scale)
+    return tuple(outs)
+
+
+def run_workload_3d(w, qkv, q_weight, k_weight, q_out=None, k_out=None, v_out=None):
+    """fused_qk_rmsnorm_rope with the parameters of a 3D workload description."""
+    return fused_qk_rmsnorm_rope(
+        qkv, q_weight, k_weight, ppf=w.ppf, pph=w.pph, ppw=w.ppw,
+        num_frame_channels=w.num_frame_channels, num_height_channels=w.num_height_channels,
+        num_width_channels=w.num_width_channels, num_heads_q=w.num_heads_q,
+        num_heads_k=w.num_heads_k, num_heads_v=w.num_heads_v, head_dim=w.head_dim, eps=w.eps,
+        base=w.base, interleave=w.interleave, factor=w.factor, low=w.low, high=w.high,
+        attention_factor=w.attention_factor, is_qk_norm=w.is_qk_norm, output_fp8=w.output_fp8,
+        output_quant_scale=w.output_quant_scale, v_quant_scale=w.v_quant_scale,
+        q_out=q_out, k_out=k_out, v_out=v_out)

@@ -1,0 +1,76 @@
+"""Build libqkrope.so: the HIP kernel family and the C ABI, for gfx950.
+
+The library links against the HIP runtime that PyTorch loads (torch/lib/libamdhip64.so), so a
+process that uses torch for memory and streams has exactly one HIP runtime, and the hipStream_t
+handles torch gives out are valid inside the library.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_PATH = os.path.join(PKG, "libqkrope.so")
+
+SOURCES = ["qkrope_kernels_3d_d64.hip", "qkrope_kernels_3d_d128.hip", "qkrope_kernels_3d_d256.hip",
+           "qkrope_kernels_table_interleaved.hip", "qkrope_kernels_table_halfsplit.hip",
+           "qkrope_api.cpp"]
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 VALU forms in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def torch_lib_dir() -> str:
+    import torch
+    return os.path.join(os.path.dirname(torch.__file__), "lib")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "is not a recognized feature for this target" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if out.strip() and verbose:
+        print(out, flush=True)
+
+
+def build(verbose: bool = True) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    t0 = time.time()
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmds.append([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tlib = torch_lib_dir()
+    tmp = LIB_PATH + ".tmp"
+    _run(["g++", "-shared", "-o", tmp, *objs, f"-L{tlib}", "-l:libamdhip64.so",
+          f"-Wl,-rpath,{tlib}", "-Wl,--no-undefined"], verbose)
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH} in {time.time() - t0:.1f}s", flush=True)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

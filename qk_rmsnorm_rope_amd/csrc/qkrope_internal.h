@@ -1,0 +1,92 @@
+// Internal interface between the C-ABI host code (qkrope_api.cpp) and the kernel family
+// (qkrope_kernels.hip). Not installed; the public interface is include/qkrope.h.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace qkrope {
+
+constexpr int kMaxPairs = 128;      // head_dim/2 for head_dim <= 256
+
+enum Region { kQ = 0, kK = 1, kV = 2 };
+enum Norm { kNormNone = 0, kNormPerHead = 1, kNormAcross = 2 };
+enum RopeSrc { kSrcTableF32 = 0, kSrcTableBF16 = 1, kSrc3D = 2 };
+
+// Magic pair for n / d with n < 2^31: q = (mulhi(n, m) + n) >> l.
+struct FastDiv {
+    uint32_t m, l;
+};
+
+// Everything one launch needs. Passed by value as the kernel argument; host code fills it.
+struct KernelArgs {
+    // Regions Q, K, V: token t of region r starts at in[r] + t*in_stride[r] (bf16 elements) and
+    // its output at out[r] + t*out_stride[r] (output elements: bf16 or e4m3 bytes).
+    const uint16_t *in[3];
+    void *out[3];
+    int64_t in_stride[3];
+    int64_t out_stride[3];
+    int heads[3];              // Hq, Hk, Hv (Hv = 0: no V region)
+    const uint16_t *weight[2]; // q, k norm weights (bf16) or null
+    const void *table;         // table form: [T, R] cos|sin, fp32 or bf16
+    int64_t table_stride;      // elements
+
+    int64_t num_tokens;
+    int tokens_per_block;      // consecutive tokens one workgroup walks through
+    int head_dim;              // D
+    int rotary_dim;            // R (== D for the 3D form)
+    int lanes_per_head;        // L: power of two >= units per head
+    float eps;
+    float inv_count[2];        // 1 / (elements the Q, K norm averages over)
+    float qk_scale;            // FP8 scale for Q/K outputs (1 for bf16)
+    float v_scale;             // FP8 scale for V (1 for bf16)
+
+    // 3D positions: s = t mod seq_len; f = s / hw; h = (s / ppw) mod pph; w = s mod ppw.
+    uint32_t seq_len, hw, ppw, pph;
+    FastDiv div_seq, div_hw, div_w;   // for n / seq_len, n / hw, n / ppw
+    float attention_factor;
+    float omega_rev[kMaxPairs];    // per pair k: omega'_k / (2*pi), revolutions per position
+    uint8_t axis[kMaxPairs];       // per pair k: 0 frame, 1 height, 2 width
+};
+
+// Launch shape chosen by the host for one call.
+struct LaunchShape {
+    int threads;        // workgroup size, multiple of 64, <= 1024
+    int slots;          // slots per region (region-major) or per lane (mixed)
+    bool slot_uniform;  // region-major slot layout
+    int64_t blocks;     // grid size
+};
+
+// Kernel selection keys.
+struct KernelKey {
+    int head_dim_tpl;   // 64/128/256 for the 3D kernels, 0 = runtime head_dim (table form)
+    bool half_split;
+    int norm;           // Norm
+    int src;            // RopeSrc
+    bool fp8;
+    int slots;          // slots per region (region-major) or per lane (mixed)
+    bool slot_uniform;  // region-major slot layout
+};
+
+// Per-translation-unit launchers. Each returns hipSuccess or the launch error, and
+// hipErrorInvalidValue if no compiled kernel matches `key`.
+hipError_t launch_3d_d64(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_3d_d128(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_3d_d256(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_table_interleaved(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_table_halfsplit(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+
+// Slot counts the kernels are compiled for: region-major 1..4 slots per region, mixed 1, 2, 4
+// slots per lane, limited so that a lane holds at most kMaxChunks 16-byte input chunks per token
+// (half-split units are two chunks).
+constexpr int kMaxSlotsRegionMajor = 4;
+constexpr int kMixedSlots[] = {1, 2, 4};
+constexpr int kMaxChunks = 8;
+
+constexpr bool slots_compiled(int nreg, bool half, bool region_major, int ns)
+{
+    return (region_major ? ns >= 1 && ns <= kMaxSlotsRegionMajor : (ns == 1 || ns == 2 || ns == 4)) &&
+           (region_major ? nreg * ns : ns) * (half ? 2 : 1) <= kMaxChunks;
+}
+
+}  // namespace qkrope

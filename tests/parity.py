@@ -1,0 +1,100 @@
+"""Shared helpers for the GPU parity tests: running both sides and the match criteria.
+
+Match criteria (element by element against the fp64 oracle on the same seeded inputs):
+  * V copy (bf16 output): bit-exact.
+  * bf16 Q/K: |gpu - ref| <= 2^-7 * |ref| + 1e-3, with ref the oracle's unrounded fp64 value.
+  * FP8 E4M3 outputs: within one code of the oracle's round-to-nearest-even code (codes compared
+    in sign-magnitude order, so +0 and -0 are the same point).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+BF16_REL = 2.0 ** -7
+BF16_ABS = 1e-3
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def codes8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def assert_bf16_close(gpu: torch.Tensor, ref: np.ndarray, what: str) -> None:
+    g = to_f64(gpu).reshape(ref.shape)
+    err = np.abs(g - ref)
+    bound = BF16_REL * np.abs(ref) + BF16_ABS
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        idx = np.unravel_index(i, ref.shape)
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; first at {idx}: "
+            f"gpu={g[idx]!r} ref={ref[idx]!r} err={err[idx]:.3g} bound={bound[idx]:.3g}")
+
+
+def e4m3_ordinal(codes: np.ndarray) -> np.ndarray:
+    c = codes.astype(np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def assert_e4m3_within_one(gpu: torch.Tensor, ref_codes: np.ndarray, what: str) -> None:
+    g = codes8(gpu).reshape(ref_codes.shape)
+    assert not np.any((g & 0x7F) == 0x7F), f"{what}: NaN code in GPU output"
+    d = np.abs(e4m3_ordinal(g) - e4m3_ordinal(ref_codes))
+    if (d > 1).any():
+        i = np.flatnonzero((d > 1).ravel())[0]
+        idx = np.unravel_index(i, ref_codes.shape)
+        raise AssertionError(f"{what}: {(d > 1).sum()} codes more than one step away; first at "
+                             f"{idx}: gpu=0x{g[idx]:02x} ref=0x{ref_codes[idx]:02x}")
+
+
+def assert_bits_equal(gpu: torch.Tensor, ref_bits: np.ndarray, what: str) -> None:
+    g = bits16(gpu).reshape(ref_bits.shape) if gpu.dtype == torch.bfloat16 else \
+        codes8(gpu).reshape(ref_bits.shape)
+    if not np.array_equal(g, ref_bits):
+        n = int((g != ref_bits).sum())
+        raise AssertionError(f"{what}: {n} of {g.size} elements differ (bit-exact required)")
+
+
+def check_3d_outputs(w, outs, ref, tokens=None) -> None:
+    """Compare GPU (q, k, v) of a 3D workload with the oracle's fp64 (q, k, v).
+
+    `tokens` selects flattened token rows of the GPU outputs that `ref` covers (None: all).
+    """
+    names = ("q", "k", "v")
+    for i, (o, r) in enumerate(zip(outs, ref)):
+        H = (w.num_heads_q, w.num_heads_k, w.num_heads_v)[i]
+        o = o.reshape(w.num_tokens, H, w.head_dim)
+        if tokens is not None:
+            o = o[torch.as_tensor(tokens, device=o.device)]
+        if w.output_fp8:
+            scale = w.v_quant_scale if i == 2 else w.output_quant_scale
+            codes = oracle.e4m3_encode(r, scale)
+            if i == 2:
+                # v * v_quant_scale is exact for a power-of-two scale: one correct code
+                if float(np.log2(scale)).is_integer():
+                    assert_bits_equal(o, codes, f"{w.name} v (e4m3)")
+                else:
+                    assert_e4m3_within_one(o, codes, f"{w.name} v (e4m3)")
+            else:
+                assert_e4m3_within_one(o, codes, f"{w.name} {names[i]} (e4m3)")
+        elif i == 2:
+            assert_bits_equal(o, oracle.bf16_encode(r), f"{w.name} v")
+        else:
+            assert_bf16_close(o, r, f"{w.name} {names[i]}")
+
+
+def check_table_outputs(name, q_out, k_out, ref_q, ref_k) -> None:
+    assert_bf16_close(q_out, ref_q, f"{name} q")
+    assert_bf16_close(k_out, ref_k, f"{name} k")

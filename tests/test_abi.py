@@ -1,0 +1,57 @@
+"""The C-ABI library: it loads, exports every function include/qkrope.h declares, and its
+host-side argument checks answer without a GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkrope.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qkrope_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import qk_rmsnorm_rope_amd as qr
+    if not os.path.exists(qr.LIB_PATH):
+        pytest.fail(f"{qr.LIB_PATH} is not built (run __graft_entry__.build())")
+    return qr.lib()
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("qkrope_create", "qkrope_run_table", "qkrope_run_3d", "qkrope_destroy"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} missing from libqkrope.so"
+
+
+def test_status_strings_and_null_handle(lib):
+    assert lib.qkrope_status_str(0) == b"ok"
+    assert lib.qkrope_status_str(1) == b"invalid argument"
+    assert lib.qkrope_status_str(99) == b"unknown status"
+    assert lib.qkrope_destroy(None) == 0
+    # NULL handle: rejected before any HIP call
+    rc = lib.qkrope_run_3d(None, None, None, None, 0, 1, 1, 1, 0, 0, 64, 1, 1, 1, 64, 1e-6,
+                           1e4, 1, 1.0, 0.0, 0.0, 1.0, 1, 0, 1.0, 1.0, None, None, None, None)
+    assert rc == 1
+    assert b"handle" in lib.qkrope_last_error()
+    rc = lib.qkrope_run_table(None, None, None, None, None, None, 0, 1e-6, 0, 1, 1, 64, 64, 1, 1,
+                              64, 64, 64, None, None, 64, 64, None)
+    assert rc == 1
+    assert lib.qkrope_create(0, None) == 1          # out pointer NULL
+
+
+def test_library_links_torchs_hip_runtime(lib):
+    import qk_rmsnorm_rope_amd as qr
+    runtimes = qr._hip_runtimes_loaded()
+    assert len(runtimes) == 1 and "torch" in next(iter(runtimes)), runtimes

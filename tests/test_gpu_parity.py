@@ -1,0 +1,327 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element.
+
+Sizes: each named workload at a size the oracle finishes in seconds (several workgroups' worth of
+tokens, ragged where the shape allows), the same workloads at full size on sampled tokens, and a
+seeded sweep over the contract's parameters (pairing, norm mode, YaRN, FP8, head counts, tiny and
+degenerate grids, strided and in-place table views).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import assert_bf16_close, check_3d_outputs, check_table_outputs
+
+pytestmark = pytest.mark.gpu
+
+qr = pytest.importorskip("qk_rmsnorm_rope_amd")
+from qk_rmsnorm_rope_amd import workloads as wl  # noqa: E402
+
+DEV = "cuda"
+
+
+def _gpu(t):
+    return t.to(DEV)
+
+
+def run_3d(w, inputs):
+    qkv, wq, wk = (_gpu(inputs[k]) for k in ("qkv", "q_weight", "k_weight"))
+    outs = qr.run_workload_3d(w, qkv, wq, wk)
+    torch.cuda.synchronize()
+    return outs
+
+
+def oracle_3d(w, inputs, tokens=None):
+    x = inputs["qkv"].reshape(-1, w.row_elems)
+    if tokens is None:
+        return oracle.run_3d_workload(w, x, inputs["q_weight"], inputs["k_weight"])
+    parts = [oracle.run_3d_workload(w, x[t:t + 1], inputs["q_weight"], inputs["k_weight"],
+                                    token_offset=int(t)) for t in tokens]
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(3))
+
+
+def run_table(w, inputs, **kw):
+    q, k, wq, wk, tab = (_gpu(inputs[n]) for n in ("q", "k", "q_weight", "k_weight", "rope_table"))
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    qr.qkrope_run_table(q, k, wq, wk, tab, w.eps, q_out=qo, k_out=ko, rotary_dim=w.rotary_dim,
+                        interleaved=w.interleaved, norm_mode=w.norm_mode, **kw)
+    torch.cuda.synchronize()
+    return qo, ko
+
+
+def oracle_table(w, inputs):
+    return oracle.run_table(inputs["q"], inputs["k"], inputs["q_weight"], inputs["k_weight"],
+                            inputs["rope_table"], w.eps, rotary_dim=w.rotary_dim,
+                            interleaved=w.interleaved, norm_mode=w.norm_mode)
+
+
+def sample_tokens(T, S, n=48, seed=0):
+    """First/last tokens, grid corners of the first and last sequence, and random ones."""
+    rng = np.random.default_rng(seed)
+    picks = {0, 1, T - 1, T - 2, S - 1, min(S, T - 1), T - S}
+    picks |= set(rng.integers(0, T, n).tolist())
+    return np.array(sorted(p for p in picks if 0 <= p < T))
+
+
+# --- the named workloads, reduced so the oracle runs in seconds ---------------------------------
+
+REDUCED_3D = [
+    wl.ROPE3D_ACROSS_S15360.with_(ppf=2),                   # 1920 tokens, positions f in {0,1}
+    wl.ROPE3D_NEOX_FP8_S18480.with_(ppf=2, pph=7),          # batch 2 x 392 tokens
+    wl.ROPE3D_YARN_S122880.with_(ppf=1, pph=9),             # 720 tokens
+]
+
+
+@pytest.mark.parametrize("w", REDUCED_3D, ids=lambda w: w.name)
+def test_3d_workload_reduced(w):
+    inputs = wl.rope3d_inputs(w)
+    outs = run_3d(w, inputs)
+    check_3d_outputs(w, outs, oracle_3d(w, inputs))
+
+
+@pytest.mark.parametrize("w", [wl.TABLE_HALFSPLIT_T256, wl.TABLE_INTERLEAVED_T4096],
+                         ids=lambda w: w.name)
+def test_table_workload_full(w):
+    inputs = wl.table_inputs(w)
+    qo, ko = run_table(w, inputs)
+    rq, rk = oracle_table(w, inputs)
+    check_table_outputs(w.name, qo, ko, rq, rk)
+
+
+def test_table_workload_ragged_tokens():
+    w = wl.TABLE_INTERLEAVED_T4096.with_(num_tokens=333)
+    inputs = wl.table_inputs(w)
+    qo, ko = run_table(w, inputs)
+    check_table_outputs(w.name, qo, ko, *oracle_table(w, inputs))
+
+
+# --- the named 3D workloads at full size, sampled ----------------------------------------------
+
+@pytest.mark.parametrize("w", [wl.ROPE3D_ACROSS_S15360, wl.ROPE3D_NEOX_FP8_S18480,
+                               wl.ROPE3D_YARN_S122880], ids=lambda w: w.name)
+def test_3d_workload_full_size_sampled(w):
+    inputs = wl.rope3d_inputs(w)
+    outs = run_3d(w, inputs)
+    tokens = sample_tokens(w.num_tokens, w.seq_len)
+    check_3d_outputs(w, outs, oracle_3d(w, inputs, tokens), tokens=tokens)
+    if not w.output_fp8:
+        # V is a bit copy of the packed input at every token, not only the sampled ones
+        qkv = _gpu(inputs["qkv"]).reshape(-1, w.row_elems)
+        v_in = qkv[:, (w.num_heads_q + w.num_heads_k) * w.head_dim:]
+        assert torch.equal(outs[2].reshape(v_in.shape), v_in)
+
+
+# --- seeded sweep over the 3D contract ----------------------------------------------------------
+
+SWEEP_3D = [
+    # (D, Hq, Hk, Hv, grid, channels, batch, interleave, norm, fp8, yarn)
+    (64, 3, 2, 5, (2, 3, 4), (16, 24, 24), 2, True, True, False, False),
+    (64, 1, 1, 1, (1, 1, 1), (0, 0, 64), 3, False, True, True, False),
+    (128, 4, 4, 4, (3, 1, 5), (32, 48, 48), 1, False, False, False, True),
+    (128, 6, 2, 1, (1, 4, 1), (16, 56, 56), 2, True, True, True, True),
+    (256, 2, 3, 2, (2, 2, 2), (64, 96, 96), 1, True, False, True, True),
+    (256, 5, 5, 5, (1, 2, 7), (0, 128, 128), 1, False, True, False, False),
+    (128, 32, 32, 32, (1, 2, 3), (16, 56, 56), 2, True, True, False, False),
+    (64, 20, 20, 20, (2, 3, 2), (16, 24, 24), 1, True, True, True, False),
+    (128, 8, 0, 8, (1, 1, 4), (128, 0, 0), 1, True, True, False, False),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP_3D, ids=lambda c: "d{}_h{}-{}-{}_g{}".format(c[0], *c[1:4], "x".join(map(str, c[4]))))
+def test_3d_sweep(case):
+    D, Hq, Hk, Hv, (f, h, ww), (cf, ch, cw), B, inter, norm, fp8, yarn = case
+    w = wl.Rope3DWorkload(
+        name=f"sweep_d{D}", batch=B, ppf=f, pph=h, ppw=ww, num_frame_channels=cf,
+        num_height_channels=ch, num_width_channels=cw, num_heads_q=Hq, num_heads_k=Hk,
+        num_heads_v=Hv, head_dim=D, seed=1000 + D + Hq, interleave=inter, is_qk_norm=norm,
+        output_fp8=fp8, output_quant_scale=0.75 if fp8 else 1.0,
+        v_quant_scale=0.5 if fp8 else 1.0, sigma=3.0 if fp8 else 1.0,
+        factor=2.0 if yarn else 1.0, low=0.5 if yarn else 0.0, high=6.0 if yarn else 0.0,
+        attention_factor=1.07 if yarn else 1.0, base=500.0 if yarn else 10000.0)
+    inputs = wl.rope3d_inputs(w)
+    check_3d_outputs(w, run_3d(w, inputs), oracle_3d(w, inputs))
+
+
+def test_3d_fp8_saturation_and_non_power_of_two_v_scale():
+    w = wl.ROPE3D_NEOX_FP8_S18480.with_(ppf=1, pph=2, ppw=4, batch=1, sigma=300.0,
+                                       output_quant_scale=3.0, v_quant_scale=1.7)
+    inputs = wl.rope3d_inputs(w)
+    check_3d_outputs(w, run_3d(w, inputs), oracle_3d(w, inputs))
+
+
+# --- seeded sweep over the table contract -------------------------------------------------------
+
+SWEEP_TABLE = [
+    # (T, Hq, Hk, D, R, interleaved, norm_mode, table dtype)
+    (7, 3, 1, 64, 64, True, "per_head", "f32"),
+    (64, 2, 5, 128, 96, False, "per_head", "bf16"),
+    (19, 4, 4, 96, 40, True, "per_head", "f32"),
+    (33, 1, 2, 256, 256, True, "across_heads", "bf16"),
+    (12, 3, 3, 32, 16, False, "across_heads", "f32"),
+    (5, 2, 2, 8, 6, True, "none", "f32"),
+    (9, 6, 2, 128, 128, False, "none", "bf16"),
+    (1, 1, 1, 24, 2, True, "per_head", "bf16"),
+    (40, 48, 8, 64, 32, True, "per_head", "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP_TABLE, ids=lambda c: "t{}_h{}-{}_d{}_r{}_{}_{}_{}".format(
+    c[0], c[1], c[2], c[3], c[4], "il" if c[5] else "hs", c[6], c[7]))
+def test_table_sweep(case):
+    T, Hq, Hk, D, R, inter, mode, tdt = case
+    w = wl.TableWorkload(name="sweep", num_tokens=T, num_heads_q=Hq, num_heads_k=Hk,
+                         head_dim=D, rotary_dim=R, interleaved=inter, table_dtype=tdt,
+                         seed=2000 + T + D, norm_mode=mode)
+    inputs = wl.table_inputs(w)
+    qo, ko = run_table(w, inputs)
+    check_table_outputs(f"table {case}", qo, ko, *oracle_table(w, inputs))
+
+
+def test_table_strided_views_and_in_place():
+    """q and k as views into one packed [T, (Hq+Hk+pad)*D] buffer; outputs written in place."""
+    T, Hq, Hk, D = 37, 3, 2, 64
+    w = wl.TableWorkload(name="strided", num_tokens=T, num_heads_q=Hq, num_heads_k=Hk,
+                         head_dim=D, rotary_dim=48, interleaved=True, table_dtype="f32", seed=77)
+    inputs = wl.table_inputs(w)
+    rq, rk = oracle_table(w, inputs)
+    packed = torch.zeros(T, (Hq + Hk + 1) * D, dtype=torch.bfloat16, device=DEV)
+    packed[:, :Hq * D] = _gpu(inputs["q"]).reshape(T, -1)
+    packed[:, Hq * D:(Hq + Hk) * D] = _gpu(inputs["k"]).reshape(T, -1)
+    tail = packed[:, (Hq + Hk) * D:].clone()
+    q = packed[:, :Hq * D].view(T, Hq, D)
+    k = packed[:, Hq * D:(Hq + Hk) * D].view(T, Hk, D)
+    assert q.stride(0) == (Hq + Hk + 1) * D
+    qr.qkrope_run_table(q, k, _gpu(inputs["q_weight"]), _gpu(inputs["k_weight"]),
+                        _gpu(inputs["rope_table"]), w.eps, q_out=q, k_out=k, rotary_dim=48,
+                        interleaved=True)
+    torch.cuda.synchronize()
+    check_table_outputs("in-place strided", q, k, rq, rk)
+    assert torch.equal(packed[:, (Hq + Hk) * D:], tail)     # padding untouched
+
+
+def test_table_page_signature():
+    w = wl.TABLE_HALFSPLIT_T256.with_(num_tokens=20)
+    inputs = wl.table_inputs(w)
+    g = {n: _gpu(t) for n, t in inputs.items()}
+    qo, ko = qr.fused_qk_norm_rope(g["q"], g["k"], g["q_weight"], g["k_weight"], g["rope_table"],
+                                   w.eps, rotary_dim=w.rotary_dim, interleaved=False)
+    torch.cuda.synchronize()
+    check_table_outputs("page signature", qo, ko, *oracle_table(w, inputs))
+
+
+# --- invariants between the two forms on the GPU ------------------------------------------------
+
+@pytest.mark.parametrize("inter", [True, False])
+@pytest.mark.parametrize("norm", [True, False])
+def test_gpu_3d_equals_gpu_table_with_matching_table(inter, norm):
+    """run_3d(x) == run_table(x's Q/K, table of the 3D angles), norm across heads or none."""
+    w = wl.Rope3DWorkload(name="inv", batch=1, ppf=2, pph=3, ppw=5, num_frame_channels=16,
+                          num_height_channels=24, num_width_channels=24, num_heads_q=4,
+                          num_heads_k=2, num_heads_v=1, head_dim=64, seed=31, interleave=inter,
+                          is_qk_norm=norm)
+    inputs = wl.rope3d_inputs(w)
+    q3, k3, _ = run_3d(w, inputs)
+    D, T = w.head_dim, w.num_tokens
+    f, h, ww = np.meshgrid(np.arange(w.ppf), np.arange(w.pph), np.arange(w.ppw), indexing="ij")
+    pos = np.stack([f.ravel(), h.ravel(), ww.ravel()], 1)
+    freqs = np.concatenate([w.base ** (-np.arange(0, c, 2) / c)
+                            for c in (w.num_frame_channels, w.num_height_channels,
+                                      w.num_width_channels)])
+    axis = np.repeat([0, 1, 2], [w.num_frame_channels // 2, w.num_height_channels // 2,
+                                 w.num_width_channels // 2])
+    theta = pos[:, axis] * freqs
+    tab = torch.from_numpy(np.ascontiguousarray(
+        np.concatenate([np.cos(theta), np.sin(theta)], 1).astype(np.float32)))
+    qkv = _gpu(inputs["qkv"]).reshape(T, -1)
+    q = qkv[:, :w.num_heads_q * D].reshape(T, w.num_heads_q, D)
+    k = qkv[:, w.num_heads_q * D:(w.num_heads_q + w.num_heads_k) * D].reshape(T, w.num_heads_k, D)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    qr.qkrope_run_table(q, k, _gpu(inputs["q_weight"]), _gpu(inputs["k_weight"]), _gpu(tab),
+                        w.eps, q_out=qo, k_out=ko, interleaved=inter,
+                        norm_mode="across_heads" if norm else "none")
+    torch.cuda.synchronize()
+    # both are bf16 roundings of values that agree to fp32 accuracy: at most one bf16 step apart
+    assert_bf16_close(qo, q3.reshape(T, -1, D).double().cpu().numpy(), "q 3d vs table")
+    assert_bf16_close(ko, k3.reshape(T, -1, D).double().cpu().numpy(), "k 3d vs table")
+
+
+def test_gpu_position_zero_no_norm_is_identity():
+    w = wl.Rope3DWorkload(name="id", batch=1, ppf=1, pph=1, ppw=1, num_frame_channels=64,
+                          num_height_channels=32, num_width_channels=32, num_heads_q=3,
+                          num_heads_k=3, num_heads_v=3, head_dim=128, seed=5, is_qk_norm=False)
+    inputs = wl.rope3d_inputs(w)
+    q, k, v = run_3d(w, inputs)
+    qkv = _gpu(inputs["qkv"]).reshape(1, -1)
+    assert torch.equal(q.reshape(1, -1), qkv[:, :3 * 128])
+    assert torch.equal(k.reshape(1, -1), qkv[:, 3 * 128:6 * 128])
+    assert torch.equal(v.reshape(1, -1), qkv[:, 6 * 128:])
+
+
+# --- the boundary: validation and error mapping -------------------------------------------------
+
+def test_empty_inputs_are_no_ops():
+    w = wl.ROPE3D_ACROSS_S15360
+    D = w.head_dim
+    qkv = torch.empty(0, w.row_elems, dtype=torch.bfloat16, device=DEV)
+    wq = torch.ones(w.num_heads_q * D, dtype=torch.bfloat16, device=DEV)
+    q, k, v = qr.run_workload_3d(w, qkv, wq, wq)
+    assert q.shape == (0, w.num_heads_q, D) and v.numel() == 0
+    z = torch.empty(0, 2, 64, dtype=torch.bfloat16, device=DEV)
+    tab = torch.empty(0, 64, dtype=torch.float32, device=DEV)
+    w64 = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    qo, ko = qr.fused_qk_norm_rope(z, z, w64, w64, tab, 1e-6)
+    assert qo.shape == z.shape
+
+
+def test_contract_violations_raise_value_error():
+    w = wl.ROPE3D_ACROSS_S15360.with_(ppf=1, pph=2, ppw=2)
+    inputs = wl.rope3d_inputs(w)
+    qkv, wq, wk = (_gpu(inputs[k]) for k in ("qkv", "q_weight", "k_weight"))
+    base = dict(ppf=w.ppf, pph=w.pph, ppw=w.ppw, num_frame_channels=16, num_height_channels=56,
+                num_width_channels=56, num_heads_q=32, num_heads_k=32, num_heads_v=32,
+                head_dim=128)
+    bad = [
+        dict(num_frame_channels=18),                       # channels do not sum to head_dim
+        dict(num_frame_channels=15, num_height_channels=57),  # odd channels
+        dict(attention_factor=1.5),                        # attention factor without YaRN
+        dict(factor=2.0, low=4.0, high=4.0),               # empty YaRN ramp
+        dict(ppw=3),                                       # tokens not a multiple of seq_len
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            qr.fused_qk_rmsnorm_rope(qkv, wq, wk, **{**base, **kw})
+    # head_dim outside {64, 128, 256} is rejected by the library itself
+    x96 = torch.zeros(4, 3 * 96, dtype=torch.bfloat16, device=DEV)
+    w96 = torch.ones(96, dtype=torch.bfloat16, device=DEV)
+    o96 = [torch.empty(4, 1, 96, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    with pytest.raises(ValueError, match="head_dim"):
+        qr.qkrope_run_3d(x96, w96, w96, ppf=1, pph=2, ppw=2, num_frame_channels=32,
+                         num_height_channels=32, num_width_channels=32, num_heads_q=1,
+                         num_heads_k=1, num_heads_v=1, head_dim=96, q_out=o96[0], k_out=o96[1],
+                         v_out=o96[2])
+    # outputs overlapping the input are rejected by the library
+    flat = qkv.view(-1, w.row_elems)
+    q_alias = flat[:, :32 * 128].contiguous()
+    with pytest.raises(ValueError):
+        qr.qkrope_run_3d(flat, wq, wk, ppf=w.ppf, pph=w.pph, ppw=w.ppw, num_frame_channels=16,
+                         num_height_channels=56, num_width_channels=56, num_heads_q=32,
+                         num_heads_k=32, num_heads_v=32, head_dim=128,
+                         q_out=flat.view(-1)[:q_alias.numel()].view(q_alias.shape),
+                         k_out=torch.empty_like(q_alias), v_out=torch.empty_like(q_alias))
+    # half-split table pairing needs rotary_dim % 16 == 0 in this library: unsupported
+    t = wl.TableWorkload(name="u", num_tokens=4, num_heads_q=1, num_heads_k=1, head_dim=64,
+                         rotary_dim=40, interleaved=False, table_dtype="f32", seed=3)
+    ti = {n: _gpu(v) for n, v in wl.table_inputs(t).items()}
+    with pytest.raises(ValueError, match="unsupported"):
+        qr.fused_qk_norm_rope(ti["q"], ti["k"], ti["q_weight"], ti["k_weight"], ti["rope_table"],
+                              1e-6, rotary_dim=40, interleaved=False)
+
+
+def test_single_hip_runtime_loaded():
+    qr.lib()
+    runtimes = qr._hip_runtimes_loaded()
+    assert len(runtimes) == 1, runtimes
