@@ -85,14 +85,16 @@ const char *qkrope_last_error(void);
  *              table_dtype. Row t holds cos(theta_t,i) for i < rotary_dim/2, then sin(theta_t,i).
  *              Row t rotates token t.
  *   eps        RMSNorm epsilon: n = x * (mean(x^2) + eps)^(-1/2) * w.
- *   rotary_dim even, 0 < rotary_dim <= head_dim; dims >= rotary_dim are normalised, not rotated.
+ *   rotary_dim even, 0 <= rotary_dim <= head_dim; dims >= rotary_dim are normalised, not
+ *              rotated (rotary_dim 0: RoPE is skipped and rope_table may be NULL).
  *   interleaved 0: half-split pairs (i, i + rotary_dim/2); 1: adjacent pairs (2i, 2i + 1).
  *   q_out,     outputs with the inputs' shapes, bf16, token strides *_out_token_stride.
  *   k_out      q_out == q (with equal strides) works in place, likewise k_out == k; any other
  *              overlap between an output and an input is QKROPE_ERR_INVALID.
  *
  * Limits (else QKROPE_ERR_UNSUPPORTED): head_dim a multiple of 8 and <= 256; half-split needs
- * head_dim and rotary_dim multiples of 16; num_tokens < 2^31.
+ * rotary_dim to be a multiple of 16 (each half a whole number of 16-byte chunks);
+ * num_tokens < 2^31.
  * num_tokens == 0 (or zero heads) is a valid no-op.
  */
 int qkrope_run_table(qkrope_handle h,

@@ -248,6 +248,41 @@ def fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_c
     return tuple(outs)
 
 
+class Prepared3D:
+    """Arguments of one qkrope_run_3d call marshalled once, for launching repeatedly with no
+    per-call Python work beyond the C call (the tensors must stay alive and unmoved)."""
+
+    def __init__(self, w, qkv, q_weight, k_weight, q_out, k_out, v_out, stream=None):
+        # validate once through the regular path (this also launches once)
+        qkrope_run_3d(qkv, q_weight, k_weight, ppf=w.ppf, pph=w.pph, ppw=w.ppw,
+                      num_frame_channels=w.num_frame_channels,
+                      num_height_channels=w.num_height_channels,
+                      num_width_channels=w.num_width_channels, num_heads_q=w.num_heads_q,
+                      num_heads_k=w.num_heads_k, num_heads_v=w.num_heads_v,
+                      head_dim=w.head_dim, q_out=q_out, k_out=k_out, v_out=v_out, eps=w.eps,
+                      base=w.base, interleave=w.interleave, factor=w.factor, low=w.low,
+                      high=w.high, attention_factor=w.attention_factor,
+                      is_qk_norm=w.is_qk_norm, output_fp8=w.output_fp8,
+                      output_quant_scale=w.output_quant_scale,
+                      v_quant_scale=w.v_quant_scale, stream=stream)
+        self._fn = lib().qkrope_run_3d
+        self._args = (
+            _handle_for(qkv.device), _ptr(qkv), _ptr(q_weight) if w.is_qk_norm else None,
+            _ptr(k_weight) if w.is_qk_norm else None, qkv.numel() // w.row_elems, w.ppf, w.pph,
+            w.ppw, w.num_frame_channels, w.num_height_channels, w.num_width_channels,
+            w.num_heads_q, w.num_heads_k, w.num_heads_v, w.head_dim, float(w.eps),
+            float(w.base), int(w.interleave), float(w.factor), float(w.low), float(w.high),
+            float(w.attention_factor), int(w.is_qk_norm), int(w.output_fp8),
+            float(w.output_quant_scale), float(w.v_quant_scale), _ptr(q_out), _ptr(k_out),
+            _ptr(v_out), _stream(qkv.device, stream))
+        self._keep = (qkv, q_weight, k_weight, q_out, k_out, v_out)
+
+    def __call__(self) -> None:
+        s = self._fn(*self._args)
+        if s != QKROPE_OK:
+            _check(s, "qkrope_run_3d")
+
+
 def run_workload_3d(w, qkv, q_weight, k_weight, q_out=None, k_out=None, v_out=None):
     """fused_qk_rmsnorm_rope with the parameters of a 3D workload description."""
     return fused_qk_rmsnorm_rope(

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <algorithm>
 #include <cstring>
@@ -84,25 +85,38 @@ int next_pow2(int v)
     return p;
 }
 
-// Workgroup size and slot layout for a token whose regions hold n[r] lane-units each.
-// Region-major gives every region `slots` slots per lane (compiled 1..4); mixed concatenates the
-// regions and gives every lane `slots` slots (compiled 1, 2, 4). The layout that leaves the
-// fewest lanes idle wins; among equals, workgroups nearer 256 lanes, then region-major (whose
-// slots have scalar bases).
-bool choose_shape(const int64_t *n, int nreg, bool half, LaunchShape *s)
+// Workgroup size and slot layout for a token whose regions hold n[r] lane-units (16-byte
+// chunks) each. Region-major gives every region `slots` slots per lane (compiled 1..4); mixed
+// concatenates the regions and gives every lane `slots` slots (compiled 1, 2, 4).
+// Measured on MI355X (launch-shape sweeps of the 3D workloads): region-major with the fewest
+// slots that fit one workgroup, threads rounded up to whole waves, is best or within 1.5% of
+// best whenever it keeps at least 3/4 of the lanes busy (15360 tokens x 3x32 heads x 128,
+// 122880 x 3x16 x 256, and 36960 x 3x20 x 64 at 83% busy lanes, where the best mixed layout was
+// 10% slower). Otherwise the layout that leaves the fewest lanes idle wins, preferring
+// workgroups near 128 lanes.
+bool choose_shape(const int64_t *n, int nreg, LaunchShape *s)
 {
     int64_t total = 0, maxn = 0;
     for (int r = 0; r < nreg; ++r) {
         total += n[r];
         maxn = n[r] > maxn ? n[r] : maxn;
     }
+    if (maxn > 0) {
+        const int64_t ns = (maxn + 1023) / 1024;
+        const int64_t threads = ((maxn + ns - 1) / ns + 63) / 64 * 64;
+        const double util = (double)total / ((double)nreg * ns * threads);
+        if (util >= 0.75 && slots_compiled(nreg, true, (int)std::min<int64_t>(ns, 1 << 20))) {
+            *s = LaunchShape{(int)threads, (int)ns, true, 0};
+            return true;
+        }
+    }
     double best = -1.0;
     for (int threads = 64; threads <= 1024; threads += 64) {
-        const double dist = std::fabs(std::log2(threads / 256.0));
+        const double dist = std::fabs(std::log2(threads / 128.0));
         const int64_t ns_rm = (maxn + threads - 1) / threads;
-        if (slots_compiled(nreg, half, true, (int)std::min<int64_t>(ns_rm, 1 << 20))) {
+        if (slots_compiled(nreg, true, (int)std::min<int64_t>(ns_rm, 1 << 20))) {
             const double util = (double)total / ((double)nreg * ns_rm * threads);
-            const double score = util - 0.01 * dist + 0.001;
+            const double score = util - 0.01 * dist;
             if (score > best) {
                 best = score;
                 *s = LaunchShape{threads, (int)ns_rm, true, 0};
@@ -110,9 +124,9 @@ bool choose_shape(const int64_t *n, int nreg, bool half, LaunchShape *s)
         }
         const int64_t need = (total + threads - 1) / threads;
         for (int ns : kMixedSlots) {
-            if (ns < need || !slots_compiled(nreg, half, false, ns)) continue;
+            if (ns < need || !slots_compiled(nreg, false, ns)) continue;
             const double util = (double)total / ((double)ns * threads);
-            const double score = util - 0.01 * dist;
+            const double score = util - 0.01 * dist + 0.001;
             if (score > best) {
                 best = score;
                 *s = LaunchShape{threads, ns, false, 0};
@@ -244,8 +258,8 @@ int qkrope_run_table(qkrope_handle h, const void *q, const void *k, const void *
     if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(QKROPE_ERR_INVALID, "eps must be finite and >= 0");
     if (D % 8 || D > 256) return fail(QKROPE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and <= 256");
     const bool half = !interleaved;
-    if (half && (D % 16 || R % 16))
-        return fail(QKROPE_ERR_UNSUPPORTED, "half-split pairing needs head_dim and rotary_dim multiples of 16");
+    if (half && R % 16)
+        return fail(QKROPE_ERR_UNSUPPORTED, "half-split pairing needs rotary_dim to be a multiple of 16");
     if (T >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "num_tokens must be < 2^31");
     if (T == 0 || Hq + Hk == 0) return ok();
 
@@ -287,11 +301,10 @@ int qkrope_run_table(qkrope_handle h, const void *q, const void *k, const void *
         overlap(rko, rwq) || overlap(rko, rwk))
         return fail(QKROPE_ERR_INVALID, "k_out overlaps another argument");
 
-    const int units = half ? D / 16 : D / 8;
-    const int L = next_pow2(units);
+    const int L = next_pow2(D / 8);           // lanes per head: one 16-byte chunk each
     const int64_t n_units[2] = {(int64_t)Hq * L, (int64_t)Hk * L};
     LaunchShape shape;
-    if (!choose_shape(n_units, 2, half, &shape))
+    if (!choose_shape(n_units, 2, &shape))
         return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
 
     KernelArgs a;
@@ -312,7 +325,6 @@ int qkrope_run_table(qkrope_handle h, const void *q, const void *k, const void *
     a.table = rope_table;
     a.table_stride = table_token_stride;
     a.num_tokens = T;
-    a.tokens_per_block = 1;
     a.head_dim = D;
     a.rotary_dim = R;
     a.lanes_per_head = L;
@@ -322,7 +334,7 @@ int qkrope_run_table(qkrope_handle h, const void *q, const void *k, const void *
     a.inv_count[1] = (float)(1.0 / (double)(across ? (int64_t)Hk * D : D));
     a.qk_scale = 1.0f;
     a.v_scale = 1.0f;
-    shape.blocks = (T + a.tokens_per_block - 1) / a.tokens_per_block;
+    shape.blocks = T;
 
     KernelKey key;
     key.head_dim_tpl = 0;
@@ -399,10 +411,10 @@ int qkrope_run_3d(qkrope_handle h, const void *qkv, const void *q_weight, const 
     }
 
     const bool half = !interleave;
-    const int units = half ? D / 16 : D / 8;   // a power of two for head_dim 64/128/256
+    const int units = D / 8;                   // 16-byte chunks per head: 8, 16 or 32
     const int64_t n_units[3] = {(int64_t)Hq * units, (int64_t)Hk * units, (int64_t)Hv * units};
     LaunchShape shape;
-    if (!choose_shape(n_units, 3, half, &shape))
+    if (!choose_shape(n_units, 3, &shape))
         return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
 
     KernelArgs a;
@@ -424,7 +436,6 @@ int qkrope_run_3d(qkrope_handle h, const void *qkv, const void *q_weight, const 
     a.weight[0] = static_cast<const uint16_t *>(q_weight);
     a.weight[1] = static_cast<const uint16_t *>(k_weight);
     a.num_tokens = T;
-    a.tokens_per_block = 1;
     a.head_dim = D;
     a.rotary_dim = D;
     a.lanes_per_head = units;
@@ -458,7 +469,7 @@ int qkrope_run_3d(qkrope_handle h, const void *qkv, const void *q_weight, const 
         a.omega_rev[k] = (float)(omega / two_pi);
         a.axis[k] = (uint8_t)axis;
     }
-    shape.blocks = (T + a.tokens_per_block - 1) / a.tokens_per_block;
+    shape.blocks = T;
 
     KernelKey key;
     key.head_dim_tpl = D;

@@ -31,11 +31,10 @@ struct KernelArgs {
     const void *table;         // table form: [T, R] cos|sin, fp32 or bf16
     int64_t table_stride;      // elements
 
-    int64_t num_tokens;
-    int tokens_per_block;      // consecutive tokens one workgroup walks through
+    int64_t num_tokens;        // = grid size: one workgroup per token
     int head_dim;              // D
     int rotary_dim;            // R (== D for the 3D form)
-    int lanes_per_head;        // L: power of two >= units per head
+    int lanes_per_head;        // L: power of two >= head_dim / 8 (16-byte chunks per head)
     float eps;
     float inv_count[2];        // 1 / (elements the Q, K norm averages over)
     float qk_scale;            // FP8 scale for Q/K outputs (1 for bf16)
@@ -77,16 +76,15 @@ hipError_t launch_table_interleaved(const KernelKey &key, const LaunchShape &sha
 hipError_t launch_table_halfsplit(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
 
 // Slot counts the kernels are compiled for: region-major 1..4 slots per region, mixed 1, 2, 4
-// slots per lane, limited so that a lane holds at most kMaxChunks 16-byte input chunks per token
-// (half-split units are two chunks).
+// slots per lane, limited so that a lane holds at most kMaxChunks 16-byte chunks per token.
 constexpr int kMaxSlotsRegionMajor = 4;
 constexpr int kMixedSlots[] = {1, 2, 4};
 constexpr int kMaxChunks = 8;
 
-constexpr bool slots_compiled(int nreg, bool half, bool region_major, int ns)
+constexpr bool slots_compiled(int nreg, bool region_major, int ns)
 {
     return (region_major ? ns >= 1 && ns <= kMaxSlotsRegionMajor : (ns == 1 || ns == 2 || ns == 4)) &&
-           (region_major ? nreg * ns : ns) * (half ? 2 : 1) <= kMaxChunks;
+           (region_major ? nreg * ns : ns) <= kMaxChunks;
 }
 
 }  // namespace qkrope

@@ -13,26 +13,29 @@
 // Work decomposition (MI355X-first; the pages give no kernel design for this hardware):
 //   * The operation is HBM-bound (a few flops per byte), so the design goal is 16-byte coalesced
 //     loads and stores with many bytes in flight, and little ALU work per byte.
-//   * A workgroup owns whole tokens and walks `tokens_per_block` consecutive ones.
-//   * A token's Q, K (and V) rows are cut into units: one 16-byte chunk of 8 bf16 (interleaved
-//     pairs never leave a chunk) or, for half-split/NeoX pairing, the two chunks at dims 8m and
-//     8m + R/2 that hold both halves of 8 rotation pairs, so no lane needs a neighbour's data.
-//     Each head gets L = 2^k >= units-per-head consecutive lanes; lane `tid` owns unit
-//     tid mod L of several heads (its slots). Because the workgroup size is a multiple of L,
-//     every slot of a lane covers the same dims, so angles and per-head weights are fetched
-//     once per lane.
+//   * One workgroup per token (grid = tokens). On MI355X the hardware's own workgroup
+//     scheduling hides memory latency better than a software-pipelined walk over several
+//     tokens per workgroup, which measured slower at every depth tried.
+//   * A token's Q, K (and V) rows are cut into units of one 16-byte chunk (8 bf16), so every
+//     load and store instruction of a wave covers whole contiguous cache lines. Interleaved
+//     pairs never leave a chunk. Half-split/NeoX pairs (d, d + R/2) join chunk c with chunk
+//     c + R/16 of the same head: each lane normalises its own chunk, then fetches its partner
+//     lane's normalised values with a cross-lane permute and writes only its own chunk.
+//     Each head gets L = 2^k >= D/8 consecutive lanes; lane `tid` owns chunk tid mod L of
+//     several heads (its slots). Because the workgroup size is a multiple of L, every slot of a
+//     lane covers the same dims, so angles and per-head weights are fetched once per lane.
 //   * Two slot layouts. Region-major (SU): each region (Q, K, V) has NS slots per lane, slot i
 //     covering heads (tid + i*nth)/L of that region; region, base pointers and weights of every
 //     slot are compile-time/scalar. Mixed: the regions' units are concatenated and lane-slot j
 //     covers unit tid + j*nth of the token, whichever region it falls in (fills the lanes when
 //     a region's unit count does not divide the workgroup, e.g. 20 heads of 64).
-//   * Sum of squares: per-head norm reduces inside the L lanes of the head with xor shuffles;
-//     across-heads norm reduces each wave, then combines the waves through LDS.
+//   * Sum of squares: per-head norm reduces inside the L lanes of the head with DPP/permlane
+//     butterflies; across-heads norm reduces each wave, then combines the waves through LDS.
 //   * 3D angles: lanes k < head_dim/2 compute (cos, sin) of pair k once per token (angle in
 //     revolutions, fract, hardware sin/cos), scaled by the attention factor, into LDS; the
-//     barrier that publishes them is the one the across-heads reduction needs anyway. LDS is
-//     double-buffered by token parity, so one barrier per token suffices.
-//   * V units are copied (or E4M3-quantised) and stored before the barrier.
+//     barrier that publishes them is the one the across-heads reduction needs anyway.
+//   * Phases per token: all loads, reductions and the barrier, all outputs computed into
+//     registers, then all stores, so no data wait ever sits behind an outstanding store.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -44,6 +47,7 @@ namespace qkrope {
 namespace dev {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---- number formats ---------------------------------------------------------------------------
@@ -81,16 +85,30 @@ __device__ __forceinline__ float sat_e4m3(float y)
     return __builtin_fabsf(y) > 448.0f ? __builtin_copysignf(448.0f, y) : y;
 }
 
+// Each conversion writes one 16-bit half of its destination and keeps the other; the first of
+// each pair starts from a register that is live anyway (its bits are overwritten by the second).
 __device__ __forceinline__ uint2 pack8_e4m3(const float y[8])
 {
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(y[0]), sat_e4m3(y[1]), 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(y[2]), sat_e4m3(y[3]), lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(y[4]), sat_e4m3(y[5]), 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(y[6]), sat_e4m3(y[7]), hi, true);
+    const float a0 = sat_e4m3(y[0]), a1 = sat_e4m3(y[1]), a2 = sat_e4m3(y[2]), a3 = sat_e4m3(y[3]);
+    const float b0 = sat_e4m3(y[4]), b1 = sat_e4m3(y[5]), b2 = sat_e4m3(y[6]), b3 = sat_e4m3(y[7]);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, __float_as_int(a2), false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(b0, b1, __float_as_int(b2), false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(b2, b3, hi, true);
     return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
 // ---- memory -----------------------------------------------------------------------------------
+
+// Cache policy of the streamed activations: every input byte is read once and every output
+// byte written once, so both carry the non-temporal hint. Weights and tables, which every
+// workgroup re-reads, use normal loads.
+#ifndef QKROPE_NT_STORE
+#define QKROPE_NT_STORE 1
+#endif
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte load at a (usually uniform) base plus a 32-bit unsigned byte offset, the form the
 // global_load saddr+voffset encoding takes: one VGPR per address.
@@ -99,15 +117,35 @@ __device__ __forceinline__ uint4 ld16(const void *base, uint32_t byte_off)
     return *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(base) + byte_off);
 }
 
+// The same for streamed (read-once) activations; NT selects the non-temporal hint.
+template <bool NT>
+__device__ __forceinline__ uint4 ld16_stream(const void *base, uint32_t byte_off)
+{
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(base) + byte_off);
+    const u32x4 v = NT ? __builtin_nontemporal_load(p) : *p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void st16_stream(uint8_t *p, uint4 v)
+{
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    if (QKROPE_NT_STORE) __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+    else *reinterpret_cast<u32x4 *>(p) = w;
+}
+
+__device__ __forceinline__ void st8_stream(uint8_t *p, uint2 v)
+{
+    const u32x2 w = {v.x, v.y};
+    if (QKROPE_NT_STORE) __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
+    else *reinterpret_cast<u32x2 *>(p) = w;
+}
+
 // Store 8 outputs (16 bytes of bf16 or 8 bytes of E4M3) at element `elem` of a row.
 template <bool FP8>
 __device__ __forceinline__ void store8(uint8_t *row, uint32_t elem, const float y[8])
 {
-    if (FP8) {
-        *reinterpret_cast<uint2 *>(row + elem) = pack8_e4m3(y);
-    } else {
-        *reinterpret_cast<uint4 *>(row + 2 * elem) = pack8_bf16(y);
-    }
+    if (FP8) st8_stream(row + elem, pack8_e4m3(y));
+    else st16_stream(row + 2 * elem, pack8_bf16(y));
 }
 
 // n / d for n < 2^31 with a host-computed magic pair (m, l): q = (mulhi(n, m) + n) >> l.
@@ -120,20 +158,56 @@ template <typename T>
 __device__ __forceinline__ T sel3(int r, T a, T b, T c) { return r == 0 ? a : (r == 1 ? b : c); }
 
 // ---- reductions -------------------------------------------------------------------------------
+//
+// All on the VALU: DPP quad permutations and row mirrors inside each 16-lane row, then the gfx950
+// row-swap permutes across rows. Each step adds a lane's value to its partner's, and IEEE
+// addition is commutative, so every lane of a group ends with a bitwise identical sum.
 
-// Sum over aligned groups of `width` lanes (a power of two <= 64) with xor butterflies.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    return v + __builtin_amdgcn_update_dpp(0.0f, v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppRowMirror = 0x140;    // lane i <-> 15-i inside each 16 lanes
+
+__device__ __forceinline__ float swap16_add(float v)   // rows 0+1 and 2+3
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float swap32_add(float v)   // lanes 0-31 + 32-63
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Sum over aligned groups of `width` lanes (1, 2, 4, ..., 64); `width` is uniform.
 __device__ __forceinline__ float group_sum(float v, int width)
 {
-    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (width >= 2) v = dpp_add<kDppQuadXor1>(v);
+    if (width >= 4) v = dpp_add<kDppQuadXor2>(v);
+    if (width >= 8) v = dpp_add<kDppHalfMirror>(v);
+    if (width >= 16) v = dpp_add<kDppRowMirror>(v);
+    if (width >= 32) v = swap16_add(v);
+    if (width >= 64) v = swap32_add(v);
     return v;
 }
 
-__device__ __forceinline__ float sumsq8(const float x[8])
+__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
+
+// Sum of squares of the 8 bf16 of a chunk, from the packed pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float sumsq_packed(const uint4 v, float acc)
 {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = __builtin_fmaf(x[i], x[i], s);
-    return s;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), __builtin_bit_cast(bf16x2, v.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), __builtin_bit_cast(bf16x2, v.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), __builtin_bit_cast(bf16x2, v.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), __builtin_bit_cast(bf16x2, v.w), acc, false);
+    return acc;
 }
 
 // ---- the kernel -------------------------------------------------------------------------------
@@ -148,37 +222,45 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     constexpr bool IS3D = (SRC == kSrc3D);
     constexpr int NREG = IS3D ? 3 : 2;          // regions: Q, K (, V)
     constexpr int NSLOT = SU ? NREG * NS : NS;
-    constexpr int NPAIR = HALF ? 8 : 4;         // rotation pairs per unit
+    constexpr int NPAIR = HALF ? 8 : 4;         // rotation pairs a chunk takes part in
     constexpr bool NEED_BARRIER = IS3D || NORM == kNormAcross;
     constexpr int ESIZE = FP8 ? 1 : 2;          // output bytes per element
 
-    __shared__ f32x2 s_cs[IS3D ? 2 : 1][IS3D ? kMaxPairs : 1];
-    __shared__ f32x2 s_red[NORM == kNormAcross ? 2 : 1][16];
+    // 3D angles of the token: per pair (cos, -sin, cos, sin), so a half-split lane reads its
+    // signed pair directly (first half: y = n cos - n' sin, second half: y = n cos + n' sin).
+    __shared__ f32x4 s_cs[IS3D ? kMaxPairs : 1];
+    __shared__ f32x2 s_red[16];
 
     const int D = DT > 0 ? DT : a.head_dim;
     const int R = IS3D ? D : a.rotary_dim;
-    const int units = HALF ? D / 16 : D / 8;
+    const int units = D / 8;                    // chunks per head
     const int L = DT > 0 ? units : a.lanes_per_head;
     const int lgL = __builtin_ctz(L);
-    const int P = HALF ? R / 16 : 0;            // rotated chunk pairs per head (half-split)
     const int tid = threadIdx.x;
     const int nth = blockDim.x;
-    const int u = tid & (L - 1);
+    const int u = tid & (L - 1);                // this lane's chunk inside every head it covers
     const bool unit_ok = u < units;
+    const uint32_t off0 = 8 * u;                // element offset of the chunk inside a head
 
-    // Element offsets of this lane's unit inside a head, and whether it is rotated.
-    uint32_t off0, off1;
+    // Rotation geometry of the chunk.
+    //   interleaved: pairs (2i, 2i+1) inside the chunk, angles 4u .. 4u+3 (those < R/2 rotate)
+    //   half-split:  chunk u < P pairs with chunk u + P (P = R/16), angles 8u .. 8u+7; the
+    //                partner lane is tid +- P; chunks >= 2P pass through.
+    const int P = HALF ? R / 16 : 0;
     bool rotated;
+    int pair0, partner;
+    float half_sign = 1.0f;                     // first half: y = n c - n' s; second: n c + n' s
     if (HALF) {
-        rotated = u < P;
-        off0 = rotated ? 8 * u : 16 * u;        // pass-through units take chunk pairs 2u, 2u+1
-        off1 = rotated ? 8 * (u + P) : 16 * u + 8;
+        rotated = u < 2 * P;
+        const bool first = u < P;
+        pair0 = 8 * (first ? u : u - P);
+        partner = rotated ? ((tid & 63) + (first ? P : -P)) : (tid & 63);
+        half_sign = first ? -1.0f : 1.0f;
     } else {
         rotated = 8 * u < R;
-        off0 = 8 * u;
-        off1 = 0;
+        pair0 = 4 * u;
+        partner = tid & 63;
     }
-    const int pair0 = HALF ? 8 * u : 4 * u;     // first rotation pair (angle index) of the unit
 
     // Slot -> region (3 = idle) and the element offset of the slot's head inside its region row.
     const int Hq = a.heads[kQ], Hk = a.heads[kK], Hv = NREG == 3 ? a.heads[kV] : 0;
@@ -204,16 +286,10 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     }
 
     // Per-head norm weights ([head_dim], shared by every head) stay packed in registers.
-    uint4 wq0 = make_uint4(0, 0, 0, 0), wq1 = wq0, wk0 = wq0, wk1 = wq0;
+    uint4 wq = make_uint4(0, 0, 0, 0), wk = wq;
     if (NORM == kNormPerHead && unit_ok) {
-        if (Hq > 0) {
-            wq0 = ld16(a.weight[0], 2 * off0);
-            if (HALF) wq1 = ld16(a.weight[0], 2 * off1);
-        }
-        if (Hk > 0) {
-            wk0 = ld16(a.weight[1], 2 * off0);
-            if (HALF) wk1 = ld16(a.weight[1], 2 * off1);
-        }
+        if (Hq > 0) wq = ld16(a.weight[0], 2 * off0);
+        if (Hk > 0) wk = ld16(a.weight[1], 2 * off0);
     }
 
     // 3D: this lane's pair (tid < D/2) frequency in revolutions and its position axis.
@@ -224,34 +300,24 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         axis = a.axis[tid];
     }
 
-    const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_block;
-    int64_t t_end = t_begin + a.tokens_per_block;
-    if (t_end > a.num_tokens) t_end = a.num_tokens;
-
-    int buf = 0;
-    for (int64_t t = t_begin; t < t_end; ++t, buf ^= 1) {
-        // Row bases of this token (scalar).
-        const uint16_t *in_q = a.in[kQ] + t * a.in_stride[kQ];
-        const uint16_t *in_k = a.in[kK] + t * a.in_stride[kK];
-        const uint16_t *in_v = NREG == 3 ? a.in[kV] + t * a.in_stride[kV] : in_k;
-        uint8_t *out_q = static_cast<uint8_t *>(a.out[kQ]) + t * a.out_stride[kQ] * ESIZE;
-        uint8_t *out_k = static_cast<uint8_t *>(a.out[kK]) + t * a.out_stride[kK] * ESIZE;
-        uint8_t *out_v = NREG == 3 ? static_cast<uint8_t *>(a.out[kV]) + t * a.out_stride[kV] * ESIZE
-                                   : out_k;
-
-        // -- load every unit of the token, and across-heads weights (all in flight before use)
-        uint4 x0[NSLOT], x1[NSLOT], wa0[NSLOT], wa1[NSLOT];
+    const int64_t t = blockIdx.x;              // one token per workgroup
+    {
+        // -- loads: every chunk of every slot, and the across-heads weights. Issued
+        // unconditionally from one basic block so all are in flight together; an idle slot
+        // reads its row's first chunk (in bounds, and read by another lane anyway).
+        uint4 x[NSLOT], wa[NSLOT];
+        {
+            const uint16_t *in_q = a.in[kQ] + t * a.in_stride[kQ];
+            const uint16_t *in_k = a.in[kK] + t * a.in_stride[kK];
+            const uint16_t *in_v = NREG == 3 ? a.in[kV] + t * a.in_stride[kV] : in_k;
 #pragma unroll
-        for (int j = 0; j < NSLOT; ++j) {
-            if (ok[j]) {
-                const int r = reg[j];
-                const uint16_t *row = sel3(r, in_q, in_k, in_v);
-                x0[j] = ld16(row, 2 * (hoff[j] + off0));
-                if (HALF) x1[j] = ld16(row, 2 * (hoff[j] + off1));
-                if (NORM == kNormAcross && r < 2) {
-                    const uint16_t *w = r == 0 ? a.weight[0] : a.weight[1];
-                    wa0[j] = ld16(w, 2 * (hoff[j] + off0));
-                    if (HALF) wa1[j] = ld16(w, 2 * (hoff[j] + off1));
+            for (int j = 0; j < NSLOT; ++j) {
+                const int r = reg[j] < 3 ? reg[j] : 0;
+                const uint32_t o = ok[j] ? 2 * (hoff[j] + off0) : 0u;
+                x[j] = ld16_stream<true>(sel3(r, in_q, in_k, in_v), o);
+                if (NORM == kNormAcross && (SU ? r < 2 : true)) {
+                    const uint16_t *w = r == 1 ? a.weight[1] : a.weight[0];
+                    wa[j] = ld16(w, (ok[j] && r < 2) ? o : 0u);
                 }
             }
         }
@@ -270,8 +336,9 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                 const uint32_t pos = axis == 0 ? pf : (axis == 1 ? ph : pw);
                 // angle in revolutions, reduced to [0, 1): sin/cos(2*pi*rev) in hardware
                 const float rev = __builtin_amdgcn_fractf((float)pos * omega_rev);
-                s_cs[buf][tid] = f32x2{__builtin_amdgcn_cosf(rev) * a.attention_factor,
-                                       __builtin_amdgcn_sinf(rev) * a.attention_factor};
+                const float c = __builtin_amdgcn_cosf(rev) * a.attention_factor;
+                const float sn = __builtin_amdgcn_sinf(rev) * a.attention_factor;
+                s_cs[tid] = f32x4{c, -sn, c, sn};
             }
         } else if (unit_ok && rotated) {
             const int half = R / 2;
@@ -279,36 +346,31 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 #pragma unroll
             for (int e = 0; e < NPAIR; ++e) {
                 const int i = pair0 + e;
-                float c = 1.0f, s = 0.0f;
+                float c = 1.0f, sn = 0.0f;
                 if (HALF || i < half) {
                     if (SRC == kSrcTableF32) {
                         const float *tab = static_cast<const float *>(a.table) + trow;
                         c = tab[i];
-                        s = tab[half + i];
+                        sn = tab[half + i];
                     } else {
                         const uint16_t *tab = static_cast<const uint16_t *>(a.table) + trow;
                         c = __uint_as_float((uint32_t)tab[i] << 16);
-                        s = __uint_as_float((uint32_t)tab[half + i] << 16);
+                        sn = __uint_as_float((uint32_t)tab[half + i] << 16);
                     }
                 }
                 cs_c[e] = c;
-                cs_s[e] = s;
+                cs_s[e] = HALF ? sn * half_sign : sn;
             }
         }
 
-        // -- sum of squares
+        // -- sums of squares (Q and K slots only)
         float ss[NSLOT];
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
             ss[j] = 0.0f;
-            if (NORM != kNormNone && ok[j] && reg[j] < 2) {
-                float x[8];
-                unpack8(x0[j], x);
-                ss[j] = sumsq8(x);
-                if (HALF) {
-                    unpack8(x1[j], x);
-                    ss[j] += sumsq8(x);
-                }
+            if (NORM != kNormNone) {
+                const float v = sumsq_packed(x[j], 0.0f);
+                ss[j] = (ok[j] && reg[j] < 2) ? v : 0.0f;
             }
         }
         if (NORM == kNormPerHead) {
@@ -321,115 +383,101 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                 sq += reg[j] == kQ ? ss[j] : 0.0f;
                 sk += reg[j] == kK ? ss[j] : 0.0f;
             }
-            sq = group_sum(sq, 64);
-            sk = group_sum(sk, 64);
-            if ((tid & 63) == 0) s_red[buf][tid >> 6] = f32x2{sq, sk};
-        }
-
-        // -- V: copy or quantise, no dependence on the reductions
-        if (NREG == 3) {
-#pragma unroll
-            for (int j = 0; j < NSLOT; ++j) {
-                if (!(ok[j] && reg[j] == kV)) continue;
-                uint8_t *vrow = out_v;
-                if (FP8) {
-                    float x[8];
-                    unpack8(x0[j], x);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] *= a.v_scale;
-                    store8<true>(vrow, hoff[j] + off0, x);
-                    if (HALF) {
-                        unpack8(x1[j], x);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) x[i] *= a.v_scale;
-                        store8<true>(vrow, hoff[j] + off1, x);
-                    }
-                } else {
-                    *reinterpret_cast<uint4 *>(vrow + 2 * (hoff[j] + off0)) = x0[j];
-                    if (HALF) *reinterpret_cast<uint4 *>(vrow + 2 * (hoff[j] + off1)) = x1[j];
-                }
-            }
+            sq = wave_sum(sq);
+            sk = wave_sum(sk);
+            if ((tid & 63) == 0) s_red[tid >> 6] = f32x2{sq, sk};
         }
 
         if (NEED_BARRIER) __syncthreads();
 
         float rq = 1.0f, rk = 1.0f;
         if (NORM == kNormAcross) {
-            float sq = 0.0f, sk = 0.0f;
-            const int nw = nth >> 6;
-            for (int w = 0; w < nw; ++w) {
-                const f32x2 p = s_red[buf][w];
-                sq += p.x;
-                sk += p.y;
-            }
+            // every wave sums the per-wave partials: lane w of each 16-lane row reads wave w's
+            const int w = tid & 15;
+            const f32x2 p = w < (nth >> 6) ? s_red[w] : f32x2{0.0f, 0.0f};
+            const float sq = group_sum(p.x, 16), sk = group_sum(p.y, 16);
             rq = __builtin_amdgcn_rsqf(sq * a.inv_count[0] + a.eps);
             rk = __builtin_amdgcn_rsqf(sk * a.inv_count[1] + a.eps);
         }
         if (IS3D && unit_ok) {
+            // interleaved and second-half lanes read (cos, sin), first-half lanes (cos, -sin)
+            const f32x2 *tab = reinterpret_cast<const f32x2 *>(s_cs) + (HALF && half_sign < 0.0f ? 0 : 1);
 #pragma unroll
             for (int e = 0; e < NPAIR; ++e) {
-                const f32x2 cs = s_cs[buf][pair0 + e];
+                const f32x2 cs = tab[2 * (pair0 + e)];
                 cs_c[e] = cs.x;
                 cs_s[e] = cs.y;
             }
         }
 
-        // -- Q and K: normalise, rotate, round once, store
+        // -- every slot's outputs, computed unconditionally (idle slots compute on the chunk
+        // they loaded and are not stored): normalise, rotate, round once. V is a bit copy or
+        // an E4M3 quantisation.
+        uint4 pk[NSLOT];                    // bf16 results (FP8: .xy hold the 8 codes)
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
-            if (!ok[j] || reg[j] >= 2) continue;
+            const bool isv = NREG == 3 && reg[j] == kV;   // compile-time in the region-major layout
             const bool isq = reg[j] == 0;
-            float scale = FP8 ? a.qk_scale : 1.0f;
-            if (NORM == kNormAcross) scale *= isq ? rq : rk;
+            float n[8];
+            unpack8(x[j], n);
+            float scale = FP8 ? (isv ? a.v_scale : a.qk_scale) : 1.0f;
+            if (NORM == kNormAcross && !isv) scale *= isq ? rq : rk;
             if (NORM == kNormPerHead)
                 scale *= __builtin_amdgcn_rsqf(ss[j] * (isq ? a.inv_count[0] : a.inv_count[1]) + a.eps);
-
-            float n0[8], n1[8];
-            unpack8(x0[j], n0);
-            if (HALF) unpack8(x1[j], n1);
-            if (NORM != kNormNone) {
+            if (NORM != kNormNone && !isv) {
                 float w[8];
-                unpack8(NORM == kNormAcross ? wa0[j] : (isq ? wq0 : wk0), w);
+                unpack8(NORM == kNormAcross ? wa[j] : (isq ? wq : wk), w);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) n0[i] *= w[i];
-                if (HALF) {
-                    unpack8(NORM == kNormAcross ? wa1[j] : (isq ? wq1 : wk1), w);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) n1[i] *= w[i];
-                }
+                for (int i = 0; i < 8; ++i) n[i] *= w[i];
             }
+            if (FP8 || !isv) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                n0[i] *= scale;
-                if (HALF) n1[i] *= scale;
+                for (int i = 0; i < 8; ++i) n[i] *= scale;
             }
-
-            float y0[8], y1[8];
-            if (!rotated) {
+            float y[8];
+            if (HALF) {
+                // partner chunk's normalised values (all lanes take part in the permute)
+                float np[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    y0[i] = n0[i];
-                    if (HALF) y1[i] = n1[i];
-                }
-            } else if (HALF) {
+                for (int i = 0; i < 8; ++i) np[i] = __shfl(n[i], partner, 64);
+                const bool rot = rotated && !isv;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    y0[e] = n0[e] * cs_c[e] - n1[e] * cs_s[e];
-                    y1[e] = n1[e] * cs_c[e] + n0[e] * cs_s[e];
-                }
+                for (int e = 0; e < 8; ++e)
+                    y[e] = rot ? n[e] * cs_c[e] + np[e] * cs_s[e] : n[e];
+            } else if (!rotated || isv) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = n[i];
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float xa = n0[2 * e], xb = n0[2 * e + 1];
+                    const float xa = n[2 * e], xb = n[2 * e + 1];
                     const bool on = IS3D || pair0 + e < R / 2;
-                    y0[2 * e] = on ? xa * cs_c[e] - xb * cs_s[e] : xa;
-                    y0[2 * e + 1] = on ? xb * cs_c[e] + xa * cs_s[e] : xb;
+                    y[2 * e] = on ? xa * cs_c[e] - xb * cs_s[e] : xa;
+                    y[2 * e + 1] = on ? xb * cs_c[e] + xa * cs_s[e] : xb;
                 }
             }
+            if (FP8) {
+                const uint2 c = pack8_e4m3(y);
+                pk[j] = make_uint4(c.x, c.y, 0, 0);
+            } else if (isv) {
+                pk[j] = x[j];                           // V: bit copy
+            } else {
+                pk[j] = pack8_bf16(y);
+            }
+        }
 
-            uint8_t *orow = isq ? out_q : out_k;
-            store8<FP8>(orow, hoff[j] + off0, y0);
-            if (HALF) store8<FP8>(orow, hoff[j] + off1, y1);
+        // -- all stores last
+        uint8_t *out_q = static_cast<uint8_t *>(a.out[kQ]) + t * a.out_stride[kQ] * ESIZE;
+        uint8_t *out_k = static_cast<uint8_t *>(a.out[kK]) + t * a.out_stride[kK] * ESIZE;
+        uint8_t *out_v = NREG == 3 ? static_cast<uint8_t *>(a.out[kV]) + t * a.out_stride[kV] * ESIZE
+                                   : out_k;
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+            if (!ok[j]) continue;
+            uint8_t *orow = sel3(reg[j], out_q, out_k, out_v);
+            const uint32_t e0 = hoff[j] + off0;
+            if (FP8) st8_stream(orow + e0, make_uint2(pk[j].x, pk[j].y));
+            else st16_stream(orow + 2 * e0, pk[j]);
         }
     }
 }
@@ -447,7 +495,7 @@ hipError_t go(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 template <int DT, bool HALF, int NORM, int SRC, bool FP8, int NS, bool SU>
 hipError_t go_if(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    if constexpr (slots_compiled(SRC == kSrc3D ? 3 : 2, HALF, SU, NS))
+    if constexpr (slots_compiled(SRC == kSrc3D ? 3 : 2, SU, NS))
         return go<DT, HALF, NORM, SRC, FP8, NS, SU>(s, a, st);
     else
         return hipErrorInvalidValue;
