@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the benchm
 leg may import this module. The HIP product path never does, and this module imports nothing from
 the product package.
 
-Inputs are CPU tensors or numpy arrays holding bf16 bit patterns (uint16) or float32 tables;
-outputs are float64 numpy arrays, unrounded, plus the encoders that turn them into bf16 bits and
-OCP E4M3 codes.
+Inputs are CPU tensors (bf16 / float16 / float32) or numpy arrays (uint16 bf16 bit patterns,
+float16, float32, float64 tables); outputs are float64 numpy arrays, unrounded, plus the encoders
+that turn them into bf16 or binary16 bits and OCP E4M3 codes.
 """
 from __future__ import annotations
 
@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SOURCE = os.path.join(_HERE, "oracle.c")
 
 NORM_MODES = {"none": 0, "per_head": 1, "across_heads": 2}
-TABLE_BF16, TABLE_F32, TABLE_F64 = 0, 1, 2
+TABLE_BF16, TABLE_F32, TABLE_F64, TABLE_F16 = 0, 1, 2, 3
+ACT_BF16, ACT_F16 = 0, 1
 
 
 def build(verbose: bool = False) -> str:
@@ -49,6 +50,17 @@ def lib() -> ctypes.CDLL:
         L.oracle_run_table.argtypes = [P, P, P, P, P, I, D, I64, I, I, I, I, I, I,
                                        I64, I64, I64, P, P]
         L.oracle_run_table.restype = I
+        L.oracle_run_table_split.argtypes = [P, P, P, P, I, P, P, I, D, I64, I, I, I, I, I, I,
+                                             I64, I64, I64, I64, P, P]
+        L.oracle_run_table_split.restype = I
+        L.oracle_sumsq_3d.argtypes = [P, I64, I, I, I, I, P]
+        L.oracle_sumsq_3d.restype = I
+        L.oracle_f16_encode.argtypes = [D]
+        L.oracle_f16_encode.restype = ctypes.c_uint16
+        L.oracle_f16_decode.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_decode.restype = D
+        L.oracle_encode_f16_array.argtypes = [P, I64, P]
+        L.oracle_encode_f16_array.restype = None
         L.oracle_run_3d.argtypes = [P, P, P, I64, I64, I, I, I, I, I, I, I, I, I, I,
                                     D, D, I, D, D, D, D, I, P, P, P]
         L.oracle_run_3d.restype = I
@@ -90,19 +102,39 @@ def _bits16(x) -> np.ndarray:
     return x
 
 
+def _act_bits(x):
+    """(uint16 bits, activation code) of 16-bit activations: torch bf16 or float16, numpy
+    uint16 (bf16 bit patterns) or float16."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach()
+        if x.dtype == torch.float16:
+            x = x.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            return np.ascontiguousarray(x), ACT_F16
+        return _bits16(x), ACT_BF16
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        return x.view(np.uint16), ACT_F16
+    return _bits16(x), ACT_BF16
+
+
 def _table(x):
-    """(array, dtype code) for a rope table: torch bf16/fp32, numpy uint16/float32/float64."""
+    """(array, dtype code) for a rope table: torch bf16/float16/fp32, numpy uint16 (bf16 bits)
+    /float16/float32/float64."""
     if hasattr(x, "detach"):
         import torch
         x = x.detach().cpu().contiguous()
         if x.dtype == torch.float32:
             return np.ascontiguousarray(x.numpy()), TABLE_F32
-        return _bits16(x), TABLE_BF16
+        bits, act = _act_bits(x)
+        return bits, TABLE_F16 if act == ACT_F16 else TABLE_BF16
     x = np.ascontiguousarray(x)
     if x.dtype == np.float64:
         return x, TABLE_F64
     if x.dtype == np.float32:
         return x, TABLE_F32
+    if x.dtype == np.float16:
+        return x.view(np.uint16), TABLE_F16
     return _bits16(x), TABLE_BF16
 
 
@@ -113,25 +145,52 @@ def _ptr(a: np.ndarray):
 # --- the two forms -----------------------------------------------------------------------------
 
 def run_table(q, k, q_weight, k_weight, rope_table, eps, *, rotary_dim=None,
-              interleaved=False, norm_mode="per_head"):
-    """fp64 table form. q [T,Hq,D], k [T,Hk,D] bf16; table [T,R]. Returns (q_out, k_out) fp64."""
-    qb, kb = _bits16(q), _bits16(k)
+              interleaved=False, norm_mode="per_head", sin_table=None):
+    """fp64 table form. q [T,Hq,D], k [T,Hk,D] bf16 or float16 (weights alike).
+
+    With sin_table None, rope_table is the pages' packed [T, >=R] = [cos | sin] table. Otherwise
+    rope_table is the [T, >=R/2] cosine table and sin_table the matching sine table (the split
+    layout). Returns (q_out, k_out) fp64, unrounded."""
+    qb, act = _act_bits(q)
+    kb, act_k = _act_bits(k)
+    if act_k != act:
+        raise ValueError("q and k must share the activation dtype")
     if qb.ndim != 3 or kb.ndim != 3:
         raise ValueError("q and k must be [tokens, heads, head_dim]")
     T, Hq, D = qb.shape
     Hk = kb.shape[1]
     tab, tdt = _table(rope_table)
-    R = tab.shape[1] if rotary_dim is None else rotary_dim
-    wq = _bits16(q_weight) if q_weight is not None else np.zeros(1, np.uint16)
-    wk = _bits16(k_weight) if k_weight is not None else np.zeros(1, np.uint16)
+    wq = _act_bits(q_weight)[0] if q_weight is not None else np.zeros(1, np.uint16)
+    wk = _act_bits(k_weight)[0] if k_weight is not None else np.zeros(1, np.uint16)
     qo = np.empty((T, Hq, D), np.float64)
     ko = np.empty((T, Hk, D), np.float64)
-    rc = lib().oracle_run_table(_ptr(qb), _ptr(kb), _ptr(wq), _ptr(wk), _ptr(tab), tdt,
-                                float(eps), T, Hq, Hk, D, R, int(bool(interleaved)),
-                                NORM_MODES[norm_mode], Hq * D, Hk * D, tab.shape[1],
-                                _ptr(qo), _ptr(ko))
+    if sin_table is None:
+        R = tab.shape[1] if rotary_dim is None else rotary_dim
+        if act != ACT_BF16:
+            # the packed row seen as the split layout: sine columns start R/2 after the cosines
+            sin_ptr = ctypes.c_void_p(tab.ctypes.data + (R // 2) * tab.itemsize)
+            rc = lib().oracle_run_table_split(_ptr(qb), _ptr(kb), _ptr(wq), _ptr(wk), act,
+                                              _ptr(tab), sin_ptr, tdt, float(eps), T, Hq, Hk,
+                                              D, R, int(bool(interleaved)),
+                                              NORM_MODES[norm_mode], Hq * D, Hk * D,
+                                              tab.shape[1], tab.shape[1], _ptr(qo), _ptr(ko))
+        else:
+            rc = lib().oracle_run_table(_ptr(qb), _ptr(kb), _ptr(wq), _ptr(wk), _ptr(tab), tdt,
+                                        float(eps), T, Hq, Hk, D, R, int(bool(interleaved)),
+                                        NORM_MODES[norm_mode], Hq * D, Hk * D, tab.shape[1],
+                                        _ptr(qo), _ptr(ko))
+    else:
+        stab, sdt = _table(sin_table)
+        if sdt != tdt:
+            raise ValueError("cos and sin tables must share a dtype")
+        R = 2 * tab.shape[1] if rotary_dim is None else rotary_dim
+        rc = lib().oracle_run_table_split(_ptr(qb), _ptr(kb), _ptr(wq), _ptr(wk), act,
+                                          _ptr(tab), _ptr(stab), tdt, float(eps), T, Hq, Hk, D,
+                                          R, int(bool(interleaved)), NORM_MODES[norm_mode],
+                                          Hq * D, Hk * D, tab.shape[1], stab.shape[1],
+                                          _ptr(qo), _ptr(ko))
     if rc != 0:
-        raise ValueError(f"oracle_run_table rejected its arguments (code {rc})")
+        raise ValueError(f"oracle table form rejected its arguments (code {rc})")
     return qo, ko
 
 
@@ -164,6 +223,19 @@ def run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
     return qo, ko, vo
 
 
+def sumsq_3d(qkv, *, num_heads_q, num_heads_k, num_heads_v, head_dim) -> np.ndarray:
+    """Per-token sums of squares of the Q and K rows of packed bf16 qkv, fp64 [T, 2]."""
+    x = _bits16(qkv)
+    row = (num_heads_q + num_heads_k + num_heads_v) * head_dim
+    x = x.reshape(-1, row)
+    out = np.empty((x.shape[0], 2), np.float64)
+    rc = lib().oracle_sumsq_3d(_ptr(x), x.shape[0], num_heads_q, num_heads_k, num_heads_v,
+                               head_dim, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_sumsq_3d rejected its arguments (code {rc})")
+    return out
+
+
 def run_3d_workload(w, qkv, q_weight, k_weight, token_offset=0):
     """run_3d with the parameters of a 3D workload description (any object with those fields)."""
     return run_3d(qkv, q_weight, k_weight, ppf=w.ppf, pph=w.pph, ppw=w.ppw,
@@ -189,6 +261,21 @@ def bf16_encode(x) -> np.ndarray:
 def bf16_decode(bits) -> np.ndarray:
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16_encode(x) -> np.ndarray:
+    """Round-to-nearest-even IEEE binary16 bit patterns (uint16) of an fp64 array."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, np.uint16)
+    lib().oracle_encode_f16_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def f16_decode(bits) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    f = lib().oracle_f16_decode
+    table = np.array([f(i) for i in range(65536)], dtype=np.float64)
+    return table[b]
 
 
 def e4m3_encode(x, scale: float = 1.0) -> np.ndarray:

@@ -12,6 +12,8 @@
  *       rotary_dim/2, in the activation dtype or float32; interleaved=False rotates the pairs
  *       (d, d + rotary_dim/2), interleaved=True the adjacent pairs (2i, 2i+1) by theta_i.
  *       The fused path materialises no normalised or rotated intermediates.
+ *   [split tables] vLLM-Omni API docs, "vllm_omni.diffusion.models.sana_wm.ucpe", cam_prep_func
+ *       parameters: separate (N, D/2) cosine and sine tables for interleaved pairs.
  *   [3D form] FlashInfer API docs, "flashinfer.norm.fused_qk_rmsnorm_rope", description and
  *       parameter list: across-heads RMSNorm of Q and K (weights [heads*head_dim]); RoPE with a
  *       frame/height/width decomposition (seq_len = ppf*pph*ppw, channel counts per axis that
@@ -33,6 +35,9 @@
  *     original frequencies); cos and sin are then multiplied by attention_factor.
  *   - FP8: OCP E4M3 (bias 7, max 448, no infinities, NaN = S.1111.111), round to nearest even,
  *     value multiplied by its scale, finite overflow saturates to +-448.
+ *   - "Activation dtype" covers bf16 and IEEE binary16; weights share the activation dtype.
+ *   - A head-sharded across-heads norm uses the sums of squares of the whole row (every shard's
+ *     heads), i.e. it equals the unsharded norm; oracle_sumsq_3d gives those per-token sums.
  *
  * Everything is computed in double from the exact decoded inputs and rounded once at the output.
  */
@@ -48,7 +53,9 @@ enum { ORACLE_OK = 0, ORACLE_BAD_ARG = 1, ORACLE_NO_MEMORY = 2 };
 enum { ORACLE_NORM_NONE = 0, ORACLE_NORM_PER_HEAD = 1, ORACLE_NORM_ACROSS_HEADS = 2 };
 /* Table dtypes: the pages allow the activation dtype (bf16) or float32. F64 is a test-only
  * extension that lets the table form be compared exactly with the 3D form. */
-enum { ORACLE_TABLE_BF16 = 0, ORACLE_TABLE_F32 = 1, ORACLE_TABLE_F64 = 2 };
+enum { ORACLE_TABLE_BF16 = 0, ORACLE_TABLE_F32 = 1, ORACLE_TABLE_F64 = 2, ORACLE_TABLE_F16 = 3 };
+/* 16-bit activation formats. */
+enum { ORACLE_ACT_BF16 = 0, ORACLE_ACT_F16 = 1 };
 
 /* ---------------------------------------------------------------------------------------------
  * Number formats.
@@ -60,6 +67,18 @@ double oracle_bf16_decode(uint16_t b)
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* IEEE-754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits; exponent 0 holds zero
+ * and subnormals (fraction * 2^-24), exponent 31 infinities and NaNs. Decoding is exact. */
+double oracle_f16_decode(uint16_t h)
+{
+    int s = h >> 15, E = (h >> 10) & 31, M = h & 1023;
+    double v;
+    if (E == 31) v = M ? NAN : INFINITY;
+    else if (E == 0) v = ldexp((double)M, -24);
+    else v = ldexp(1.0 + M / 1024.0, E - 15);
+    return s ? -v : v;
 }
 
 double oracle_f32_decode(uint32_t u)
@@ -99,6 +118,32 @@ uint16_t oracle_bf16_encode(double x)
     uint32_t u;
     memcpy(&u, &f, sizeof u);
     return (uint16_t)(sign | (u >> 16));
+}
+
+/* binary16 round-to-nearest-even of an fp64 value (11 significant bits, smallest normal
+ * 2^-14, largest finite 65504). Overflow rounds to infinity; NaN becomes a quiet NaN. */
+uint16_t oracle_f16_encode(double x)
+{
+    if (isnan(x)) return signbit(x) ? 0xFE00 : 0x7E00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7C00;
+    double r = round_to_grid(a, 11, -14);
+    if (r > 65504.0) return sign | 0x7C00;
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -14))                        /* subnormal: fraction counts 2^-24 steps */
+        return (uint16_t)(sign | (int)(r / ldexp(1.0, -24)));
+    int e;
+    frexp(r, &e);
+    int lead = e - 1;                               /* r in [2^lead, 2^(lead+1)) */
+    int mant = (int)((r / ldexp(1.0, lead) - 1.0) * 1024.0);
+    return (uint16_t)(sign | ((lead + 15) << 10) | mant);
+}
+
+void oracle_encode_f16_array(const double *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_encode(x[i]);
 }
 
 /* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; normal binades
@@ -154,27 +199,35 @@ static double inv_rms(const double *x, int64_t n, double eps)
     return 1.0 / sqrt(sum / (double)n + eps);
 }
 
+static double act_decode(int act, uint16_t b)
+{
+    return act == ORACLE_ACT_F16 ? oracle_f16_decode(b) : oracle_bf16_decode(b);
+}
+
 /* Normalise one token's [H, D] block x in place. PER_HEAD: one scale per head, weight w[d].
  * ACROSS_HEADS: one scale for the whole H*D row, weight w[h*D + d]. NONE: unchanged. */
-static void normalise_token(double *x, int H, int D, int norm_mode, const uint16_t *w, double eps)
+static void normalise_token(double *x, int H, int D, int norm_mode, const uint16_t *w, int act,
+                            double eps)
 {
     if (norm_mode == ORACLE_NORM_PER_HEAD) {
         for (int h = 0; h < H; ++h) {
             double r = inv_rms(x + (int64_t)h * D, D, eps);
             for (int d = 0; d < D; ++d)
-                x[h * D + d] = x[h * D + d] * r * oracle_bf16_decode(w[d]);
+                x[h * D + d] = x[h * D + d] * r * act_decode(act, w[d]);
         }
     } else if (norm_mode == ORACLE_NORM_ACROSS_HEADS) {
         double r = inv_rms(x, (int64_t)H * D, eps);
         for (int i = 0; i < H * D; ++i)
-            x[i] = x[i] * r * oracle_bf16_decode(w[i]);
+            x[i] = x[i] * r * act_decode(act, w[i]);
     }
 }
 
 /* ---------------------------------------------------------------------------------------------
  * Table form.
- * q: [T, Hq, D] bf16 with token stride q_stride (elements); k likewise. rope_table: [T, R]
- * with token stride table_stride, dtype bf16, f32 (or f64 for tests). Outputs: fp64 [T, H, D], unrounded.
+ * q: [T, Hq, D] 16-bit activations (bf16 or binary16) with token stride q_stride (elements);
+ * k likewise; weights in the activation format. cos_table / sin_table: [T, R/2] each, with
+ * their own token strides, dtype bf16, binary16, f32 (or f64 for tests); the pages' packed
+ * [T, R] = [cos | sin] table is sin_table = cos_table + R/2. Outputs: fp64 [T, H, D], unrounded.
  * norm_mode PER_HEAD is the pages' contract ([head_dim] weights); NONE and ACROSS_HEADS
  * (weights [H*D]) are extensions used to relate the table form to the 3D form.
  * ------------------------------------------------------------------------------------------- */
@@ -182,22 +235,24 @@ static double table_value(const void *table, int dtype, int64_t idx)
 {
     if (dtype == ORACLE_TABLE_F64) return ((const double *)table)[idx];
     if (dtype == ORACLE_TABLE_F32) return oracle_f32_decode(((const uint32_t *)table)[idx]);
+    if (dtype == ORACLE_TABLE_F16) return oracle_f16_decode(((const uint16_t *)table)[idx]);
     return oracle_bf16_decode(((const uint16_t *)table)[idx]);
 }
 
-static void table_token(const uint16_t *src, int H, int D, int R, int interleaved,
+static void table_token(const uint16_t *src, int act, int H, int D, int R, int interleaved,
                         int norm_mode, const uint16_t *w, double eps,
-                        const void *table, int dtype, int64_t trow, double *out, double *n)
+                        const void *cos_table, const void *sin_table, int dtype,
+                        int64_t cos_row, int64_t sin_row, double *out, double *n)
 {
-    for (int i = 0; i < H * D; ++i) n[i] = oracle_bf16_decode(src[i]);
-    normalise_token(n, H, D, norm_mode, w, eps);
+    for (int i = 0; i < H * D; ++i) n[i] = act_decode(act, src[i]);
+    normalise_token(n, H, D, norm_mode, w, act, eps);
     for (int h = 0; h < H; ++h) {
         const double *nh = n + (int64_t)h * D;
         double *oh = out + (int64_t)h * D;
         for (int d = 0; d < D; ++d) oh[d] = nh[d];            /* dims >= R pass through */
         for (int i = 0; i < R / 2; ++i) {
-            double c = table_value(table, dtype, trow + i);
-            double s = table_value(table, dtype, trow + R / 2 + i);
+            double c = table_value(cos_table, dtype, cos_row + i);
+            double s = table_value(sin_table, dtype, sin_row + i);
             int a = interleaved ? 2 * i : i;
             int b = interleaved ? 2 * i + 1 : i + R / 2;
             oh[a] = nh[a] * c - nh[b] * s;
@@ -206,20 +261,19 @@ static void table_token(const uint16_t *src, int H, int D, int R, int interleave
     }
 }
 
-int oracle_run_table(const uint16_t *q, const uint16_t *k,
-                     const uint16_t *q_weight, const uint16_t *k_weight,
-                     const void *rope_table, int table_dtype, double eps,
-                     int64_t num_tokens, int num_heads_q, int num_heads_k, int head_dim,
-                     int rotary_dim, int interleaved, int norm_mode,
-                     int64_t q_stride, int64_t k_stride, int64_t table_stride,
-                     double *q_out, double *k_out)
+int oracle_run_table_split(const uint16_t *q, const uint16_t *k,
+                           const uint16_t *q_weight, const uint16_t *k_weight, int act_dtype,
+                           const void *cos_table, const void *sin_table, int table_dtype,
+                           double eps, int64_t num_tokens, int num_heads_q, int num_heads_k,
+                           int head_dim, int rotary_dim, int interleaved, int norm_mode,
+                           int64_t q_stride, int64_t k_stride, int64_t cos_stride,
+                           int64_t sin_stride, double *q_out, double *k_out)
 {
     if (num_tokens < 0 || num_heads_q < 0 || num_heads_k < 0 || head_dim <= 0) return ORACLE_BAD_ARG;
     if (rotary_dim < 0 || rotary_dim > head_dim || rotary_dim % 2) return ORACLE_BAD_ARG;
     if (norm_mode < 0 || norm_mode > 2) return ORACLE_BAD_ARG;
-    if (table_dtype != ORACLE_TABLE_BF16 && table_dtype != ORACLE_TABLE_F32 &&
-        table_dtype != ORACLE_TABLE_F64)
-        return ORACLE_BAD_ARG;
+    if (act_dtype != ORACLE_ACT_BF16 && act_dtype != ORACLE_ACT_F16) return ORACLE_BAD_ARG;
+    if (table_dtype < ORACLE_TABLE_BF16 || table_dtype > ORACLE_TABLE_F16) return ORACLE_BAD_ARG;
     int D = head_dim, R = rotary_dim;
     int Hmax = num_heads_q > num_heads_k ? num_heads_q : num_heads_k;
     int64_t T = num_tokens;
@@ -234,16 +288,36 @@ int oracle_run_table(const uint16_t *q, const uint16_t *k,
 #pragma omp for schedule(static)
         for (int64_t t = 0; t < T; ++t) {
             if (!scratch) continue;
-            table_token(q + t * q_stride, num_heads_q, D, R, interleaved, norm_mode, q_weight,
-                        eps, rope_table, table_dtype, t * table_stride,
-                        q_out + t * num_heads_q * D, scratch);
-            table_token(k + t * k_stride, num_heads_k, D, R, interleaved, norm_mode, k_weight,
-                        eps, rope_table, table_dtype, t * table_stride,
-                        k_out + t * num_heads_k * D, scratch);
+            table_token(q + t * q_stride, act_dtype, num_heads_q, D, R, interleaved, norm_mode,
+                        q_weight, eps, cos_table, sin_table, table_dtype, t * cos_stride,
+                        t * sin_stride, q_out + t * num_heads_q * D, scratch);
+            table_token(k + t * k_stride, act_dtype, num_heads_k, D, R, interleaved, norm_mode,
+                        k_weight, eps, cos_table, sin_table, table_dtype, t * cos_stride,
+                        t * sin_stride, k_out + t * num_heads_k * D, scratch);
         }
         free(scratch);
     }
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* The pages' packed table: row t = [cos(theta_t,0..R/2-1) | sin(theta_t,0..R/2-1)], bf16
+ * activations. */
+int oracle_run_table(const uint16_t *q, const uint16_t *k,
+                     const uint16_t *q_weight, const uint16_t *k_weight,
+                     const void *rope_table, int table_dtype, double eps,
+                     int64_t num_tokens, int num_heads_q, int num_heads_k, int head_dim,
+                     int rotary_dim, int interleaved, int norm_mode,
+                     int64_t q_stride, int64_t k_stride, int64_t table_stride,
+                     double *q_out, double *k_out)
+{
+    int esize = table_dtype == ORACLE_TABLE_F64 ? 8 : (table_dtype == ORACLE_TABLE_F32 ? 4 : 2);
+    if (rotary_dim < 0 || rotary_dim % 2) return ORACLE_BAD_ARG;
+    const void *sin_table = rope_table ? (const char *)rope_table + (size_t)(rotary_dim / 2) * esize
+                                       : NULL;
+    return oracle_run_table_split(q, k, q_weight, k_weight, ORACLE_ACT_BF16, rope_table,
+                                  sin_table, table_dtype, eps, num_tokens, num_heads_q,
+                                  num_heads_k, head_dim, rotary_dim, interleaved, norm_mode,
+                                  q_stride, k_stride, table_stride, table_stride, q_out, k_out);
 }
 
 /* ---------------------------------------------------------------------------------------------
@@ -284,7 +358,8 @@ static void rope3d_region(const uint16_t *src, int H, int D, int interleave, int
                           double *out, double *n)
 {
     for (int i = 0; i < H * D; ++i) n[i] = oracle_bf16_decode(src[i]);
-    normalise_token(n, H, D, norm ? ORACLE_NORM_ACROSS_HEADS : ORACLE_NORM_NONE, w, eps);
+    normalise_token(n, H, D, norm ? ORACLE_NORM_ACROSS_HEADS : ORACLE_NORM_NONE, w,
+                    ORACLE_ACT_BF16, eps);
     for (int h = 0; h < H; ++h) {
         const double *nh = n + (int64_t)h * D;
         double *oh = out + (int64_t)h * D;
@@ -351,6 +426,34 @@ int oracle_run_3d(const uint16_t *qkv, const uint16_t *q_weight, const uint16_t 
         free(scratch);
     }
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* Per-token sums of squares of the Q and K rows of packed bf16 qkv (rows of (Hq+Hk+Hv)*D):
+ * out[2t] = sum of x^2 over the token's Hq*D Q values, out[2t+1] over its Hk*D K values. These
+ * are the sums the across-heads norm of the 3D form takes its mean of. */
+int oracle_sumsq_3d(const uint16_t *qkv, int64_t num_tokens, int num_heads_q, int num_heads_k,
+                    int num_heads_v, int head_dim, double *out)
+{
+    if (num_tokens < 0 || num_heads_q < 0 || num_heads_k < 0 || num_heads_v < 0 || head_dim <= 0)
+        return ORACLE_BAD_ARG;
+    int64_t nq = (int64_t)num_heads_q * head_dim, nk = (int64_t)num_heads_k * head_dim;
+    int64_t row = (int64_t)(num_heads_q + num_heads_k + num_heads_v) * head_dim;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const uint16_t *x = qkv + t * row;
+        double sq = 0.0, sk = 0.0;
+        for (int64_t i = 0; i < nq; ++i) {
+            double v = oracle_bf16_decode(x[i]);
+            sq += v * v;
+        }
+        for (int64_t i = 0; i < nk; ++i) {
+            double v = oracle_bf16_decode(x[nq + i]);
+            sk += v * v;
+        }
+        out[2 * t] = sq;
+        out[2 * t + 1] = sk;
+    }
+    return ORACLE_OK;
 }
 
 /* Threads an OpenMP parallel region of this library will use. */

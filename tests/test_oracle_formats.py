@@ -101,3 +101,48 @@ def test_bf16_decode_is_exact(bits):
     v = oracle.bf16_decode(np.array([bits], np.uint16))[0]
     assert oracle.lib().oracle_bf16_decode(bits) == v
     assert int(oracle.bf16_encode(np.array([v]))[0]) == bits
+
+
+# --- IEEE binary16 (the table form's "activation dtype" may be float16) ------------------------
+
+def test_f16_decode_every_code_matches_ieee_binary16():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_decode(codes)
+    ref = codes.view(np.float16).astype(np.float64)   # numpy's IEEE-754 binary16
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+    np.testing.assert_array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_f16_encode_hand_values():
+    enc = lambda x: int(oracle.f16_encode(np.array([x]))[0])
+    assert enc(1.0) == 0x3C00 and enc(-2.0) == 0xC000
+    assert enc(65504.0) == 0x7BFF                      # largest finite
+    assert enc(65519.99) == 0x7BFF                     # below the overflow midpoint
+    assert enc(65520.0) == 0x7C00                      # midpoint ties to even = infinity
+    assert enc(2.0 ** -24) == 0x0001                   # smallest subnormal
+    assert enc(2.0 ** -25) == 0x0000                   # half of it: tie to even (zero)
+    assert enc(3 * 2.0 ** -25) == 0x0002               # 1.5 quanta -> 2
+    assert enc(2.0 ** -14) == 0x0400                   # smallest normal
+    assert enc(1.0 + 2.0 ** -11) == 0x3C00             # tie between 1 and 1+2^-10 -> even
+    assert enc(1.0 + 3 * 2.0 ** -11) == 0x3C02         # tie -> even mantissa 2
+    assert enc(math.inf) == 0x7C00 and enc(-math.inf) == 0xFC00
+    assert enc(-0.0) == 0x8000
+    assert np.isnan(oracle.f16_decode(np.array([enc(math.nan)], np.uint16))[0])
+
+
+def test_f16_encode_matches_numpy_rounding():
+    rng = np.random.default_rng(17)
+    x = np.concatenate([rng.standard_normal(40000) * s for s in (1e-7, 1e-3, 1.0, 3e3, 6e4)])
+    # every midpoint between neighbouring finite codes, and just either side of it
+    fin = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (fin[1:] + fin[:-1]) / 2
+    x = np.concatenate([x, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf)])
+    ours = oracle.f16_encode(x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)      # numpy rounds double -> half to nearest even
+    np.testing.assert_array_equal(ours, ref)
+    # every finite code encodes back to itself
+    codes = np.arange(0, 0x7C00, dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.f16_encode(oracle.f16_decode(codes)), codes)

@@ -265,6 +265,57 @@ def test_table_form_matches_brute_force(D, R, inter, mode):
                                rtol=1e-12, atol=1e-13)
 
 
+def rand_f16(rng, shape, sigma=1.0):
+    return (rng.standard_normal(shape) * sigma).astype(np.float16)
+
+
+@pytest.mark.parametrize("D,R,inter,mode,tdt", [(8, 8, True, "per_head", np.float16),
+                                                (16, 16, False, "per_head", np.float32),
+                                                (12, 6, True, "across_heads", np.float32),
+                                                (16, 8, False, "none", np.float16)])
+def test_table_form_float16_matches_brute_force(D, R, inter, mode, tdt):
+    # float16 activations and weights ("the activation dtype"); the table in float16 or float32
+    rng = np.random.default_rng(D * 10 + R + 7)
+    T, Hq, Hk = 4, 3, 2
+    q, k = rand_f16(rng, (T, Hq, D)), rand_f16(rng, (T, Hk, D))
+    wl = D if mode != "across_heads" else None
+    wq, wk = (1 + 0.1 * rand_f16(rng, wl or Hq * D)).astype(np.float16), \
+        (1 + 0.1 * rand_f16(rng, wl or Hk * D)).astype(np.float16)
+    theta = rng.uniform(-50, 50, (T, R // 2))
+    tab = angle_table(theta).astype(tdt)
+    qo, ko = oracle.run_table(q, k, wq, wk, tab, 1e-5, rotary_dim=R, interleaved=inter,
+                              norm_mode=mode)
+    # the rounded table entries are not an exact unit phasor: multiply by c + i s as stored
+    c, s = tab[:, : R // 2].astype(np.float64), tab[:, R // 2:].astype(np.float64)
+    f = lambda a: a.astype(np.float64)
+    for x, w, out in ((q, wq, qo), (k, wk, ko)):
+        ref = brute_table(f(x), f(w), np.zeros((T, R // 2)), 1e-5, R, inter, mode)  # norm only
+        z = to_complex(ref, inter, R) * (c + 1j * s)[:, None, :]
+        ref[..., :R] = from_complex(z, inter, R)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_split_cos_sin_tables_match_brute_force():
+    # separate [T, R/2] cosine and sine tables with their own (padded) token strides
+    rng = np.random.default_rng(23)
+    T, H, D, R = 5, 2, 16, 12
+    q, k = rand_bf16(rng, (T, H, D)), rand_bf16(rng, (T, H, D))
+    wq, wk = rand_bf16(rng, D), rand_bf16(rng, D)
+    theta = rng.uniform(-9, 9, (T, R // 2))
+    cos_t = np.zeros((T, R // 2 + 3))
+    sin_t = np.zeros((T, R // 2 + 5))
+    cos_t[:, : R // 2], sin_t[:, : R // 2] = np.cos(theta), np.sin(theta)
+    cos_t[:, R // 2:], sin_t[:, R // 2:] = 7.0, -7.0       # padding the oracle must not read
+    dq = oracle.bf16_decode
+    for inter in (True, False):
+        qo, ko = oracle.run_table(q, k, wq, wk, cos_t, 1e-6, rotary_dim=R, interleaved=inter,
+                                  sin_table=sin_t)
+        np.testing.assert_allclose(qo, brute_table(dq(q), dq(wq), theta, 1e-6, R, inter,
+                                                   "per_head"), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ko, brute_table(dq(k), dq(wk), theta, 1e-6, R, inter,
+                                                   "per_head"), rtol=1e-12, atol=1e-13)
+
+
 # --- 3D form -----------------------------------------------------------------------------------
 
 def rope1d_freqs(C, base):
@@ -419,3 +470,43 @@ def test_3d_rejects_contract_violations():
     with pytest.raises(ValueError):                   # attention factor without YaRN
         run3d(qkv, None, None, num_frame_channels=2, num_height_channels=2,
               num_width_channels=4, is_qk_norm=False, attention_factor=2.0, **kw)
+
+
+# --- per-token sums of squares (first phase of a head-sharded across-heads norm) --------------
+
+def test_sumsq_closed_form_and_head_split_additivity():
+    Hq, Hk, Hv, D, T = 4, 2, 3, 8, 6
+    row = (Hq + Hk + Hv) * D
+    const = np.tile(bf16_bits(np.r_[np.full(Hq * D, 0.5), np.full(Hk * D, -3.0),
+                                    np.full(Hv * D, 100.0)]), (T, 1))
+    s = oracle.sumsq_3d(const, num_heads_q=Hq, num_heads_k=Hk, num_heads_v=Hv, head_dim=D)
+    np.testing.assert_array_equal(s, np.tile([Hq * D * 0.25, Hk * D * 9.0], (T, 1)))
+    # shards holding 1 + 3 Q heads and 1 + 1 K heads: their sums add up to the whole row's
+    rng = np.random.default_rng(29)
+    x = rand_bf16(rng, (T, row)).reshape(T, Hq + Hk + Hv, D)
+    full = oracle.sumsq_3d(x.reshape(T, row), num_heads_q=Hq, num_heads_k=Hk, num_heads_v=Hv,
+                           head_dim=D)
+    parts = []
+    for qh, kh in (((0,), (4,)), ((1, 2, 3), (5,))):
+        sx = np.ascontiguousarray(np.concatenate([x[:, list(qh)], x[:, list(kh)]], axis=1))
+        parts.append(oracle.sumsq_3d(sx.reshape(T, -1), num_heads_q=len(qh),
+                                     num_heads_k=len(kh), num_heads_v=0, head_dim=D))
+    np.testing.assert_allclose(parts[0] + parts[1], full, rtol=1e-14)
+
+
+def test_sumsq_is_what_the_across_heads_norm_averages():
+    # one grid position (ppf = pph = ppw = 1): no rotation, unit weights, so the 3D form's Q
+    # output is x / sqrt(sumsq / (Hq*D) + eps)
+    Hq, Hk, Hv, D, T, eps = 3, 2, 1, 8, 5, 1e-3
+    rng = np.random.default_rng(31)
+    qkv = rand_bf16(rng, (T, (Hq + Hk + Hv) * D))
+    ones_q, ones_k = bf16_bits(np.ones(Hq * D)), bf16_bits(np.ones(Hk * D))
+    q, k, _ = oracle.run_3d(qkv, ones_q, ones_k, ppf=1, pph=1, ppw=1, num_frame_channels=D,
+                            num_height_channels=0, num_width_channels=0, num_heads_q=Hq,
+                            num_heads_k=Hk, num_heads_v=Hv, head_dim=D, eps=eps)
+    s = oracle.sumsq_3d(qkv, num_heads_q=Hq, num_heads_k=Hk, num_heads_v=Hv, head_dim=D)
+    x = oracle.bf16_decode(qkv)
+    np.testing.assert_allclose(q.reshape(T, -1) * np.sqrt(s[:, :1] / (Hq * D) + eps),
+                               x[:, : Hq * D], rtol=1e-13)
+    np.testing.assert_allclose(k.reshape(T, -1) * np.sqrt(s[:, 1:] / (Hk * D) + eps),
+                               x[:, Hq * D:(Hq + Hk) * D], rtol=1e-13)
