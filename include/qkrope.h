@@ -21,11 +21,11 @@
  *     frees, or synchronises on them; it only enqueues work on `stream` (a hipStream_t; NULL is
  *     the default stream) and returns. A kernel fault therefore surfaces at the caller's next
  *     synchronisation with that stream.
- *   - Activations are bf16 (raw 16-bit patterns). Every tensor pointer must be 16-byte aligned
- *     and every token stride a multiple of 8 elements (one 16-byte chunk), else
- *     QKROPE_ERR_UNSUPPORTED.
- *   - Arithmetic is fp32 on the GPU; each output element is rounded once (bf16 round-to-nearest-
- *     even, or OCP E4M3 round-to-nearest-even with saturation to +-448).
+ *   - Activations are bf16 (qkrope_run_table_ex also takes IEEE binary16), passed as raw 16-bit
+ *     patterns. Every 16-bit tensor pointer must be 16-byte aligned and every token stride a
+ *     multiple of 8 elements (one 16-byte chunk), else QKROPE_ERR_UNSUPPORTED.
+ *   - Arithmetic is fp32 on the GPU; each output element is rounded once (to the 16-bit format
+ *     round-to-nearest-even, or OCP E4M3 round-to-nearest-even with saturation to +-448).
  *   - A handle is immutable after qkrope_create, so calls on different streams may run
  *     concurrently from several host threads.
  */
@@ -47,9 +47,13 @@ typedef enum qkrope_status {
     QKROPE_ERR_ALLOC = 4         /* host memory for the handle could not be allocated */
 } qkrope_status;
 
+/* Element formats. bf16 and IEEE binary16 (F16) are 16-bit activations; F32 appears only in
+ * RoPE tables; E4M3 is the OCP FP8 output format (one byte per element). */
+enum { QKROPE_DTYPE_BF16 = 0, QKROPE_DTYPE_F32 = 1, QKROPE_DTYPE_F16 = 2, QKROPE_DTYPE_E4M3 = 3 };
+
 /* rope_table element types for qkrope_run_table: the table form's page allows the activation
  * dtype (bf16) or float32. */
-enum { QKROPE_TABLE_BF16 = 0, QKROPE_TABLE_F32 = 1 };
+enum { QKROPE_TABLE_BF16 = QKROPE_DTYPE_BF16, QKROPE_TABLE_F32 = QKROPE_DTYPE_F32 };
 
 /* Norm modes for qkrope_run_table. PER_HEAD is the table form's contract (weights [head_dim],
  * one RMS per head). ACROSS_HEADS (weights [heads*head_dim], one RMS over the token's whole Q or
@@ -108,6 +112,36 @@ int qkrope_run_table(qkrope_handle h,
                      void *stream);
 
 /*
+ * Table form, extended contract. Everything qkrope_run_table does, plus:
+ *   - separate cosine and sine tables, each [num_tokens, rotary_dim/2] with its own token stride
+ *     (the layout of the rope_cos / rope_sin tables of vLLM-Omni's SANA-WM camera prologue,
+ *     "vllm_omni.diffusion.models.sana_wm.ucpe", cam_prep_func parameters); row t of cos_table
+ *     holds cos(theta_t,i), row t of sin_table sin(theta_t,i), i < rotary_dim/2. A packed
+ *     [cos | sin] table is cos_table = table, sin_table = table + rotary_dim/2 with equal strides.
+ *   - act_dtype QKROPE_DTYPE_BF16 or QKROPE_DTYPE_F16: format of q, k and the norm weights (the
+ *     table form's page ties the table dtype and outputs to "the activation dtype");
+ *     table_dtype is QKROPE_DTYPE_F32 or equal to act_dtype.
+ *   - out_dtype equal to act_dtype (each output rounded once, to nearest even), or
+ *     QKROPE_DTYPE_E4M3: outputs are OCP E4M3 bytes of y * out_scale (round to nearest even,
+ *     finite overflow saturating to +-448, NaN kept), as the 3D form's output_fp8 does; then
+ *     out_scale must be finite and > 0 (it is ignored otherwise), the output token strides count
+ *     bytes, outputs must be 8-byte aligned, and no output may alias an input.
+ * In-place use (q_out == q with equal strides) needs out_dtype == act_dtype. Other arguments,
+ * limits and errors are those of qkrope_run_table.
+ */
+int qkrope_run_table_ex(qkrope_handle h,
+                        const void *q, const void *k, const void *q_weight, const void *k_weight,
+                        const void *cos_table, const void *sin_table, int table_dtype,
+                        int act_dtype, int out_dtype, double out_scale, double eps,
+                        int64_t num_tokens, int num_heads_q, int num_heads_k, int head_dim,
+                        int rotary_dim, int interleaved, int norm_mode,
+                        int64_t q_token_stride, int64_t k_token_stride,
+                        int64_t cos_token_stride, int64_t sin_token_stride,
+                        void *q_out, void *k_out,
+                        int64_t q_out_token_stride, int64_t k_out_token_stride,
+                        void *stream);
+
+/*
  * 3D form (FlashInfer fused_qk_rmsnorm_rope).
  *
  *   qkv        [num_tokens, (num_heads_q + num_heads_k + num_heads_v) * head_dim] bf16,
@@ -146,6 +180,52 @@ int qkrope_run_3d(qkrope_handle h,
                   double high, double attention_factor, int is_qk_norm, int output_fp8,
                   double output_quant_scale, double v_quant_scale,
                   void *q_out, void *k_out, void *v_out, void *stream);
+
+/*
+ * Sharded 3D form: the pieces one rank of a sequence- or head-sharded run needs.
+ *
+ * The FlashInfer page defines the across-heads norm over a token's whole Q (K) row; vLLM-Omni's
+ * SANA-WM page ("vllm_omni.diffusion.models.sana_wm.ucpe", cam_prep_func) notes that under
+ * tensor parallelism the norm must still span every channel, not only a shard's. A rank whose
+ * qkv holds only some heads of each token therefore (1) computes per-token partial sums of
+ * squares of its Q and K heads with qkrope_sumsq_3d, (2) sums them over the ranks of its
+ * head group (an all-reduce, the caller's), and (3) passes the totals to qkrope_run_3d_sharded.
+ * A rank that holds a contiguous slice of tokens passes the slice's first global token index
+ * as token_offset, so that every token keeps its (frame, height, width) position.
+ */
+
+/* sumsq[2t] = sum of x^2 over token t's num_heads_q*head_dim Q values in qkv,
+ * sumsq[2t+1] = the same over its K values; fp32, accumulated in fp32. qkv has the layout of
+ * qkrope_run_3d (num_heads_v heads of V after K; they are not read). sumsq is a device array
+ * of 2*num_tokens floats, 8-byte aligned, not overlapping qkv. head_dim must be a multiple of
+ * 8; (num_heads_q + num_heads_k) * head_dim / 8 <= 8192. num_tokens == 0 is a no-op. */
+int qkrope_sumsq_3d(qkrope_handle h, const void *qkv, int64_t num_tokens, int num_heads_q,
+                    int num_heads_k, int num_heads_v, int head_dim, float *sumsq, void *stream);
+
+/* qkrope_run_3d on a shard:
+ *   token_offset  global index of qkv's first token: token t sits at grid position
+ *                 (token_offset + t) mod (ppf*pph*ppw). num_tokens need not be a multiple of
+ *                 ppf*pph*ppw; token_offset >= 0 and token_offset + num_tokens < 2^31.
+ *   sumsq         NULL: the norm spans the shard's own heads (as qkrope_run_3d).
+ *                 Otherwise (with is_qk_norm) a device array [num_tokens, 2] of fp32 sums of
+ *                 squares of each token's Q and K rows over ALL heads of the unsharded problem
+ *                 (the reduced output of qkrope_sumsq_3d), 8-byte aligned; the norm is then
+ *                 x * (sumsq / norm_elems + eps)^(-1/2) * w, where norm_elems_q/k are the
+ *                 element counts the sums cover (num_heads_q_total * head_dim, ...) and must be
+ *                 >= the shard's own; q_weight/k_weight are the shard's slices [num_heads * D].
+ *                 norm_elems_* are ignored when sumsq is NULL.
+ * Every other argument is that of qkrope_run_3d. */
+int qkrope_run_3d_sharded(qkrope_handle h,
+                          const void *qkv, const void *q_weight, const void *k_weight,
+                          int64_t num_tokens, int64_t token_offset, const float *sumsq,
+                          int64_t norm_elems_q, int64_t norm_elems_k,
+                          int ppf, int pph, int ppw,
+                          int num_frame_channels, int num_height_channels, int num_width_channels,
+                          int num_heads_q, int num_heads_k, int num_heads_v, int head_dim,
+                          double eps, double base, int interleave, double factor, double low,
+                          double high, double attention_factor, int is_qk_norm, int output_fp8,
+                          double output_quant_scale, double v_quant_scale,
+                          void *q_out, void *k_out, void *v_out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,8 @@ kernels. PyTorch provides device memory and the current stream.
 
 Entry points, with the names of the C ABI:
   qkrope_create / qkrope_destroy / qkrope_run_table / qkrope_run_3d
+  qkrope_run_table_ex (split cos/sin tables, float16 activations, E4M3 outputs)
+  qkrope_sumsq_3d / qkrope_run_3d_sharded (sequence- and head-sharded 3D form)
 and the two page-shaped conveniences that allocate outputs:
   fused_qk_norm_rope      -- vLLM-Omni "vllm_omni.diffusion.layers.fused_qk_norm_rope"
   fused_qk_rmsnorm_rope   -- FlashInfer "flashinfer.norm.fused_qk_rmsnorm_rope"
@@ -25,7 +27,8 @@ from .workloads import WORKLOADS  # noqa: F401  (re-exported for convenience)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqkrope.so")
 
 QKROPE_OK, QKROPE_ERR_INVALID, QKROPE_ERR_UNSUPPORTED, QKROPE_ERR_DEVICE, QKROPE_ERR_ALLOC = range(5)
-QKROPE_TABLE_BF16, QKROPE_TABLE_F32 = 0, 1
+QKROPE_DTYPE_BF16, QKROPE_DTYPE_F32, QKROPE_DTYPE_F16, QKROPE_DTYPE_E4M3 = 0, 1, 2, 3
+QKROPE_TABLE_BF16, QKROPE_TABLE_F32 = QKROPE_DTYPE_BF16, QKROPE_DTYPE_F32
 NORM_MODES = {"none": 0, "per_head": 1, "across_heads": 2}
 
 _lock = threading.Lock()
@@ -68,6 +71,15 @@ def lib() -> ctypes.CDLL:
         L.qkrope_run_3d.argtypes = [P, P, P, P, I64, I, I, I, I, I, I, I, I, I, I,
                                     D, D, I, D, D, D, D, I, I, D, D, P, P, P, P]
         L.qkrope_run_3d.restype = I
+        L.qkrope_run_table_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, D, D, I64, I, I, I, I,
+                                          I, I, I64, I64, I64, I64, P, P, I64, I64, P]
+        L.qkrope_run_table_ex.restype = I
+        L.qkrope_sumsq_3d.argtypes = [P, P, I64, I, I, I, I, P, P]
+        L.qkrope_sumsq_3d.restype = I
+        L.qkrope_run_3d_sharded.argtypes = [P, P, P, P, I64, I64, P, I64, I64, I, I, I, I, I, I,
+                                            I, I, I, I, D, D, I, D, D, D, D, I, I, D, D,
+                                            P, P, P, P]
+        L.qkrope_run_3d_sharded.restype = I
         runtimes = _hip_runtimes_loaded()
         if len(runtimes) > 1:
             raise RuntimeError(f"two HIP runtimes are loaded ({sorted(runtimes)}); "
@@ -171,6 +183,117 @@ def qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, *, q_out, k_out,
     _check(s, "qkrope_run_table")
 
 
+_DTYPE_CODES = {torch.bfloat16: QKROPE_DTYPE_BF16, torch.float16: QKROPE_DTYPE_F16,
+                torch.float32: QKROPE_DTYPE_F32, torch.float8_e4m3fn: QKROPE_DTYPE_E4M3}
+
+
+def _table_cols(t, T, cols, name) -> int:
+    """Token stride of a GPU [tokens, >= cols] table with unit column stride."""
+    if t.dim() != 2 or t.shape[0] != T or t.shape[1] < cols or not t.is_cuda or \
+            (cols > 0 and t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a GPU [tokens, >= {cols}] tensor whose columns are "
+                         "contiguous")
+    return t.stride(0) if T > 1 else t.shape[1]
+
+
+def qkrope_run_table_ex(q, k, q_weight, k_weight, cos_table, sin_table, eps, *, q_out, k_out,
+                        head_dim=None, rotary_dim=None, interleaved=False, norm_mode="per_head",
+                        out_scale=1.0, stream=None) -> None:
+    """Table form with separate [tokens, rotary_dim/2] cos and sin tables, bfloat16 or float16
+    activations (weights alike), and outputs in the activation dtype or float8_e4m3fn (codes of
+    y * out_scale). Formats are taken from the tensors' dtypes."""
+    act = _DTYPE_CODES.get(q.dtype)
+    if act not in (QKROPE_DTYPE_BF16, QKROPE_DTYPE_F16) or k.dtype != q.dtype:
+        raise ValueError("q and k must both be bfloat16 or both float16")
+    out = _DTYPE_CODES.get(q_out.dtype)
+    if out not in (act, QKROPE_DTYPE_E4M3) or k_out.dtype != q_out.dtype:
+        raise ValueError("q_out and k_out must have q's dtype or float8_e4m3fn")
+    tdt = _DTYPE_CODES.get(cos_table.dtype)
+    if tdt not in (QKROPE_DTYPE_F32, act) or sin_table.dtype != cos_table.dtype:
+        raise ValueError("cos and sin tables must both be float32 or both the activation dtype")
+    for name, t in (("q", q), ("k", k), ("q_out", q_out), ("k_out", k_out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    D = head_dim if head_dim is not None else q.shape[-1]
+    Hq = q.shape[1] if q.dim() == 3 else q.shape[1] // D
+    Hk = k.shape[1] if k.dim() == 3 else k.shape[1] // D
+    T = q.shape[0]
+    if k.shape[0] != T or q_out.shape[0] != T or k_out.shape[0] != T:
+        raise ValueError("q, k and outputs must have the same number of tokens")
+    R = rotary_dim if rotary_dim is not None else 2 * cos_table.shape[-1]
+    cs = _table_cols(cos_table, T, R // 2, "cos_table")
+    ss = _table_cols(sin_table, T, R // 2, "sin_table")
+    for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+        if norm_mode != "none" and (w is None or w.dtype != q.dtype or not w.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor of q's dtype")
+    s = lib().qkrope_run_table_ex(
+        _handle_for(q.device), _ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight),
+        _ptr(cos_table), _ptr(sin_table), tdt, act, out, float(out_scale), float(eps), T, Hq, Hk,
+        D, R, int(bool(interleaved)), NORM_MODES[norm_mode], _rows(q, Hq, D, "q"),
+        _rows(k, Hk, D, "k"), cs, ss, _ptr(q_out), _ptr(k_out), _rows(q_out, Hq, D, "q_out"),
+        _rows(k_out, Hk, D, "k_out"), _stream(q.device, stream))
+    _check(s, "qkrope_run_table_ex")
+
+
+def qkrope_sumsq_3d(qkv, *, num_heads_q, num_heads_k, num_heads_v, head_dim, out=None,
+                    stream=None) -> torch.Tensor:
+    """Per-token fp32 sums of squares of the Q and K rows of packed bf16 qkv: [tokens, 2]."""
+    if qkv.dtype != torch.bfloat16 or not qkv.is_cuda or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous bfloat16 GPU tensor")
+    row = (num_heads_q + num_heads_k + num_heads_v) * head_dim
+    if qkv.shape[-1] != row:
+        raise ValueError(f"qkv rows must hold {row} elements")
+    T = qkv.numel() // row
+    if out is None:
+        out = torch.empty((T, 2), dtype=torch.float32, device=qkv.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != 2 * T:
+        raise ValueError("out must be a contiguous float32 [tokens, 2] tensor")
+    s = lib().qkrope_sumsq_3d(_handle_for(qkv.device), _ptr(qkv), T, num_heads_q, num_heads_k,
+                              num_heads_v, head_dim, _ptr(out), _stream(qkv.device, stream))
+    _check(s, "qkrope_sumsq_3d")
+    return out
+
+
+def qkrope_run_3d_sharded(qkv, q_weight, k_weight, *, token_offset=0, sumsq=None,
+                          norm_elems_q=0, norm_elems_k=0, ppf, pph, ppw, num_frame_channels,
+                          num_height_channels, num_width_channels, num_heads_q, num_heads_k,
+                          num_heads_v, head_dim, q_out, k_out, v_out, eps=1e-6, base=10000.0,
+                          interleave=True, factor=1.0, low=0.0, high=0.0, attention_factor=1.0,
+                          is_qk_norm=True, output_fp8=False, output_quant_scale=1.0,
+                          v_quant_scale=1.0, stream=None) -> None:
+    """3D form on one shard: tokens from global index token_offset on, and (with sumsq, a
+    float32 [tokens, 2] tensor of sums over every head) the across-heads norm of the whole
+    row."""
+    if qkv.dtype != torch.bfloat16 or not qkv.is_cuda or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous bfloat16 GPU tensor")
+    row = (num_heads_q + num_heads_k + num_heads_v) * head_dim
+    if qkv.shape[-1] != row:
+        raise ValueError(f"qkv rows must hold {row} elements")
+    T = qkv.numel() // row
+    odt = torch.float8_e4m3fn if output_fp8 else torch.bfloat16
+    for name, o, H in (("q_out", q_out, num_heads_q), ("k_out", k_out, num_heads_k),
+                       ("v_out", v_out, num_heads_v)):
+        if o.dtype != odt or not o.is_contiguous() or o.numel() != T * H * head_dim or not o.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {odt} GPU tensor of {T}x{H}x{head_dim}")
+    if sumsq is not None and (sumsq.dtype != torch.float32 or not sumsq.is_contiguous() or
+                              sumsq.numel() != 2 * T or not sumsq.is_cuda):
+        raise ValueError("sumsq must be a contiguous float32 GPU tensor [tokens, 2]")
+    if is_qk_norm:
+        for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+            if w is None or w.dtype != torch.bfloat16 or not w.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    s = lib().qkrope_run_3d_sharded(
+        _handle_for(qkv.device), _ptr(qkv), _ptr(q_weight) if is_qk_norm else None,
+        _ptr(k_weight) if is_qk_norm else None, T, int(token_offset), _ptr(sumsq),
+        int(norm_elems_q), int(norm_elems_k), ppf, pph, ppw, num_frame_channels,
+        num_height_channels, num_width_channels, num_heads_q, num_heads_k, num_heads_v, head_dim,
+        float(eps), float(base), int(bool(interleave)), float(factor), float(low), float(high),
+        float(attention_factor), int(bool(is_qk_norm)), int(bool(output_fp8)),
+        float(output_quant_scale), float(v_quant_scale), _ptr(q_out), _ptr(k_out), _ptr(v_out),
+        _stream(qkv.device, stream))
+    _check(s, "qkrope_run_3d_sharded")
+
+
 def qkrope_run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
                   num_height_channels, num_width_channels, num_heads_q, num_heads_k,
                   num_heads_v, head_dim, q_out, k_out, v_out, eps=1e-6, base=10000.0,
@@ -210,12 +333,16 @@ def fused_qk_norm_rope(q, k, q_weight, k_weight, rope_table, eps, *, head_dim=No
                        rotary_dim=None, interleaved=False):
     """Q/K RMSNorm (per head, [head_dim] weights) then RoPE from a [tokens, rotary_dim] table.
 
-    Signature of vLLM-Omni's fused_qk_norm_rope. Returns new (q, k) with the inputs' shapes.
+    Signature of vLLM-Omni's fused_qk_norm_rope. q/k are bfloat16 or float16; the table is
+    float32 or q's dtype. Returns new (q, k) with the inputs' shapes.
     """
     q_out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     k_out = torch.empty(k.shape, dtype=k.dtype, device=k.device)
-    qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, q_out=q_out, k_out=k_out,
-                     head_dim=head_dim, rotary_dim=rotary_dim, interleaved=interleaved)
+    R = rotary_dim if rotary_dim is not None else rope_table.shape[-1]
+    # the packed [cos | sin] row as two column views
+    qkrope_run_table_ex(q, k, q_weight, k_weight, rope_table[:, : R // 2],
+                        rope_table[:, R // 2: R], eps, q_out=q_out, k_out=k_out,
+                        head_dim=head_dim, rotary_dim=R, interleaved=interleaved)
     return q_out, k_out
 
 
@@ -281,6 +408,37 @@ class Prepared3D:
         s = self._fn(*self._args)
         if s != QKROPE_OK:
             _check(s, "qkrope_run_3d")
+
+
+class PreparedTable:
+    """Arguments of one qkrope_run_table call marshalled once (see Prepared3D)."""
+
+    def __init__(self, q, k, q_weight, k_weight, rope_table, eps, *, q_out, k_out,
+                 head_dim=None, rotary_dim=None, interleaved=False, norm_mode="per_head",
+                 stream=None):
+        qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, q_out=q_out, k_out=k_out,
+                         head_dim=head_dim, rotary_dim=rotary_dim, interleaved=interleaved,
+                         norm_mode=norm_mode, stream=stream)
+        D = head_dim if head_dim is not None else q.shape[-1]
+        Hq = q.shape[1] if q.dim() == 3 else q.shape[1] // D
+        Hk = k.shape[1] if k.dim() == 3 else k.shape[1] // D
+        T = q.shape[0]
+        R = rotary_dim if rotary_dim is not None else rope_table.shape[-1]
+        tdt = QKROPE_TABLE_F32 if rope_table.dtype == torch.float32 else QKROPE_TABLE_BF16
+        ts = rope_table.stride(0) if T > 1 else rope_table.shape[1]
+        self._fn = lib().qkrope_run_table
+        self._args = (
+            _handle_for(q.device), _ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight),
+            _ptr(rope_table), tdt, float(eps), T, Hq, Hk, D, R, int(bool(interleaved)),
+            NORM_MODES[norm_mode], _rows(q, Hq, D, "q"), _rows(k, Hk, D, "k"), ts, _ptr(q_out),
+            _ptr(k_out), _rows(q_out, Hq, D, "q_out"), _rows(k_out, Hk, D, "k_out"),
+            _stream(q.device, stream))
+        self._keep = (q, k, q_weight, k_weight, rope_table, q_out, k_out)
+
+    def __call__(self) -> None:
+        s = self._fn(*self._args)
+        if s != QKROPE_OK:
+            _check(s, "qkrope_run_table")
 
 
 def run_workload_3d(w, qkv, q_weight, k_weight, q_out=None, k_out=None, v_out=None):

@@ -20,8 +20,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libqkrope.so")
 
 SOURCES = ["qkrope_kernels_3d_d64.hip", "qkrope_kernels_3d_d128.hip", "qkrope_kernels_3d_d256.hip",
-           "qkrope_kernels_table_interleaved.hip", "qkrope_kernels_table_halfsplit.hip",
-           "qkrope_api.cpp"]
+           "qkrope_kernels_table_interleaved_bf16.hip", "qkrope_kernels_table_halfsplit_bf16.hip",
+           "qkrope_kernels_table_interleaved_f16.hip", "qkrope_kernels_table_halfsplit_f16.hip",
+           "qkrope_kernels_sumsq.hip", "qkrope_api.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

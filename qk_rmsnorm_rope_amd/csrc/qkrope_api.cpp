@@ -158,7 +158,9 @@ hipError_t launch(const KernelKey &k, const LaunchShape &s, const KernelArgs &a,
         default: return hipErrorInvalidValue;
         }
     }
-    return k.half_split ? launch_table_halfsplit(k, s, a, st) : launch_table_interleaved(k, s, a, st);
+    if (k.act == kActF16)
+        return k.half_split ? launch_table_halfsplit_f16(k, s, a, st) : launch_table_interleaved_f16(k, s, a, st);
+    return k.half_split ? launch_table_halfsplit_bf16(k, s, a, st) : launch_table_interleaved_bf16(k, s, a, st);
 }
 
 // Device guard: make h->device current for the launch and restore the caller's device after.
@@ -188,6 +190,301 @@ int do_launch(qkrope_handle h, const KernelKey &key, const LaunchShape &shape,
     hipError_t e = launch(key, shape, args, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+
+// Every argument of the table form, extended contract (qkrope_run_table_ex).
+struct TableCall {
+    const void *q, *k, *q_weight, *k_weight, *cos_table, *sin_table;
+    int table_dtype, act_dtype, out_dtype;
+    double out_scale, eps;
+    int64_t T;
+    int Hq, Hk, D, R, interleaved, norm_mode;
+    int64_t q_stride, k_stride, cos_stride, sin_stride;
+    void *q_out, *k_out;
+    int64_t q_out_stride, k_out_stride;
+};
+
+int run_table(qkrope_handle h, const TableCall &c, void *stream)
+{
+    if (!h) return fail(QKROPE_ERR_INVALID, "handle is NULL");
+    const int D = c.D, R = c.R, Hq = c.Hq, Hk = c.Hk;
+    const int64_t T = c.T;
+    if (T < 0 || Hq < 0 || Hk < 0) return fail(QKROPE_ERR_INVALID, "negative size");
+    if (D <= 0) return fail(QKROPE_ERR_INVALID, "head_dim must be positive");
+    if (R < 0 || R > D || R % 2) return fail(QKROPE_ERR_INVALID, "rotary_dim must be even and in [0, head_dim]");
+    if (c.act_dtype != QKROPE_DTYPE_BF16 && c.act_dtype != QKROPE_DTYPE_F16)
+        return fail(QKROPE_ERR_INVALID, "act_dtype must be QKROPE_DTYPE_BF16 or QKROPE_DTYPE_F16");
+    if (c.table_dtype != QKROPE_DTYPE_F32 && c.table_dtype != c.act_dtype)
+        return fail(QKROPE_ERR_INVALID, "table_dtype must be float32 or the activation dtype");
+    if (c.out_dtype != c.act_dtype && c.out_dtype != QKROPE_DTYPE_E4M3)
+        return fail(QKROPE_ERR_INVALID, "out_dtype must be the activation dtype or QKROPE_DTYPE_E4M3");
+    const bool fp8 = c.out_dtype == QKROPE_DTYPE_E4M3;
+    if (fp8 && (!(c.out_scale > 0.0) || !std::isfinite(c.out_scale)))
+        return fail(QKROPE_ERR_INVALID, "out_scale must be finite and > 0 for E4M3 outputs");
+    if (c.norm_mode < QKROPE_NORM_NONE || c.norm_mode > QKROPE_NORM_ACROSS_HEADS)
+        return fail(QKROPE_ERR_INVALID, "unknown norm_mode %d", c.norm_mode);
+    if (!(c.eps >= 0.0) || !std::isfinite(c.eps)) return fail(QKROPE_ERR_INVALID, "eps must be finite and >= 0");
+    if (D % 8 || D > 256) return fail(QKROPE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and <= 256");
+    const bool half = !c.interleaved;
+    if (half && R % 16)
+        return fail(QKROPE_ERR_UNSUPPORTED, "half-split pairing needs rotary_dim to be a multiple of 16");
+    if (T >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "num_tokens must be < 2^31");
+    if (T == 0 || Hq + Hk == 0) return ok();
+
+    if (!c.q && Hq) return fail(QKROPE_ERR_INVALID, "q is NULL");
+    if (!c.k && Hk) return fail(QKROPE_ERR_INVALID, "k is NULL");
+    if (!c.q_out && Hq) return fail(QKROPE_ERR_INVALID, "q_out is NULL");
+    if (!c.k_out && Hk) return fail(QKROPE_ERR_INVALID, "k_out is NULL");
+    if (R > 0 && (!c.cos_table || !c.sin_table)) return fail(QKROPE_ERR_INVALID, "rope table is NULL");
+    if (c.norm_mode != QKROPE_NORM_NONE && ((Hq && !c.q_weight) || (Hk && !c.k_weight)))
+        return fail(QKROPE_ERR_INVALID, "norm weights are NULL");
+    if (c.q_stride < (int64_t)Hq * D || c.k_stride < (int64_t)Hk * D ||
+        c.q_out_stride < (int64_t)Hq * D || c.k_out_stride < (int64_t)Hk * D)
+        return fail(QKROPE_ERR_INVALID, "token strides must be >= heads*head_dim");
+    if (R > 0 && (c.cos_stride < R / 2 || c.sin_stride < R / 2))
+        return fail(QKROPE_ERR_INVALID, "table token strides must be >= rotary_dim/2");
+    if (c.q_stride % 8 || c.k_stride % 8 || c.q_out_stride % 8 || c.k_out_stride % 8)
+        return fail(QKROPE_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements");
+    const uintptr_t oalign = fp8 ? 8 : 16;
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.q_weight, 16) || !aligned(c.k_weight, 16))
+        return fail(QKROPE_ERR_UNSUPPORTED, "q, k and weights must be 16-byte aligned");
+    if (!aligned(c.q_out, oalign) || !aligned(c.k_out, oalign))
+        return fail(QKROPE_ERR_UNSUPPORTED, "outputs must be %d-byte aligned", (int)oalign);
+    const int tsize = c.table_dtype == QKROPE_DTYPE_F32 ? 4 : 2;
+    if (!aligned(c.cos_table, tsize) || !aligned(c.sin_table, tsize))
+        return fail(QKROPE_ERR_UNSUPPORTED, "rope table is misaligned");
+
+    // Outputs may alias their own input exactly (in place, same format and stride); any other
+    // overlap is rejected.
+    const int osize = fp8 ? 1 : 2;
+    const int64_t wq_len = c.norm_mode == QKROPE_NORM_ACROSS_HEADS ? (int64_t)Hq * D : D;
+    const int64_t wk_len = c.norm_mode == QKROPE_NORM_ACROSS_HEADS ? (int64_t)Hk * D : D;
+    const Range rq = span_of(c.q, T, c.q_stride, (int64_t)Hq * D, 2);
+    const Range rk = span_of(c.k, T, c.k_stride, (int64_t)Hk * D, 2);
+    const Range rqo = span_of(c.q_out, T, c.q_out_stride, (int64_t)Hq * D, osize);
+    const Range rko = span_of(c.k_out, T, c.k_out_stride, (int64_t)Hk * D, osize);
+    const Range rc = span_of(c.cos_table, R > 0 ? T : 0, c.cos_stride, R / 2, tsize);
+    const Range rs = span_of(c.sin_table, R > 0 ? T : 0, c.sin_stride, R / 2, tsize);
+    const Range none{0, 0, 0, 0};
+    const Range rwq = c.norm_mode != QKROPE_NORM_NONE ? span_of(c.q_weight, 1, 0, wq_len, 2) : none;
+    const Range rwk = c.norm_mode != QKROPE_NORM_NONE ? span_of(c.k_weight, 1, 0, wk_len, 2) : none;
+    const bool q_inplace = !fp8 && c.q_out == c.q && c.q_out_stride == c.q_stride;
+    const bool k_inplace = !fp8 && c.k_out == c.k && c.k_out_stride == c.k_stride;
+    if ((!q_inplace && overlap(rqo, rq)) || overlap(rqo, rk) || overlap(rqo, rc) || overlap(rqo, rs) ||
+        overlap(rqo, rwq) || overlap(rqo, rwk) || overlap(rqo, rko))
+        return fail(QKROPE_ERR_INVALID, "q_out overlaps another argument");
+    if ((!k_inplace && overlap(rko, rk)) || overlap(rko, rq) || overlap(rko, rc) || overlap(rko, rs) ||
+        overlap(rko, rwq) || overlap(rko, rwk))
+        return fail(QKROPE_ERR_INVALID, "k_out overlaps another argument");
+
+    const int L = next_pow2(D / 8);           // lanes per head: one 16-byte chunk each
+    const int64_t n_units[2] = {(int64_t)Hq * L, (int64_t)Hk * L};
+    LaunchShape shape;
+    if (!choose_shape(n_units, 2, &shape))
+        return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
+
+    KernelArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.in[kQ] = static_cast<const uint16_t *>(c.q);
+    a.in[kK] = static_cast<const uint16_t *>(c.k);
+    a.out[kQ] = c.q_out;
+    a.out[kK] = c.k_out;
+    a.in_stride[kQ] = c.q_stride;
+    a.in_stride[kK] = c.k_stride;
+    a.out_stride[kQ] = c.q_out_stride;
+    a.out_stride[kK] = c.k_out_stride;
+    a.heads[kQ] = Hq;
+    a.heads[kK] = Hk;
+    a.heads[kV] = 0;
+    a.weight[0] = static_cast<const uint16_t *>(c.q_weight);
+    a.weight[1] = static_cast<const uint16_t *>(c.k_weight);
+    a.table_cos = c.cos_table;
+    a.table_sin = c.sin_table;
+    a.cos_stride = c.cos_stride;
+    a.sin_stride = c.sin_stride;
+    a.num_tokens = T;
+    a.head_dim = D;
+    a.rotary_dim = R;
+    a.lanes_per_head = L;
+    a.eps = (float)c.eps;
+    const bool across = c.norm_mode == QKROPE_NORM_ACROSS_HEADS;
+    a.inv_count[0] = (float)(1.0 / (double)(across ? (int64_t)Hq * D : D));
+    a.inv_count[1] = (float)(1.0 / (double)(across ? (int64_t)Hk * D : D));
+    a.qk_scale = fp8 ? (float)c.out_scale : 1.0f;
+    a.v_scale = 1.0f;
+    shape.blocks = T;
+
+    KernelKey key;
+    key.head_dim_tpl = 0;
+    key.half_split = half;
+    key.norm = c.norm_mode == QKROPE_NORM_NONE ? kNormNone
+             : c.norm_mode == QKROPE_NORM_PER_HEAD ? kNormPerHead : kNormAcross;
+    key.src = c.table_dtype == QKROPE_DTYPE_F32 ? kSrcTableF32
+            : c.table_dtype == QKROPE_DTYPE_BF16 ? kSrcTableBF16 : kSrcTableF16;
+    key.act = c.act_dtype == QKROPE_DTYPE_F16 ? kActF16 : kActBF16;
+    key.fp8 = fp8;
+    key.slots = shape.slots;
+    key.slot_uniform = shape.slot_uniform;
+    return do_launch(h, key, shape, a, stream);
+}
+
+// Every argument of the 3D form, sharded contract (qkrope_run_3d_sharded).
+struct Rope3DCall {
+    const void *qkv, *q_weight, *k_weight;
+    int64_t T, token_offset;
+    const float *sumsq;
+    int64_t norm_elems_q, norm_elems_k;
+    int ppf, pph, ppw, C[3], Hq, Hk, Hv, D;
+    double eps, base;
+    int interleave;
+    double factor, low, high, attention_factor;
+    int is_qk_norm, output_fp8;
+    double output_quant_scale, v_quant_scale;
+    void *q_out, *k_out, *v_out;
+    bool whole_sequences;     // num_tokens must be a multiple of ppf*pph*ppw (unsharded call)
+};
+
+int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
+{
+    if (!h) return fail(QKROPE_ERR_INVALID, "handle is NULL");
+    const int D = c.D, Hq = c.Hq, Hk = c.Hk, Hv = c.Hv;
+    const int *C = c.C;
+    const int64_t T = c.T;
+    if (T < 0 || Hq < 0 || Hk < 0 || Hv < 0) return fail(QKROPE_ERR_INVALID, "negative size");
+    if (D != 64 && D != 128 && D != 256) return fail(QKROPE_ERR_INVALID, "head_dim must be 64, 128 or 256");
+    for (int i = 0; i < 3; ++i)
+        if (C[i] < 0 || C[i] % 2) return fail(QKROPE_ERR_INVALID, "channel counts must be even and >= 0");
+    if (C[0] + C[1] + C[2] != D) return fail(QKROPE_ERR_INVALID, "channel counts must sum to head_dim");
+    if (c.ppf <= 0 || c.pph <= 0 || c.ppw <= 0) return fail(QKROPE_ERR_INVALID, "ppf, pph, ppw must be positive");
+    const int64_t S = (int64_t)c.ppf * c.pph * c.ppw;
+    if (c.whole_sequences && T % S) return fail(QKROPE_ERR_INVALID, "num_tokens must be a multiple of ppf*pph*ppw");
+    if (c.token_offset < 0) return fail(QKROPE_ERR_INVALID, "token_offset must be >= 0");
+    if (!(c.base > 0.0) || !std::isfinite(c.base)) return fail(QKROPE_ERR_INVALID, "base must be finite and > 0");
+    if (!(c.eps >= 0.0) || !std::isfinite(c.eps)) return fail(QKROPE_ERR_INVALID, "eps must be finite and >= 0");
+    if (!(c.factor > 0.0) || !std::isfinite(c.factor)) return fail(QKROPE_ERR_INVALID, "factor must be finite and > 0");
+    if (!std::isfinite(c.attention_factor)) return fail(QKROPE_ERR_INVALID, "attention_factor must be finite");
+    if (c.factor == 1.0 && c.attention_factor != 1.0)
+        return fail(QKROPE_ERR_INVALID, "attention_factor must be 1.0 when factor is 1.0");
+    if (c.factor != 1.0 && !(c.high > c.low))
+        return fail(QKROPE_ERR_INVALID, "YaRN needs high > low");
+    if (c.factor != 1.0 && (!std::isfinite(c.low) || !std::isfinite(c.high)))
+        return fail(QKROPE_ERR_INVALID, "YaRN low/high must be finite");
+    if (c.output_fp8 && (!(c.output_quant_scale > 0.0) || !std::isfinite(c.output_quant_scale) ||
+                         !(c.v_quant_scale > 0.0) || !std::isfinite(c.v_quant_scale)))
+        return fail(QKROPE_ERR_INVALID, "FP8 scales must be finite and > 0");
+    const bool ext = c.is_qk_norm && c.sumsq != nullptr;
+    if (ext && (c.norm_elems_q < (int64_t)Hq * D || c.norm_elems_k < (int64_t)Hk * D ||
+                c.norm_elems_q <= 0 || c.norm_elems_k <= 0))
+        return fail(QKROPE_ERR_INVALID, "norm_elems_q/k must be positive and cover the shard's own heads");
+    if (T + c.token_offset >= (int64_t(1) << 31))
+        return fail(QKROPE_ERR_UNSUPPORTED, "token_offset + num_tokens must be < 2^31");
+    if (T == 0 || Hq + Hk + Hv == 0) return ok();
+
+    if (!c.qkv) return fail(QKROPE_ERR_INVALID, "qkv is NULL");
+    if ((Hq && !c.q_out) || (Hk && !c.k_out) || (Hv && !c.v_out)) return fail(QKROPE_ERR_INVALID, "output is NULL");
+    if (c.is_qk_norm && ((Hq && !c.q_weight) || (Hk && !c.k_weight)))
+        return fail(QKROPE_ERR_INVALID, "norm weights are NULL while is_qk_norm is set");
+    const int osize = c.output_fp8 ? 1 : 2;
+    const uintptr_t oalign = c.output_fp8 ? 8 : 16;
+    if (!aligned(c.qkv, 16) || !aligned(c.q_out, oalign) || !aligned(c.k_out, oalign) || !aligned(c.v_out, oalign))
+        return fail(QKROPE_ERR_UNSUPPORTED, "qkv must be 16-byte aligned, outputs %d-byte aligned", (int)oalign);
+    if (c.is_qk_norm && (!aligned(c.q_weight, 16) || !aligned(c.k_weight, 16)))
+        return fail(QKROPE_ERR_UNSUPPORTED, "norm weights must be 16-byte aligned");
+    if (ext && !aligned(c.sumsq, 8)) return fail(QKROPE_ERR_UNSUPPORTED, "sumsq must be 8-byte aligned");
+
+    const int64_t row = (int64_t)(Hq + Hk + Hv) * D;
+    const Range none{0, 0, 0, 0};
+    const Range rin = span_of(c.qkv, T, row, row, 2);
+    const Range rq = span_of(c.q_out, T, (int64_t)Hq * D, (int64_t)Hq * D, osize);
+    const Range rk = span_of(c.k_out, T, (int64_t)Hk * D, (int64_t)Hk * D, osize);
+    const Range rv = span_of(c.v_out, T, (int64_t)Hv * D, (int64_t)Hv * D, osize);
+    const Range rwq = c.is_qk_norm ? span_of(c.q_weight, 1, 0, (int64_t)Hq * D, 2) : none;
+    const Range rwk = c.is_qk_norm ? span_of(c.k_weight, 1, 0, (int64_t)Hk * D, 2) : none;
+    const Range rss = ext ? span_of(c.sumsq, T, 2, 2, 4) : none;
+    const Range outs[3] = {rq, rk, rv};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], rin) || overlap(outs[i], rwq) || overlap(outs[i], rwk) || overlap(outs[i], rss))
+            return fail(QKROPE_ERR_INVALID, "an output overlaps qkv, a weight or sumsq");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return fail(QKROPE_ERR_INVALID, "outputs overlap each other");
+    }
+
+    const bool half = !c.interleave;
+    const int units = D / 8;                   // 16-byte chunks per head: 8, 16 or 32
+    const int64_t n_units[3] = {(int64_t)Hq * units, (int64_t)Hk * units, (int64_t)Hv * units};
+    LaunchShape shape;
+    if (!choose_shape(n_units, 3, &shape))
+        return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
+
+    KernelArgs a;
+    std::memset(&a, 0, sizeof a);
+    const uint16_t *base_in = static_cast<const uint16_t *>(c.qkv);
+    a.in[kQ] = base_in;
+    a.in[kK] = base_in + (int64_t)Hq * D;
+    a.in[kV] = base_in + (int64_t)(Hq + Hk) * D;
+    a.out[kQ] = c.q_out;
+    a.out[kK] = c.k_out;
+    a.out[kV] = c.v_out;
+    for (int r = 0; r < 3; ++r) a.in_stride[r] = row;
+    a.out_stride[kQ] = (int64_t)Hq * D;
+    a.out_stride[kK] = (int64_t)Hk * D;
+    a.out_stride[kV] = (int64_t)Hv * D;
+    a.heads[kQ] = Hq;
+    a.heads[kK] = Hk;
+    a.heads[kV] = Hv;
+    a.weight[0] = static_cast<const uint16_t *>(c.q_weight);
+    a.weight[1] = static_cast<const uint16_t *>(c.k_weight);
+    a.sumsq_in = ext ? c.sumsq : nullptr;
+    a.num_tokens = T;
+    a.head_dim = D;
+    a.rotary_dim = D;
+    a.lanes_per_head = units;
+    a.eps = (float)c.eps;
+    const double nq = ext ? (double)c.norm_elems_q : (double)Hq * D;
+    const double nk = ext ? (double)c.norm_elems_k : (double)Hk * D;
+    a.inv_count[0] = nq > 0 ? (float)(1.0 / nq) : 0.0f;
+    a.inv_count[1] = nk > 0 ? (float)(1.0 / nk) : 0.0f;
+    a.qk_scale = c.output_fp8 ? (float)c.output_quant_scale : 1.0f;
+    a.v_scale = c.output_fp8 ? (float)c.v_quant_scale : 1.0f;
+    a.token_offset = (uint32_t)c.token_offset;
+    a.seq_len = (uint32_t)S;
+    a.hw = (uint32_t)((int64_t)c.pph * c.ppw);
+    a.ppw = (uint32_t)c.ppw;
+    a.pph = (uint32_t)c.pph;
+    a.div_seq = make_fast_div(a.seq_len);
+    a.div_hw = make_fast_div(a.hw);
+    a.div_w = make_fast_div(a.ppw);
+    a.attention_factor = (float)c.attention_factor;
+    // Per pair k of the concatenated [frame | height | width] frequency vector: its axis and the
+    // YaRN-blended angular frequency, in fp64, handed to the kernel as revolutions per position.
+    const double two_pi = 2.0 * 3.14159265358979323846;
+    for (int k = 0, axis = 0, j = 0; k < D / 2; ++k, ++j) {
+        while (j >= C[axis] / 2) {
+            j -= C[axis] / 2;
+            ++axis;
+        }
+        double omega = std::pow(c.base, -2.0 * j / (double)C[axis]);
+        if (c.factor != 1.0) {
+            double rho = (j - c.low) / (c.high - c.low);
+            rho = rho < 0.0 ? 0.0 : (rho > 1.0 ? 1.0 : rho);
+            omega = (omega / c.factor) * rho + omega * (1.0 - rho);
+        }
+        a.omega_rev[k] = (float)(omega / two_pi);
+        a.axis[k] = (uint8_t)axis;
+    }
+    shape.blocks = T;
+
+    KernelKey key;
+    key.head_dim_tpl = D;
+    key.half_split = half;
+    key.norm = !c.is_qk_norm ? kNormNone : (ext ? kNormAcrossExt : kNormAcross);
+    key.src = kSrc3D;
+    key.act = kActBF16;
+    key.fp8 = c.output_fp8 != 0;
+    key.slots = shape.slots;
+    key.slot_uniform = shape.slot_uniform;
+    return do_launch(h, key, shape, a, stream);
 }
 
 }  // namespace
@@ -245,107 +542,37 @@ int qkrope_run_table(qkrope_handle h, const void *q, const void *k, const void *
                      int64_t k_token_stride, int64_t table_token_stride, void *q_out, void *k_out,
                      int64_t q_out_token_stride, int64_t k_out_token_stride, void *stream)
 {
-    if (!h) return fail(QKROPE_ERR_INVALID, "handle is NULL");
-    const int D = head_dim, R = rotary_dim, Hq = num_heads_q, Hk = num_heads_k;
-    const int64_t T = num_tokens;
-    if (T < 0 || Hq < 0 || Hk < 0) return fail(QKROPE_ERR_INVALID, "negative size");
-    if (D <= 0) return fail(QKROPE_ERR_INVALID, "head_dim must be positive");
-    if (R < 0 || R > D || R % 2) return fail(QKROPE_ERR_INVALID, "rotary_dim must be even and in [0, head_dim]");
     if (table_dtype != QKROPE_TABLE_BF16 && table_dtype != QKROPE_TABLE_F32)
         return fail(QKROPE_ERR_INVALID, "table_dtype must be QKROPE_TABLE_BF16 or QKROPE_TABLE_F32");
-    if (norm_mode < QKROPE_NORM_NONE || norm_mode > QKROPE_NORM_ACROSS_HEADS)
-        return fail(QKROPE_ERR_INVALID, "unknown norm_mode %d", norm_mode);
-    if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(QKROPE_ERR_INVALID, "eps must be finite and >= 0");
-    if (D % 8 || D > 256) return fail(QKROPE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and <= 256");
-    const bool half = !interleaved;
-    if (half && R % 16)
-        return fail(QKROPE_ERR_UNSUPPORTED, "half-split pairing needs rotary_dim to be a multiple of 16");
-    if (T >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "num_tokens must be < 2^31");
-    if (T == 0 || Hq + Hk == 0) return ok();
-
-    if (!q && Hq) return fail(QKROPE_ERR_INVALID, "q is NULL");
-    if (!k && Hk) return fail(QKROPE_ERR_INVALID, "k is NULL");
-    if (!q_out && Hq) return fail(QKROPE_ERR_INVALID, "q_out is NULL");
-    if (!k_out && Hk) return fail(QKROPE_ERR_INVALID, "k_out is NULL");
-    if (R > 0 && !rope_table) return fail(QKROPE_ERR_INVALID, "rope_table is NULL");
-    if (norm_mode != QKROPE_NORM_NONE && ((Hq && !q_weight) || (Hk && !k_weight)))
-        return fail(QKROPE_ERR_INVALID, "norm weights are NULL");
-    if (q_token_stride < (int64_t)Hq * D || k_token_stride < (int64_t)Hk * D ||
-        q_out_token_stride < (int64_t)Hq * D || k_out_token_stride < (int64_t)Hk * D)
-        return fail(QKROPE_ERR_INVALID, "token strides must be >= heads*head_dim");
-    if (R > 0 && table_token_stride < R) return fail(QKROPE_ERR_INVALID, "table_token_stride must be >= rotary_dim");
-    if (q_token_stride % 8 || k_token_stride % 8 || q_out_token_stride % 8 || k_out_token_stride % 8)
-        return fail(QKROPE_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) ||
-        !aligned(q_weight, 16) || !aligned(k_weight, 16))
-        return fail(QKROPE_ERR_UNSUPPORTED, "q, k, outputs and weights must be 16-byte aligned");
+    if (rotary_dim > 0 && table_token_stride < rotary_dim)
+        return fail(QKROPE_ERR_INVALID, "table_token_stride must be >= rotary_dim");
+    // the packed [cos | sin] row is the split layout with sin starting rotary_dim/2 later
     const int tsize = table_dtype == QKROPE_TABLE_F32 ? 4 : 2;
-    if (!aligned(rope_table, tsize)) return fail(QKROPE_ERR_UNSUPPORTED, "rope_table is misaligned");
+    const void *sin_table = rope_table && rotary_dim > 0
+        ? static_cast<const uint8_t *>(rope_table) + (int64_t)(rotary_dim / 2) * tsize : nullptr;
+    const TableCall c{q, k, q_weight, k_weight, rope_table, sin_table, table_dtype,
+                      QKROPE_DTYPE_BF16, QKROPE_DTYPE_BF16, 1.0, eps, num_tokens, num_heads_q,
+                      num_heads_k, head_dim, rotary_dim, interleaved, norm_mode, q_token_stride,
+                      k_token_stride, table_token_stride, table_token_stride, q_out, k_out,
+                      q_out_token_stride, k_out_token_stride};
+    return run_table(h, c, stream);
+}
 
-    // Outputs may alias their own input exactly (in place); any other overlap is rejected.
-    const int64_t wq_len = norm_mode == QKROPE_NORM_ACROSS_HEADS ? (int64_t)Hq * D : D;
-    const int64_t wk_len = norm_mode == QKROPE_NORM_ACROSS_HEADS ? (int64_t)Hk * D : D;
-    Range rq = span_of(q, T, q_token_stride, (int64_t)Hq * D, 2);
-    Range rk = span_of(k, T, k_token_stride, (int64_t)Hk * D, 2);
-    Range rqo = span_of(q_out, T, q_out_token_stride, (int64_t)Hq * D, 2);
-    Range rko = span_of(k_out, T, k_out_token_stride, (int64_t)Hk * D, 2);
-    Range rt = span_of(rope_table, R > 0 ? T : 0, table_token_stride, R, tsize);
-    Range rwq = norm_mode != QKROPE_NORM_NONE ? span_of(q_weight, 1, 0, wq_len, 2) : Range{0, 0, 0, 0};
-    Range rwk = norm_mode != QKROPE_NORM_NONE ? span_of(k_weight, 1, 0, wk_len, 2) : Range{0, 0, 0, 0};
-    const bool q_inplace = q_out == q && q_out_token_stride == q_token_stride;
-    const bool k_inplace = k_out == k && k_out_token_stride == k_token_stride;
-    if ((!q_inplace && overlap(rqo, rq)) || overlap(rqo, rk) || overlap(rqo, rt) ||
-        overlap(rqo, rwq) || overlap(rqo, rwk) || overlap(rqo, rko))
-        return fail(QKROPE_ERR_INVALID, "q_out overlaps another argument");
-    if ((!k_inplace && overlap(rko, rk)) || overlap(rko, rq) || overlap(rko, rt) ||
-        overlap(rko, rwq) || overlap(rko, rwk))
-        return fail(QKROPE_ERR_INVALID, "k_out overlaps another argument");
-
-    const int L = next_pow2(D / 8);           // lanes per head: one 16-byte chunk each
-    const int64_t n_units[2] = {(int64_t)Hq * L, (int64_t)Hk * L};
-    LaunchShape shape;
-    if (!choose_shape(n_units, 2, &shape))
-        return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
-
-    KernelArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.in[kQ] = static_cast<const uint16_t *>(q);
-    a.in[kK] = static_cast<const uint16_t *>(k);
-    a.out[kQ] = q_out;
-    a.out[kK] = k_out;
-    a.in_stride[kQ] = q_token_stride;
-    a.in_stride[kK] = k_token_stride;
-    a.out_stride[kQ] = q_out_token_stride;
-    a.out_stride[kK] = k_out_token_stride;
-    a.heads[kQ] = Hq;
-    a.heads[kK] = Hk;
-    a.heads[kV] = 0;
-    a.weight[0] = static_cast<const uint16_t *>(q_weight);
-    a.weight[1] = static_cast<const uint16_t *>(k_weight);
-    a.table = rope_table;
-    a.table_stride = table_token_stride;
-    a.num_tokens = T;
-    a.head_dim = D;
-    a.rotary_dim = R;
-    a.lanes_per_head = L;
-    a.eps = (float)eps;
-    const bool across = norm_mode == QKROPE_NORM_ACROSS_HEADS;
-    a.inv_count[0] = (float)(1.0 / (double)(across ? (int64_t)Hq * D : D));
-    a.inv_count[1] = (float)(1.0 / (double)(across ? (int64_t)Hk * D : D));
-    a.qk_scale = 1.0f;
-    a.v_scale = 1.0f;
-    shape.blocks = T;
-
-    KernelKey key;
-    key.head_dim_tpl = 0;
-    key.half_split = half;
-    key.norm = norm_mode == QKROPE_NORM_NONE ? kNormNone
-             : norm_mode == QKROPE_NORM_PER_HEAD ? kNormPerHead : kNormAcross;
-    key.src = table_dtype == QKROPE_TABLE_F32 ? kSrcTableF32 : kSrcTableBF16;
-    key.fp8 = false;
-    key.slots = shape.slots;
-    key.slot_uniform = shape.slot_uniform;
-    return do_launch(h, key, shape, a, stream);
+int qkrope_run_table_ex(qkrope_handle h, const void *q, const void *k, const void *q_weight,
+                        const void *k_weight, const void *cos_table, const void *sin_table,
+                        int table_dtype, int act_dtype, int out_dtype, double out_scale,
+                        double eps, int64_t num_tokens, int num_heads_q, int num_heads_k,
+                        int head_dim, int rotary_dim, int interleaved, int norm_mode,
+                        int64_t q_token_stride, int64_t k_token_stride, int64_t cos_token_stride,
+                        int64_t sin_token_stride, void *q_out, void *k_out,
+                        int64_t q_out_token_stride, int64_t k_out_token_stride, void *stream)
+{
+    const TableCall c{q, k, q_weight, k_weight, cos_table, sin_table, table_dtype, act_dtype,
+                      out_dtype, out_scale, eps, num_tokens, num_heads_q, num_heads_k, head_dim,
+                      rotary_dim, interleaved, norm_mode, q_token_stride, k_token_stride,
+                      cos_token_stride, sin_token_stride, q_out, k_out, q_out_token_stride,
+                      k_out_token_stride};
+    return run_table(h, c, stream);
 }
 
 int qkrope_run_3d(qkrope_handle h, const void *qkv, const void *q_weight, const void *k_weight,
@@ -356,130 +583,66 @@ int qkrope_run_3d(qkrope_handle h, const void *qkv, const void *q_weight, const 
                   int is_qk_norm, int output_fp8, double output_quant_scale, double v_quant_scale,
                   void *q_out, void *k_out, void *v_out, void *stream)
 {
+    const Rope3DCall c{qkv, q_weight, k_weight, num_tokens, 0, nullptr, 0, 0, ppf, pph, ppw,
+                       {num_frame_channels, num_height_channels, num_width_channels},
+                       num_heads_q, num_heads_k, num_heads_v, head_dim, eps, base, interleave,
+                       factor, low, high, attention_factor, is_qk_norm, output_fp8,
+                       output_quant_scale, v_quant_scale, q_out, k_out, v_out, true};
+    return run_3d(h, c, stream);
+}
+
+int qkrope_run_3d_sharded(qkrope_handle h, const void *qkv, const void *q_weight,
+                          const void *k_weight, int64_t num_tokens, int64_t token_offset,
+                          const float *sumsq, int64_t norm_elems_q, int64_t norm_elems_k,
+                          int ppf, int pph, int ppw, int num_frame_channels,
+                          int num_height_channels, int num_width_channels, int num_heads_q,
+                          int num_heads_k, int num_heads_v, int head_dim, double eps, double base,
+                          int interleave, double factor, double low, double high,
+                          double attention_factor, int is_qk_norm, int output_fp8,
+                          double output_quant_scale, double v_quant_scale, void *q_out,
+                          void *k_out, void *v_out, void *stream)
+{
+    const Rope3DCall c{qkv, q_weight, k_weight, num_tokens, token_offset, sumsq, norm_elems_q,
+                       norm_elems_k, ppf, pph, ppw,
+                       {num_frame_channels, num_height_channels, num_width_channels},
+                       num_heads_q, num_heads_k, num_heads_v, head_dim, eps, base, interleave,
+                       factor, low, high, attention_factor, is_qk_norm, output_fp8,
+                       output_quant_scale, v_quant_scale, q_out, k_out, v_out, false};
+    return run_3d(h, c, stream);
+}
+
+int qkrope_sumsq_3d(qkrope_handle h, const void *qkv, int64_t num_tokens, int num_heads_q,
+                    int num_heads_k, int num_heads_v, int head_dim, float *sumsq, void *stream)
+{
     if (!h) return fail(QKROPE_ERR_INVALID, "handle is NULL");
-    const int D = head_dim, Hq = num_heads_q, Hk = num_heads_k, Hv = num_heads_v;
-    const int C[3] = {num_frame_channels, num_height_channels, num_width_channels};
     const int64_t T = num_tokens;
-    if (T < 0 || Hq < 0 || Hk < 0 || Hv < 0) return fail(QKROPE_ERR_INVALID, "negative size");
-    if (D != 64 && D != 128 && D != 256) return fail(QKROPE_ERR_INVALID, "head_dim must be 64, 128 or 256");
-    for (int i = 0; i < 3; ++i)
-        if (C[i] < 0 || C[i] % 2) return fail(QKROPE_ERR_INVALID, "channel counts must be even and >= 0");
-    if (C[0] + C[1] + C[2] != D) return fail(QKROPE_ERR_INVALID, "channel counts must sum to head_dim");
-    if (ppf <= 0 || pph <= 0 || ppw <= 0) return fail(QKROPE_ERR_INVALID, "ppf, pph, ppw must be positive");
-    const int64_t S = (int64_t)ppf * pph * ppw;
-    if (T % S) return fail(QKROPE_ERR_INVALID, "num_tokens must be a multiple of ppf*pph*ppw");
-    if (!(base > 0.0) || !std::isfinite(base)) return fail(QKROPE_ERR_INVALID, "base must be finite and > 0");
-    if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(QKROPE_ERR_INVALID, "eps must be finite and >= 0");
-    if (!(factor > 0.0) || !std::isfinite(factor)) return fail(QKROPE_ERR_INVALID, "factor must be finite and > 0");
-    if (!std::isfinite(attention_factor)) return fail(QKROPE_ERR_INVALID, "attention_factor must be finite");
-    if (factor == 1.0 && attention_factor != 1.0)
-        return fail(QKROPE_ERR_INVALID, "attention_factor must be 1.0 when factor is 1.0");
-    if (factor != 1.0 && !(high > low) )
-        return fail(QKROPE_ERR_INVALID, "YaRN needs high > low");
-    if (factor != 1.0 && (!std::isfinite(low) || !std::isfinite(high)))
-        return fail(QKROPE_ERR_INVALID, "YaRN low/high must be finite");
-    if (output_fp8 && (!(output_quant_scale > 0.0) || !std::isfinite(output_quant_scale) ||
-                       !(v_quant_scale > 0.0) || !std::isfinite(v_quant_scale)))
-        return fail(QKROPE_ERR_INVALID, "FP8 scales must be finite and > 0");
+    if (T < 0 || num_heads_q < 0 || num_heads_k < 0 || num_heads_v < 0 || head_dim <= 0)
+        return fail(QKROPE_ERR_INVALID, "negative size or non-positive head_dim");
+    if (head_dim % 8) return fail(QKROPE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8");
+    const int64_t chunks = (int64_t)(num_heads_q + num_heads_k) * head_dim / 8;
+    if (chunks > 8192) return fail(QKROPE_ERR_UNSUPPORTED, "(num_heads_q + num_heads_k) * head_dim / 8 must be <= 8192");
     if (T >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "num_tokens must be < 2^31");
-    if (T == 0 || Hq + Hk + Hv == 0) return ok();
-
-    if (!qkv) return fail(QKROPE_ERR_INVALID, "qkv is NULL");
-    if ((Hq && !q_out) || (Hk && !k_out) || (Hv && !v_out)) return fail(QKROPE_ERR_INVALID, "output is NULL");
-    if (is_qk_norm && ((Hq && !q_weight) || (Hk && !k_weight)))
-        return fail(QKROPE_ERR_INVALID, "norm weights are NULL while is_qk_norm is set");
-    const int osize = output_fp8 ? 1 : 2;
-    const uintptr_t oalign = output_fp8 ? 8 : 16;
-    if (!aligned(qkv, 16) || !aligned(q_out, oalign) || !aligned(k_out, oalign) || !aligned(v_out, oalign))
-        return fail(QKROPE_ERR_UNSUPPORTED, "qkv must be 16-byte aligned, outputs %d-byte aligned", (int)oalign);
-    if (is_qk_norm && (!aligned(q_weight, 16) || !aligned(k_weight, 16)))
-        return fail(QKROPE_ERR_UNSUPPORTED, "norm weights must be 16-byte aligned");
-
-    const int64_t row = (int64_t)(Hq + Hk + Hv) * D;
-    Range rin = span_of(qkv, T, row, row, 2);
-    Range rq = span_of(q_out, T, (int64_t)Hq * D, (int64_t)Hq * D, osize);
-    Range rk = span_of(k_out, T, (int64_t)Hk * D, (int64_t)Hk * D, osize);
-    Range rv = span_of(v_out, T, (int64_t)Hv * D, (int64_t)Hv * D, osize);
-    Range rwq = is_qk_norm ? span_of(q_weight, 1, 0, (int64_t)Hq * D, 2) : Range{0, 0, 0, 0};
-    Range rwk = is_qk_norm ? span_of(k_weight, 1, 0, (int64_t)Hk * D, 2) : Range{0, 0, 0, 0};
-    const Range outs[3] = {rq, rk, rv};
-    for (int i = 0; i < 3; ++i) {
-        if (overlap(outs[i], rin) || overlap(outs[i], rwq) || overlap(outs[i], rwk))
-            return fail(QKROPE_ERR_INVALID, "an output overlaps qkv or a weight");
-        for (int j = i + 1; j < 3; ++j)
-            if (overlap(outs[i], outs[j])) return fail(QKROPE_ERR_INVALID, "outputs overlap each other");
-    }
-
-    const bool half = !interleave;
-    const int units = D / 8;                   // 16-byte chunks per head: 8, 16 or 32
-    const int64_t n_units[3] = {(int64_t)Hq * units, (int64_t)Hk * units, (int64_t)Hv * units};
-    LaunchShape shape;
-    if (!choose_shape(n_units, 3, &shape))
-        return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
-
-    KernelArgs a;
-    std::memset(&a, 0, sizeof a);
-    const uint16_t *base_in = static_cast<const uint16_t *>(qkv);
-    a.in[kQ] = base_in;
-    a.in[kK] = base_in + (int64_t)Hq * D;
-    a.in[kV] = base_in + (int64_t)(Hq + Hk) * D;
-    a.out[kQ] = q_out;
-    a.out[kK] = k_out;
-    a.out[kV] = v_out;
-    for (int r = 0; r < 3; ++r) a.in_stride[r] = row;
-    a.out_stride[kQ] = (int64_t)Hq * D;
-    a.out_stride[kK] = (int64_t)Hk * D;
-    a.out_stride[kV] = (int64_t)Hv * D;
-    a.heads[kQ] = Hq;
-    a.heads[kK] = Hk;
-    a.heads[kV] = Hv;
-    a.weight[0] = static_cast<const uint16_t *>(q_weight);
-    a.weight[1] = static_cast<const uint16_t *>(k_weight);
-    a.num_tokens = T;
-    a.head_dim = D;
-    a.rotary_dim = D;
-    a.lanes_per_head = units;
-    a.eps = (float)eps;
-    a.inv_count[0] = Hq ? (float)(1.0 / ((double)Hq * D)) : 0.0f;
-    a.inv_count[1] = Hk ? (float)(1.0 / ((double)Hk * D)) : 0.0f;
-    a.qk_scale = output_fp8 ? (float)output_quant_scale : 1.0f;
-    a.v_scale = output_fp8 ? (float)v_quant_scale : 1.0f;
-    a.seq_len = (uint32_t)S;
-    a.hw = (uint32_t)((int64_t)pph * ppw);
-    a.ppw = (uint32_t)ppw;
-    a.pph = (uint32_t)pph;
-    a.div_seq = make_fast_div(a.seq_len);
-    a.div_hw = make_fast_div(a.hw);
-    a.div_w = make_fast_div(a.ppw);
-    a.attention_factor = (float)attention_factor;
-    // Per pair k of the concatenated [frame | height | width] frequency vector: its axis and the
-    // YaRN-blended angular frequency, in fp64, handed to the kernel as revolutions per position.
-    const double two_pi = 2.0 * 3.14159265358979323846;
-    for (int k = 0, axis = 0, j = 0; k < D / 2; ++k, ++j) {
-        while (j >= C[axis] / 2) {
-            j -= C[axis] / 2;
-            ++axis;
-        }
-        double omega = std::pow(base, -2.0 * j / (double)C[axis]);
-        if (factor != 1.0) {
-            double rho = (j - low) / (high - low);
-            rho = rho < 0.0 ? 0.0 : (rho > 1.0 ? 1.0 : rho);
-            omega = (omega / factor) * rho + omega * (1.0 - rho);
-        }
-        a.omega_rev[k] = (float)(omega / two_pi);
-        a.axis[k] = (uint8_t)axis;
-    }
-    shape.blocks = T;
-
-    KernelKey key;
-    key.head_dim_tpl = D;
-    key.half_split = half;
-    key.norm = is_qk_norm ? kNormAcross : kNormNone;
-    key.src = kSrc3D;
-    key.fp8 = output_fp8 != 0;
-    key.slots = shape.slots;
-    key.slot_uniform = shape.slot_uniform;
-    return do_launch(h, key, shape, a, stream);
+    if (T == 0) return ok();
+    if (!qkv || !sumsq) return fail(QKROPE_ERR_INVALID, "qkv or sumsq is NULL");
+    if (!aligned(qkv, 16)) return fail(QKROPE_ERR_UNSUPPORTED, "qkv must be 16-byte aligned");
+    if (!aligned(sumsq, 8)) return fail(QKROPE_ERR_UNSUPPORTED, "sumsq must be 8-byte aligned");
+    const int64_t row = (int64_t)(num_heads_q + num_heads_k + num_heads_v) * head_dim;
+    if (overlap(span_of(sumsq, T, 2, 2, 4), span_of(qkv, T, row, row, 2)))
+        return fail(QKROPE_ERR_INVALID, "sumsq overlaps qkv");
+    SumsqArgs a;
+    a.qkv = static_cast<const uint16_t *>(qkv);
+    a.out = sumsq;
+    a.row = row;
+    a.q_chunks = num_heads_q * head_dim / 8;
+    a.k_chunks = num_heads_k * head_dim / 8;
+    // one 16-byte chunk per lane where the row fits one workgroup, whole waves
+    const int64_t per = chunks <= 1024 ? chunks : (chunks + (chunks + 1023) / 1024 - 1) / ((chunks + 1023) / 1024);
+    const int threads = (int)std::max<int64_t>(64, (per + 63) / 64 * 64);
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return fail(QKROPE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(g.err));
+    const hipError_t e = launch_sumsq(a, T, threads, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 }  // extern "C"

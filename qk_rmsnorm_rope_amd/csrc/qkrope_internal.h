@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host code (qkrope_api.cpp) and the kernel family
-// (qkrope_kernels.hip). Not installed; the public interface is include/qkrope.h.
+// (qkrope_kernel_impl.h, instantiated by the qkrope_kernels_*.hip translation units). Not
+// installed; the public interface is include/qkrope.h.
 #pragma once
 
 #include <stdint.h>
@@ -10,8 +11,11 @@ namespace qkrope {
 constexpr int kMaxPairs = 128;      // head_dim/2 for head_dim <= 256
 
 enum Region { kQ = 0, kK = 1, kV = 2 };
-enum Norm { kNormNone = 0, kNormPerHead = 1, kNormAcross = 2 };
-enum RopeSrc { kSrcTableF32 = 0, kSrcTableBF16 = 1, kSrc3D = 2 };
+// kNormAcrossExt: across-heads norm whose per-token sums of squares are read from memory
+// (sums over every head of a head-sharded problem, reduced by the caller).
+enum Norm { kNormNone = 0, kNormPerHead = 1, kNormAcross = 2, kNormAcrossExt = 3 };
+enum RopeSrc { kSrcTableF32 = 0, kSrcTableBF16 = 1, kSrcTableF16 = 2, kSrc3D = 3 };
+enum Act { kActBF16 = 0, kActF16 = 1 };   // 16-bit activation (and weight) format
 
 // Magic pair for n / d with n < 2^31: q = (mulhi(n, m) + n) >> l.
 struct FastDiv {
@@ -20,16 +24,20 @@ struct FastDiv {
 
 // Everything one launch needs. Passed by value as the kernel argument; host code fills it.
 struct KernelArgs {
-    // Regions Q, K, V: token t of region r starts at in[r] + t*in_stride[r] (bf16 elements) and
-    // its output at out[r] + t*out_stride[r] (output elements: bf16 or e4m3 bytes).
+    // Regions Q, K, V: token t of region r starts at in[r] + t*in_stride[r] (16-bit activation
+    // elements) and its output at out[r] + t*out_stride[r] (output elements: 16-bit, or e4m3
+    // bytes).
     const uint16_t *in[3];
     void *out[3];
     int64_t in_stride[3];
     int64_t out_stride[3];
     int heads[3];              // Hq, Hk, Hv (Hv = 0: no V region)
-    const uint16_t *weight[2]; // q, k norm weights (bf16) or null
-    const void *table;         // table form: [T, R] cos|sin, fp32 or bf16
-    int64_t table_stride;      // elements
+    const uint16_t *weight[2]; // q, k norm weights (activation format) or null
+    const void *table_cos;     // table form: row t holds cos(theta_t,i), i < R/2 (table dtype)
+    const void *table_sin;     // table form: row t holds sin(theta_t,i)
+    int64_t cos_stride;        // token strides of the two tables, elements
+    int64_t sin_stride;
+    const float *sumsq_in;     // kNormAcrossExt: [T, 2] sums of squares of Q and K rows
 
     int64_t num_tokens;        // = grid size: one workgroup per token
     int head_dim;              // D
@@ -40,7 +48,9 @@ struct KernelArgs {
     float qk_scale;            // FP8 scale for Q/K outputs (1 for bf16)
     float v_scale;             // FP8 scale for V (1 for bf16)
 
-    // 3D positions: s = t mod seq_len; f = s / hw; h = (s / ppw) mod pph; w = s mod ppw.
+    // 3D positions of token t: s = (token_offset + t) mod seq_len; f = s / hw;
+    // h = (s / ppw) mod pph; w = s mod ppw.
+    uint32_t token_offset;
     uint32_t seq_len, hw, ppw, pph;
     FastDiv div_seq, div_hw, div_w;   // for n / seq_len, n / hw, n / ppw
     float attention_factor;
@@ -62,6 +72,7 @@ struct KernelKey {
     bool half_split;
     int norm;           // Norm
     int src;            // RopeSrc
+    int act;            // Act
     bool fp8;
     int slots;          // slots per region (region-major) or per lane (mixed)
     bool slot_uniform;  // region-major slot layout
@@ -72,8 +83,20 @@ struct KernelKey {
 hipError_t launch_3d_d64(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
 hipError_t launch_3d_d128(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
 hipError_t launch_3d_d256(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
-hipError_t launch_table_interleaved(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
-hipError_t launch_table_halfsplit(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_table_interleaved_bf16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_table_halfsplit_bf16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_table_interleaved_f16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_table_halfsplit_f16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+
+// Per-token sums of squares of the Q and K rows of packed QKV: out[2t] = sum over the
+// token's q_elems Q values of x^2, out[2t+1] the same over its k_elems K values (fp32).
+struct SumsqArgs {
+    const uint16_t *qkv;
+    float *out;
+    int64_t row;           // elements per token row of qkv
+    int q_chunks, k_chunks; // 16-byte chunks of the Q and K regions (contiguous, Q first)
+};
+hipError_t launch_sumsq(const SumsqArgs &args, int64_t tokens, int threads, hipStream_t stream);
 
 // Slot counts the kernels are compiled for: region-major 1..4 slots per region, mixed 1, 2, 4
 // slots per lane, limited so that a lane holds at most kMaxChunks 16-byte chunks per token.

@@ -49,6 +49,7 @@ namespace dev {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ---- number formats ---------------------------------------------------------------------------
 
@@ -56,25 +57,47 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// IEEE binary16 -> fp32 is exact (subnormals included).
+__device__ __forceinline__ f32x2 f16x2_to_f32(uint32_t u)
+{
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
+}
+
+// Eight 16-bit activations of a chunk (bf16 or binary16, per ACT) -> fp32, exactly.
+template <int ACT>
 __device__ __forceinline__ void unpack8(const uint4 v, float x[8])
 {
-    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
-    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
-    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+    if (ACT == kActBF16) {
+        x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+        x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+        x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+        x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x2 f = f16x2_to_f32(w[i]);
+            x[2 * i] = f.x;
+            x[2 * i + 1] = f.y;
+        }
+    }
 }
 
-// Two fp32 -> two bf16 with round-to-nearest-even (one v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b)
+// Two fp32 -> two 16-bit values with round-to-nearest-even (one packed conversion on gfx950
+// for bf16; binary16 overflows to +-inf as IEEE rounding does).
+template <int ACT>
+__device__ __forceinline__ uint32_t pack2(float a, float b)
 {
     f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    if (ACT == kActBF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
-__device__ __forceinline__ uint4 pack8_bf16(const float y[8])
+template <int ACT>
+__device__ __forceinline__ uint4 pack8(const float y[8])
 {
-    return make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
-                      pack2_bf16(y[4], y[5]), pack2_bf16(y[6], y[7]));
+    return make_uint4(pack2<ACT>(y[0], y[1]), pack2<ACT>(y[2], y[3]),
+                      pack2<ACT>(y[4], y[5]), pack2<ACT>(y[6], y[7]));
 }
 
 // OCP E4M3 (gfx950's fp8 conversions produce the OCP encoding): finite values beyond the largest
@@ -140,14 +163,6 @@ __device__ __forceinline__ void st8_stream(uint8_t *p, uint2 v)
     else *reinterpret_cast<u32x2 *>(p) = w;
 }
 
-// Store 8 outputs (16 bytes of bf16 or 8 bytes of E4M3) at element `elem` of a row.
-template <bool FP8>
-__device__ __forceinline__ void store8(uint8_t *row, uint32_t elem, const float y[8])
-{
-    if (FP8) st8_stream(row + elem, pack8_e4m3(y));
-    else st16_stream(row + 2 * elem, pack8_bf16(y));
-}
-
 // n / d for n < 2^31 with a host-computed magic pair (m, l): q = (mulhi(n, m) + n) >> l.
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, uint32_t m, uint32_t l)
 {
@@ -200,30 +215,43 @@ __device__ __forceinline__ float group_sum(float v, int width)
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
 
-// Sum of squares of the 8 bf16 of a chunk, from the packed pairs (v_dot2c_f32_bf16).
+// Sum of squares of the 8 activations of a chunk, from the packed pairs (v_dot2c_f32_bf16 or
+// v_dot2_f32_f16: products of 16-bit values are exact in fp32, the sums are fp32).
+template <int ACT>
 __device__ __forceinline__ float sumsq_packed(const uint4 v, float acc)
 {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), __builtin_bit_cast(bf16x2, v.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), __builtin_bit_cast(bf16x2, v.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), __builtin_bit_cast(bf16x2, v.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), __builtin_bit_cast(bf16x2, v.w), acc, false);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (ACT == kActBF16) {
+            const bf16x2 b = __builtin_bit_cast(bf16x2, w[i]);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(b, b, acc, false);
+        } else {
+            const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+            acc = __builtin_amdgcn_fdot2(h, h, acc, false);
+        }
+    }
     return acc;
 }
 
 // ---- the kernel -------------------------------------------------------------------------------
 
 // DT: head_dim as a compile-time constant (64/128/256), or 0 to read it from the arguments.
-// HALF: half-split (NeoX) pairing; otherwise interleaved. NORM: kNormNone/PerHead/Across.
-// SRC: cos/sin from a fp32 or bf16 table, or computed (3D). FP8: E4M3 outputs.
+// HALF: half-split (NeoX) pairing; otherwise interleaved. NORM: kNormNone/PerHead/Across/
+// AcrossExt. SRC: cos/sin from a fp32, bf16 or binary16 table, or computed (3D).
+// ACT: 16-bit activation format (bf16 or binary16). FP8: E4M3 outputs.
 // SU: region-major slots (NS per region); otherwise mixed slots (NS in all).
-template <int DT, bool HALF, int NORM, int SRC, bool FP8, int NS, bool SU>
+template <int DT, bool HALF, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
 __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 {
     constexpr bool IS3D = (SRC == kSrc3D);
+    constexpr bool ACROSS = NORM == kNormAcross || NORM == kNormAcrossExt;
     constexpr int NREG = IS3D ? 3 : 2;          // regions: Q, K (, V)
     constexpr int NSLOT = SU ? NREG * NS : NS;
     constexpr int NPAIR = HALF ? 8 : 4;         // rotation pairs a chunk takes part in
     constexpr bool NEED_BARRIER = IS3D || NORM == kNormAcross;
+    static_assert(!(SRC == kSrcTableBF16 && ACT == kActF16) && !(SRC == kSrcTableF16 && ACT == kActBF16),
+                  "a 16-bit table has the activation format");
     constexpr int ESIZE = FP8 ? 1 : 2;          // output bytes per element
 
     // 3D angles of the token: per pair (cos, -sin, cos, sin), so a half-split lane reads its
@@ -306,6 +334,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         // unconditionally from one basic block so all are in flight together; an idle slot
         // reads its row's first chunk (in bounds, and read by another lane anyway).
         uint4 x[NSLOT], wa[NSLOT];
+        (void)wa;
         {
             const uint16_t *in_q = a.in[kQ] + t * a.in_stride[kQ];
             const uint16_t *in_k = a.in[kK] + t * a.in_stride[kK];
@@ -315,7 +344,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                 const int r = reg[j] < 3 ? reg[j] : 0;
                 const uint32_t o = ok[j] ? 2 * (hoff[j] + off0) : 0u;
                 x[j] = ld16_stream<true>(sel3(r, in_q, in_k, in_v), o);
-                if (NORM == kNormAcross && (SU ? r < 2 : true)) {
+                if (ACROSS && (SU ? r < 2 : true)) {
                     const uint16_t *w = r == 1 ? a.weight[1] : a.weight[0];
                     wa[j] = ld16(w, (ok[j] && r < 2) ? o : 0u);
                 }
@@ -326,7 +355,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         float cs_c[NPAIR], cs_s[NPAIR];
         if (IS3D) {
             // grid position of the token (uniform across the workgroup; t < 2^31)
-            const uint32_t tt = (uint32_t)t;
+            const uint32_t tt = (uint32_t)t + a.token_offset;
             const uint32_t s = tt - fast_div(tt, a.div_seq.m, a.div_seq.l) * a.seq_len;
             const uint32_t pf = fast_div(s, a.div_hw.m, a.div_hw.l);
             const uint32_t rem = s - pf * a.hw;
@@ -342,20 +371,24 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             }
         } else if (unit_ok && rotated) {
             const int half = R / 2;
-            const int64_t trow = t * a.table_stride;
 #pragma unroll
             for (int e = 0; e < NPAIR; ++e) {
                 const int i = pair0 + e;
                 float c = 1.0f, sn = 0.0f;
                 if (HALF || i < half) {
                     if (SRC == kSrcTableF32) {
-                        const float *tab = static_cast<const float *>(a.table) + trow;
-                        c = tab[i];
-                        sn = tab[half + i];
+                        c = (static_cast<const float *>(a.table_cos) + t * a.cos_stride)[i];
+                        sn = (static_cast<const float *>(a.table_sin) + t * a.sin_stride)[i];
                     } else {
-                        const uint16_t *tab = static_cast<const uint16_t *>(a.table) + trow;
-                        c = __uint_as_float((uint32_t)tab[i] << 16);
-                        sn = __uint_as_float((uint32_t)tab[half + i] << 16);
+                        const uint16_t cb = (static_cast<const uint16_t *>(a.table_cos) + t * a.cos_stride)[i];
+                        const uint16_t sb = (static_cast<const uint16_t *>(a.table_sin) + t * a.sin_stride)[i];
+                        if (SRC == kSrcTableBF16) {
+                            c = __uint_as_float((uint32_t)cb << 16);
+                            sn = __uint_as_float((uint32_t)sb << 16);
+                        } else {
+                            c = (float)__builtin_bit_cast(_Float16, cb);
+                            sn = (float)__builtin_bit_cast(_Float16, sb);
+                        }
                     }
                 }
                 cs_c[e] = c;
@@ -368,8 +401,8 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
             ss[j] = 0.0f;
-            if (NORM != kNormNone) {
-                const float v = sumsq_packed(x[j], 0.0f);
+            if (NORM == kNormPerHead || NORM == kNormAcross) {
+                const float v = sumsq_packed<ACT>(x[j], 0.0f);
                 ss[j] = (ok[j] && reg[j] < 2) ? v : 0.0f;
             }
         }
@@ -391,7 +424,12 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         if (NEED_BARRIER) __syncthreads();
 
         float rq = 1.0f, rk = 1.0f;
-        if (NORM == kNormAcross) {
+        if (NORM == kNormAcrossExt) {
+            // sums over every head of the token, reduced by the caller (uniform scalar load)
+            const f32x2 p = reinterpret_cast<const f32x2 *>(a.sumsq_in)[t];
+            rq = __builtin_amdgcn_rsqf(p.x * a.inv_count[0] + a.eps);
+            rk = __builtin_amdgcn_rsqf(p.y * a.inv_count[1] + a.eps);
+        } else if (NORM == kNormAcross) {
             // every wave sums the per-wave partials: lane w of each 16-lane row reads wave w's
             const int w = tid & 15;
             const f32x2 p = w < (nth >> 6) ? s_red[w] : f32x2{0.0f, 0.0f};
@@ -419,14 +457,14 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             const bool isv = NREG == 3 && reg[j] == kV;   // compile-time in the region-major layout
             const bool isq = reg[j] == 0;
             float n[8];
-            unpack8(x[j], n);
+            unpack8<ACT>(x[j], n);
             float scale = FP8 ? (isv ? a.v_scale : a.qk_scale) : 1.0f;
-            if (NORM == kNormAcross && !isv) scale *= isq ? rq : rk;
+            if (ACROSS && !isv) scale *= isq ? rq : rk;
             if (NORM == kNormPerHead)
                 scale *= __builtin_amdgcn_rsqf(ss[j] * (isq ? a.inv_count[0] : a.inv_count[1]) + a.eps);
             if (NORM != kNormNone && !isv) {
                 float w[8];
-                unpack8(NORM == kNormAcross ? wa[j] : (isq ? wq : wk), w);
+                unpack8<ACT>(ACROSS ? wa[j] : (isq ? wq : wk), w);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) n[i] *= w[i];
             }
@@ -462,7 +500,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             } else if (isv) {
                 pk[j] = x[j];                           // V: bit copy
             } else {
-                pk[j] = pack8_bf16(y);
+                pk[j] = pack8<ACT>(y);
             }
         }
 
@@ -482,92 +520,151 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     }
 }
 
+// ---- per-token sums of squares (first phase of a head-sharded across-heads norm) -----------
+//
+// One workgroup per token; lane tid covers chunks tid + i*nth (i < NI) of the token's
+// contiguous Q|K span. Loads are issued unconditionally (clamped to chunk 0, then discarded),
+// then the Q and K partial sums are reduced per wave with DPP/permlane and across waves in LDS.
+template <int NI>
+__global__ void __launch_bounds__(1024) qkrope_sumsq_kernel(const SumsqArgs a)
+{
+    __shared__ f32x2 s_red[16];
+    const int tid = threadIdx.x;
+    const int nth = blockDim.x;
+    const int64_t t = blockIdx.x;
+    const uint16_t *row = a.qkv + t * a.row;
+    const int nq = a.q_chunks, nall = a.q_chunks + a.k_chunks;
+    uint4 x[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int c = tid + i * nth;
+        x[i] = ld16_stream<true>(row, c < nall ? 16u * (uint32_t)c : 0u);
+    }
+    float sq = 0.0f, sk = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int c = tid + i * nth;
+        const float v = sumsq_packed<kActBF16>(x[i], 0.0f);
+        sq += c < nq ? v : 0.0f;
+        sk += (c >= nq && c < nall) ? v : 0.0f;
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    if ((tid & 63) == 0) s_red[tid >> 6] = f32x2{sq, sk};
+    __syncthreads();
+    if (tid < 64) {
+        const int w = tid & 15;
+        const f32x2 p = w < (nth >> 6) ? s_red[w] : f32x2{0.0f, 0.0f};
+        const float q = group_sum(p.x, 16), k = group_sum(p.y, 16);
+        if (tid == 0) reinterpret_cast<f32x2 *>(a.out)[t] = f32x2{q, k};
+    }
+}
+
 // ---- launch helpers ---------------------------------------------------------------------------
 
-template <int DT, bool HALF, int NORM, int SRC, bool FP8, int NS, bool SU>
+template <int DT, bool HALF, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
 hipError_t go(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL((qkrope_kernel<DT, HALF, NORM, SRC, FP8, NS, SU>), dim3((unsigned)s.blocks),
+    hipLaunchKernelGGL((qkrope_kernel<DT, HALF, NORM, SRC, ACT, FP8, NS, SU>), dim3((unsigned)s.blocks),
                        dim3(s.threads), 0, st, a);
     return hipGetLastError();
 }
 
-template <int DT, bool HALF, int NORM, int SRC, bool FP8, int NS, bool SU>
+template <int DT, bool HALF, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
 hipError_t go_if(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if constexpr (slots_compiled(SRC == kSrc3D ? 3 : 2, SU, NS))
-        return go<DT, HALF, NORM, SRC, FP8, NS, SU>(s, a, st);
+        return go<DT, HALF, NORM, SRC, ACT, FP8, NS, SU>(s, a, st);
     else
         return hipErrorInvalidValue;
 }
 
-template <int DT, bool HALF, int NORM, int SRC, bool FP8>
+template <int DT, bool HALF, int NORM, int SRC, int ACT, bool FP8>
 hipError_t by_slots(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if (k.slot_uniform) {
         switch (k.slots) {
-        case 1: return go_if<DT, HALF, NORM, SRC, FP8, 1, true>(s, a, st);
-        case 2: return go_if<DT, HALF, NORM, SRC, FP8, 2, true>(s, a, st);
-        case 3: return go_if<DT, HALF, NORM, SRC, FP8, 3, true>(s, a, st);
-        case 4: return go_if<DT, HALF, NORM, SRC, FP8, 4, true>(s, a, st);
+        case 1: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 1, true>(s, a, st);
+        case 2: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 2, true>(s, a, st);
+        case 3: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 3, true>(s, a, st);
+        case 4: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 4, true>(s, a, st);
         default: return hipErrorInvalidValue;
         }
     }
     switch (k.slots) {
-    case 1: return go_if<DT, HALF, NORM, SRC, FP8, 1, false>(s, a, st);
-    case 2: return go_if<DT, HALF, NORM, SRC, FP8, 2, false>(s, a, st);
-    case 4: return go_if<DT, HALF, NORM, SRC, FP8, 4, false>(s, a, st);
+    case 1: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 1, false>(s, a, st);
+    case 2: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 2, false>(s, a, st);
+    case 4: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 4, false>(s, a, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-}  // namespace dev
-}  // namespace qkrope
+template <int DT, bool HALF, int NORM, int SRC, int ACT>
+hipError_t by_fp8(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
+{
+    return k.fp8 ? by_slots<DT, HALF, NORM, SRC, ACT, true>(k, s, a, st)
+                 : by_slots<DT, HALF, NORM, SRC, ACT, false>(k, s, a, st);
+}
 
-namespace qkrope {
-namespace dev {
+// 3D form for one compile-time head_dim: pairing x norm (none / across heads / across heads
+// from given sums) x output format. Activations are bf16.
+template <int DT, bool HALF>
+hipError_t launch_3d_pairing(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
+{
+    switch (k.norm) {
+    case kNormNone: return by_fp8<DT, HALF, kNormNone, kSrc3D, kActBF16>(k, s, a, st);
+    case kNormAcross: return by_fp8<DT, HALF, kNormAcross, kSrc3D, kActBF16>(k, s, a, st);
+    case kNormAcrossExt: return by_fp8<DT, HALF, kNormAcrossExt, kSrc3D, kActBF16>(k, s, a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
 
-// 3D form for one compile-time head_dim: pairing x norm (none / across heads) x output dtype.
 template <int DT>
 hipError_t launch_3d(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    if (k.src != kSrc3D || k.head_dim_tpl != DT) return hipErrorInvalidValue;
-    if (k.norm == kNormAcross) {
-        if (k.half_split)
-            return k.fp8 ? by_slots<DT, true, kNormAcross, kSrc3D, true>(k, s, a, st)
-                         : by_slots<DT, true, kNormAcross, kSrc3D, false>(k, s, a, st);
-        return k.fp8 ? by_slots<DT, false, kNormAcross, kSrc3D, true>(k, s, a, st)
-                     : by_slots<DT, false, kNormAcross, kSrc3D, false>(k, s, a, st);
-    }
-    if (k.norm == kNormNone) {
-        if (k.half_split)
-            return k.fp8 ? by_slots<DT, true, kNormNone, kSrc3D, true>(k, s, a, st)
-                         : by_slots<DT, true, kNormNone, kSrc3D, false>(k, s, a, st);
-        return k.fp8 ? by_slots<DT, false, kNormNone, kSrc3D, true>(k, s, a, st)
-                     : by_slots<DT, false, kNormNone, kSrc3D, false>(k, s, a, st);
-    }
-    return hipErrorInvalidValue;
+    if (k.src != kSrc3D || k.head_dim_tpl != DT || k.act != kActBF16) return hipErrorInvalidValue;
+    return k.half_split ? launch_3d_pairing<DT, true>(k, s, a, st)
+                        : launch_3d_pairing<DT, false>(k, s, a, st);
 }
 
-template <bool HALF, int NORM>
+template <bool HALF, int ACT, int NORM>
 hipError_t launch_table_src(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    if (k.src == kSrcTableF32) return by_slots<0, HALF, NORM, kSrcTableF32, false>(k, s, a, st);
-    if (k.src == kSrcTableBF16) return by_slots<0, HALF, NORM, kSrcTableBF16, false>(k, s, a, st);
+    constexpr int SRC16 = ACT == kActBF16 ? kSrcTableBF16 : kSrcTableF16;
+    if (k.src == kSrcTableF32) return by_fp8<0, HALF, NORM, kSrcTableF32, ACT>(k, s, a, st);
+    if (k.src == SRC16) return by_fp8<0, HALF, NORM, SRC16, ACT>(k, s, a, st);
     return hipErrorInvalidValue;
 }
 
-// Table form (runtime head_dim, bf16 outputs): pairing x norm mode x table dtype.
-template <bool HALF>
+// Table form (runtime head_dim) for one pairing and activation format: norm mode x table
+// dtype (fp32 or the activation format) x output format (activation format or E4M3).
+template <bool HALF, int ACT>
 hipError_t launch_table(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    if (k.head_dim_tpl != 0 || k.fp8) return hipErrorInvalidValue;
+    if (k.head_dim_tpl != 0 || k.act != ACT || k.half_split != HALF) return hipErrorInvalidValue;
     switch (k.norm) {
-    case kNormNone: return launch_table_src<HALF, kNormNone>(k, s, a, st);
-    case kNormPerHead: return launch_table_src<HALF, kNormPerHead>(k, s, a, st);
-    case kNormAcross: return launch_table_src<HALF, kNormAcross>(k, s, a, st);
+    case kNormNone: return launch_table_src<HALF, ACT, kNormNone>(k, s, a, st);
+    case kNormPerHead: return launch_table_src<HALF, ACT, kNormPerHead>(k, s, a, st);
+    case kNormAcross: return launch_table_src<HALF, ACT, kNormAcross>(k, s, a, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+inline hipError_t launch_sumsq_impl(const SumsqArgs &a, int64_t tokens, int threads, hipStream_t st)
+{
+    const int n = a.q_chunks + a.k_chunks;
+    const int ni = (n + threads - 1) / threads;
+    const dim3 grid((unsigned)tokens), block(threads);
+    switch (ni) {
+    case 1: hipLaunchKernelGGL(qkrope_sumsq_kernel<1>, grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL(qkrope_sumsq_kernel<2>, grid, block, 0, st, a); break;
+    case 3:
+    case 4: hipLaunchKernelGGL(qkrope_sumsq_kernel<4>, grid, block, 0, st, a); break;
+    case 5: case 6: case 7:
+    case 8: hipLaunchKernelGGL(qkrope_sumsq_kernel<8>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace dev

@@ -12,11 +12,13 @@ Workload shapes follow the two API pages the prologue is built from:
     [batch, seq_len, (Hq+Hk+Hv)*head_dim] with seq_len = ppf*pph*ppw, weights [H*head_dim].
 
 Value recipe (stated once, used everywhere):
-  * activations: numpy PCG64(seed).standard_normal in float32, times sigma, rounded to bf16 (RNE);
-  * norm weights: 1 + 0.1*N(0,1) drawn in float64, rounded to float32 then bf16 (RNE);
+  * activations: numpy PCG64(seed).standard_normal in float32, times sigma, rounded to bf16 (RNE)
+    or, for float16 table-form workloads, to IEEE binary16 (RNE);
+  * norm weights: 1 + 0.1*N(0,1) drawn in float64, rounded to float32 then to the activation
+    format (RNE);
   * rope table (table form only): theta_i = t * base**(-2i/rotary_dim) for token t, cos/sin taken
-    in float64 and rounded to float32 (and then to bf16 for a bf16 table). The table is an input
-    of the table form; the pages leave its contents to the caller.
+    in float64 and rounded to float32 (and then to bf16 or binary16 for a 16-bit table). The
+    table is an input of the table form; the pages leave its contents to the caller.
 Every array is dense and contiguous, with no padding and no special values.
 """
 from __future__ import annotations
@@ -39,7 +41,7 @@ ROLE_WK = 3
 
 @dataclass(frozen=True)
 class TableWorkload:
-    """Table-form problem: q, k [T, H, D] bf16; table [T, R] fp32 or bf16."""
+    """Table-form problem: q, k [T, H, D] bf16 or float16; table [T, R] fp32 or 16-bit."""
     name: str
     num_tokens: int
     num_heads_q: int
@@ -47,12 +49,15 @@ class TableWorkload:
     head_dim: int
     rotary_dim: int
     interleaved: bool
-    table_dtype: str          # "f32" or "bf16"
+    table_dtype: str          # "f32", or the activation format "bf16" / "f16"
     seed: int
     eps: float = 1e-6
     base: float = 10000.0
     sigma: float = 1.0
     norm_mode: str = "per_head"   # "none" | "per_head" | "across_heads"
+    act_dtype: str = "bf16"       # "bf16" | "f16": q, k and weights
+    out_dtype: str = "act"        # "act" (the activation format) | "e4m3"
+    out_scale: float = 1.0        # E4M3 outputs: codes of y * out_scale
 
     def with_(self, **kw) -> "TableWorkload":
         return dataclasses.replace(self, **kw)
@@ -149,23 +154,27 @@ def _rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(seed))
 
 
-def bf16_normal(seed: int, n: int, sigma: float = 1.0) -> torch.Tensor:
-    """n draws of sigma*N(0,1) as a flat CPU bfloat16 tensor (float32 draws, RNE to bf16)."""
+_TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def bf16_normal(seed: int, n: int, sigma: float = 1.0, dtype: str = "bf16") -> torch.Tensor:
+    """n draws of sigma*N(0,1) as a flat CPU tensor (float32 draws, RNE to bf16, or to float16
+    with dtype="f16")."""
     rng = _rng(seed)
-    out = torch.empty(n, dtype=torch.bfloat16)
+    out = torch.empty(n, dtype=_TORCH_DTYPES[dtype])
     for start in range(0, n, _CHUNK):
         m = min(_CHUNK, n - start)
         chunk = rng.standard_normal(m, dtype=np.float32)
         if sigma != 1.0:
             chunk *= np.float32(sigma)
-        out[start:start + m] = torch.from_numpy(chunk).to(torch.bfloat16)
+        out[start:start + m] = torch.from_numpy(chunk).to(out.dtype)
     return out
 
 
-def bf16_weights(seed: int, n: int) -> torch.Tensor:
-    """Norm weights 1 + 0.1*N(0,1), drawn in float64, as a CPU bfloat16 tensor."""
+def bf16_weights(seed: int, n: int, dtype: str = "bf16") -> torch.Tensor:
+    """Norm weights 1 + 0.1*N(0,1), drawn in float64, as a CPU bfloat16 (or float16) tensor."""
     w = 1.0 + 0.1 * _rng(seed).standard_normal(n)
-    return torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16)
+    return torch.from_numpy(w.astype(np.float32)).to(_TORCH_DTYPES[dtype])
 
 
 def rope_table(num_tokens: int, rotary_dim: int, base: float, dtype: str) -> torch.Tensor:
@@ -175,23 +184,21 @@ def rope_table(num_tokens: int, rotary_dim: int, base: float, dtype: str) -> tor
     theta = np.arange(num_tokens, dtype=np.float64)[:, None] * inv[None, :]
     tab = np.concatenate([np.cos(theta), np.sin(theta)], axis=1).astype(np.float32)
     t = torch.from_numpy(np.ascontiguousarray(tab))
-    if dtype == "f32":
-        return t
-    if dtype == "bf16":
-        return t.to(torch.bfloat16)
-    raise ValueError(f"table dtype {dtype!r}")
+    if dtype not in _TORCH_DTYPES:
+        raise ValueError(f"table dtype {dtype!r}")
+    return t.to(_TORCH_DTYPES[dtype])
 
 
 def table_inputs(w: TableWorkload) -> dict:
-    """CPU tensors for a table-form workload: q, k [T,H,D] bf16; weights; table."""
-    T, D = w.num_tokens, w.head_dim
-    q = bf16_normal(w.seed + ROLE_QKV, T * w.num_heads_q * D, w.sigma).view(T, w.num_heads_q, D)
-    k = bf16_normal(w.seed + ROLE_K, T * w.num_heads_k * D, w.sigma).view(T, w.num_heads_k, D)
+    """CPU tensors for a table-form workload: q, k [T,H,D] (bf16 or float16); weights; table."""
+    T, D, a = w.num_tokens, w.head_dim, w.act_dtype
+    q = bf16_normal(w.seed + ROLE_QKV, T * w.num_heads_q * D, w.sigma, a).view(T, w.num_heads_q, D)
+    k = bf16_normal(w.seed + ROLE_K, T * w.num_heads_k * D, w.sigma, a).view(T, w.num_heads_k, D)
     wlen_q = D if w.norm_mode != "across_heads" else w.num_heads_q * D
     wlen_k = D if w.norm_mode != "across_heads" else w.num_heads_k * D
     return dict(q=q, k=k,
-                q_weight=bf16_weights(w.seed + ROLE_WQ, wlen_q),
-                k_weight=bf16_weights(w.seed + ROLE_WK, wlen_k),
+                q_weight=bf16_weights(w.seed + ROLE_WQ, wlen_q, a),
+                k_weight=bf16_weights(w.seed + ROLE_WK, wlen_k, a),
                 rope_table=rope_table(T, w.rotary_dim, w.base, w.table_dtype))
 
 

@@ -5,6 +5,10 @@ Match criteria (element by element against the fp64 oracle on the same seeded in
   * bf16 Q/K: |gpu - ref| <= 2^-7 * |ref| + 1e-3, with ref the oracle's unrounded fp64 value.
   * FP8 E4M3 outputs: within one code of the oracle's round-to-nearest-even code (codes compared
     in sign-magnitude order, so +0 and -0 are the same point).
+  * float16 Q/K (table form with binary16 activations): |gpu - ref| <= 2^-10 * |ref| + 2^-14.
+    One rounding to binary16 costs at most half an ulp (2^-11 relative for normal values); fp32
+    arithmetic before it can move a value across one rounding boundary, hence one ulp (2^-10);
+    the absolute term is the smallest normal binary16 (subnormal outputs have a fixed quantum).
 """
 from __future__ import annotations
 
@@ -33,6 +37,24 @@ def assert_bf16_close(gpu: torch.Tensor, ref: np.ndarray, what: str) -> None:
     g = to_f64(gpu).reshape(ref.shape)
     err = np.abs(g - ref)
     bound = BF16_REL * np.abs(ref) + BF16_ABS
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        idx = np.unravel_index(i, ref.shape)
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; first at {idx}: "
+            f"gpu={g[idx]!r} ref={ref[idx]!r} err={err[idx]:.3g} bound={bound[idx]:.3g}")
+
+
+F16_REL = 2.0 ** -10
+F16_ABS = 2.0 ** -14
+
+
+def assert_f16_close(gpu: torch.Tensor, ref: np.ndarray, what: str) -> None:
+    assert gpu.dtype == torch.float16, f"{what}: expected float16 output, got {gpu.dtype}"
+    g = to_f64(gpu).reshape(ref.shape)
+    err = np.abs(g - ref)
+    bound = F16_REL * np.abs(ref) + F16_ABS
     bad = ~(err <= bound)
     if bad.any():
         i = np.flatnonzero(bad.ravel())[0]
