@@ -13,6 +13,8 @@ oracle on a bounded sample of the same workload).
 Other modes (used to produce the committed profiles):
     --profile-run       only warmup + steps launches, no CPU baseline, no JSON line
     --copy-calibration  launches a plain elementwise copy of known size (counter calibration)
+    --crossover         fused table-form call vs an eager torch chain over 64..65536 tokens (the
+                        fused-vs-eager threshold of vLLM-Omni's fused_qk_norm_rope_min_tokens)
 """
 from __future__ import annotations
 
@@ -42,20 +44,38 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def is_3d(w) -> bool:
+    return hasattr(w, "row_elems")
+
+
+def is_sharded(w) -> bool:
+    return is_3d(w) and w.head_shards > 1
+
+
 def algorithmic_bytes(w) -> int:
-    """Bytes the method itself must move per launch: inputs read once, outputs written once."""
-    if hasattr(w, "row_elems"):             # 3D form
+    """Bytes the method itself must move per launch of the step's dominant kernel: inputs read
+    once, outputs written once (for a head-sharded rank: the apply kernel, which also reads the
+    [T, 2] fp32 sums)."""
+    if is_3d(w):
         T = w.num_tokens
         out_b = 1 if w.output_fp8 else 2
         read = T * w.row_elems * 2
         if w.is_qk_norm:
             read += (w.num_heads_q + w.num_heads_k) * w.head_dim * 2
+            if is_sharded(w):
+                read += T * 8
         return read + T * w.row_elems * out_b
     T, D = w.num_tokens, w.head_dim
     qk = T * (w.num_heads_q + w.num_heads_k) * D * 2
     tab = T * w.rotary_dim * (4 if w.table_dtype == "f32" else 2)
     wts = 0 if w.norm_mode == "none" else 2 * D * 2
-    return qk + tab + wts + qk
+    out = qk // 2 if w.out_dtype == "e4m3" else qk
+    return qk + tab + wts + out
+
+
+def sumsq_bytes(w) -> int:
+    """Algorithmic bytes of the per-token sum-of-squares kernel of a head-sharded rank."""
+    return w.num_tokens * ((w.num_heads_q + w.num_heads_k) * w.head_dim * 2 + 8)
 
 
 def traffic_from_profile(w) -> dict | None:
@@ -85,7 +105,19 @@ def make_launcher(w, dev, sets):
     from qk_rmsnorm_rope_amd import workloads as wl
 
     calls = []
-    if hasattr(w, "row_elems"):
+    if is_sharded(w):
+        # one rank: the all-reduce of the sums over the head group is the identity, so the
+        # apply kernel reads the rank's own sums (same bytes and arithmetic as the reduced ones)
+        cpu = wl.rope3d_inputs(w)
+        for _ in range(sets):
+            g = {k: v.to(dev) for k, v in cpu.items()}
+            odt = torch.float8_e4m3fn if w.output_fp8 else torch.bfloat16
+            outs = [torch.empty((w.num_tokens, H, w.head_dim), dtype=odt, device=dev)
+                    for H in (w.num_heads_q, w.num_heads_k, w.num_heads_v)]
+            ss = torch.empty((w.num_tokens, 2), dtype=torch.float32, device=dev)
+            calls.append(qr.PreparedSharded3D(w, g["qkv"], g["q_weight"], g["k_weight"], *outs,
+                                              ss, ss))
+    elif is_3d(w):
         cpu = wl.rope3d_inputs(w)
         for _ in range(sets):
             g = {k: v.to(dev) for k, v in cpu.items()}
@@ -95,15 +127,17 @@ def make_launcher(w, dev, sets):
         cpu = wl.table_inputs(w)
         for _ in range(sets):
             g = {k: v.to(dev) for k, v in cpu.items()}
-            qo, ko = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+            odt = torch.float8_e4m3fn if w.out_dtype == "e4m3" else g["q"].dtype
+            qo = torch.empty(g["q"].shape, dtype=odt, device=dev)
+            ko = torch.empty(g["k"].shape, dtype=odt, device=dev)
             calls.append(qr.PreparedTable(g["q"], g["k"], g["q_weight"], g["k_weight"],
                                           g["rope_table"], w.eps, q_out=qo, k_out=ko,
                                           rotary_dim=w.rotary_dim, interleaved=w.interleaved,
-                                          norm_mode=w.norm_mode))
+                                          norm_mode=w.norm_mode, out_scale=w.out_scale))
 
     def launch(i):
         calls[i % sets]()
-    return cpu, launch
+    return cpu, launch, calls
 
 
 def time_launches(launch, steps, warmup):
@@ -133,15 +167,17 @@ def cpu_baseline(w, cpu_inputs, budget_s: float = 12.0) -> dict:
 
     threads = oracle.num_threads()
     done, t_used, chunk = 0, 0.0, 64
-    if hasattr(w, "row_elems"):
+    if is_3d(w):
         x = cpu_inputs["qkv"].reshape(-1, w.row_elems)
-        limit = w.num_tokens
-    else:
-        limit = w.num_tokens
+    limit = w.num_tokens
     while t_used < budget_s and done < limit:
         n = min(chunk, limit - done)
         t0 = time.perf_counter()
-        if hasattr(w, "row_elems"):
+        if is_3d(w):
+            if is_sharded(w):
+                oracle.sumsq_3d(x[done:done + n], num_heads_q=w.num_heads_q,
+                                num_heads_k=w.num_heads_k, num_heads_v=w.num_heads_v,
+                                head_dim=w.head_dim)
             q, k, v = oracle.run_3d_workload(w, x[done:done + n], cpu_inputs["q_weight"],
                                              cpu_inputs["k_weight"], token_offset=done)
             if w.output_fp8:
@@ -156,7 +192,12 @@ def cpu_baseline(w, cpu_inputs, budget_s: float = 12.0) -> dict:
                                     cpu_inputs["rope_table"][done:done + n], w.eps,
                                     rotary_dim=w.rotary_dim, interleaved=w.interleaved,
                                     norm_mode=w.norm_mode)
-            oracle.bf16_encode(q), oracle.bf16_encode(k)
+            if w.out_dtype == "e4m3":
+                oracle.e4m3_encode(q, w.out_scale), oracle.e4m3_encode(k, w.out_scale)
+            elif w.act_dtype == "f16":
+                oracle.f16_encode(q), oracle.f16_encode(k)
+            else:
+                oracle.bf16_encode(q), oracle.bf16_encode(k)
         t_used += time.perf_counter() - t0
         done += n
         chunk = min(chunk * 2, 4096)
@@ -177,6 +218,73 @@ def copy_calibration(dev, steps, warmup):
                       "mean_launch_us": mean * 1e6, "gbs": 4 * n / mean / 1e9}), flush=True)
 
 
+def eager_table_chain(q, k, q_weight, k_weight, table, eps, rotary_dim, interleaved):
+    """The unfused chain a consumer keeps below the fused-vs-eager threshold: torch's RMSNorm
+    per head, then RoPE from the packed [cos | sin] table with torch elementwise ops, in fp32,
+    rounded back to the activation dtype (several kernel launches per call). A timing
+    comparator only; correctness is judged against the oracle elsewhere."""
+    import torch
+    import torch.nn.functional as F
+    R, D = rotary_dim, q.shape[-1]
+    cos = table[:, : R // 2].float().unsqueeze(1)
+    sin = table[:, R // 2: R].float().unsqueeze(1)
+    outs = []
+    for x, w in ((q, q_weight), (k, k_weight)):
+        n = F.rms_norm(x.float(), (D,), w.float(), eps)
+        if interleaved:
+            a, b = n[..., 0:R:2], n[..., 1:R:2]
+            rot = torch.stack((a * cos - b * sin, b * cos + a * sin), dim=-1).flatten(-2)
+        else:
+            a, b = n[..., : R // 2], n[..., R // 2: R]
+            rot = torch.cat((a * cos - b * sin, b * cos + a * sin), dim=-1)
+        outs.append(torch.cat((rot, n[..., R:]), dim=-1).to(x.dtype))
+    return tuple(outs)
+
+
+def crossover(dev, warmup) -> None:
+    """Per-call wall time of the fused table-form call (through the page's signature, outputs
+    allocated per call as a consumer does) and of the eager chain, for 64..65536 tokens of the
+    24-head, head_dim-128 interleaved workload with a bf16 table; one JSON line per size, then
+    the smallest size from which on the fused call is never slower."""
+    import torch
+    import qk_rmsnorm_rope_amd as qr
+    from qk_rmsnorm_rope_amd import workloads as wl
+
+    sizes = [64 << i for i in range(11)]
+    w = wl.TABLE_INTERLEAVED_T4096.with_(num_tokens=sizes[-1])
+    g = {k: v.to(dev) for k, v in wl.table_inputs(w).items()}
+    rows = []
+    for T in sizes:
+        q, k, tab = g["q"][:T], g["k"][:T], g["rope_table"][:T]
+        args = (q, k, g["q_weight"], g["k_weight"], tab, w.eps)
+        fused = lambda: qr.fused_qk_norm_rope(*args, rotary_dim=w.rotary_dim, interleaved=True)
+        eager = lambda: eager_table_chain(*args, w.rotary_dim, True)
+        if T == sizes[0]:
+            a, b = fused(), eager()
+            torch.cuda.synchronize()
+            assert all((x.float() - y.float()).abs().max().item() < 0.05 for x, y in zip(a, b))
+        n = max(20, min(2000, (1 << 22) // T))
+        res = {"tokens": T, "calls": n}
+        for name, fn in (("fused_us", fused), ("eager_us", eager)):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            res[name] = (time.perf_counter() - t0) / n * 1e6
+        rows.append(res)
+        print(json.dumps(res), flush=True)
+    cross = None
+    for i in range(len(rows)):
+        if all(r["fused_us"] <= r["eager_us"] for r in rows[i:]):
+            cross = rows[i]["tokens"]
+            break
+    print(json.dumps({"crossover_tokens": cross, "note": "smallest measured size from which "
+                      "the fused call is never slower than the eager chain"}), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +296,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--crossover", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -202,12 +311,27 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(dev, args.steps, args.warmup)
         return 0
+    if args.crossover:
+        crossover(dev, args.warmup)
+        return 0
     w = wl.WORKLOADS[args.workload]
-    cpu_inputs, launch = make_launcher(w, dev, args.sets)
+    cpu_inputs, launch, calls = make_launcher(w, dev, args.sets)
     torch.cuda.synchronize()
-    total, mean_launch = time_launches(launch, args.steps, args.warmup)
+    total, mean_step = time_launches(launch, args.steps, args.warmup)
+    mean_launch = mean_step
+    extra = {}
+    if is_sharded(w):
+        # the step is two kernels: time each on its own for the per-kernel rooflines
+        _, mean_launch = time_launches(lambda i: calls[i % args.sets].apply(), args.steps,
+                                       args.warmup)
+        _, mean_sumsq = time_launches(lambda i: calls[i % args.sets].sumsq(), args.steps,
+                                      args.warmup)
+        extra = {"sumsq_kernel": {"achieved": sumsq_bytes(w) / mean_sumsq / 1e9,
+                                  "unit": "GB/s", "mean_launch_us": mean_sumsq * 1e6,
+                                  "algorithmic_bytes": sumsq_bytes(w)},
+                 "apply_kernel_us": mean_launch * 1e6, "step_us": mean_step * 1e6}
     if args.profile_run:
-        print(f"{w.name}: {args.steps} launches, mean {mean_launch * 1e6:.1f} us", flush=True)
+        print(f"{w.name}: {args.steps} launches, mean {mean_step * 1e6:.1f} us", flush=True)
         return 0
 
     nbytes = algorithmic_bytes(w)
@@ -227,14 +351,18 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": w.num_tokens, "io_dtype": "bf16",
+        "config": {"workload": w.name, "tokens": w.num_tokens,
+                   "io_dtype": getattr(w, "act_dtype", "bf16"),
                    "heads": [w.num_heads_q, w.num_heads_k, getattr(w, "num_heads_v", 0)],
-                   "head_dim": w.head_dim, "parallelism": "single-gpu",
+                   "head_dim": w.head_dim,
+                   "parallelism": (f"one rank of {w.head_shards} head shards"
+                                   if is_sharded(w) else "single-gpu"),
                    "buffer_sets": args.sets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "algorithmic_bytes": nbytes, "mean_launch_us": mean_launch * 1e6},
+        **extra,
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, cpu_inputs)

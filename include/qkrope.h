@@ -78,6 +78,19 @@ const char *qkrope_status_str(int status);
 const char *qkrope_last_error(void);
 
 /*
+ * Fused-vs-eager token threshold (vLLM-Omni "vllm_omni.diffusion.layers.fused_qk_norm_rope",
+ * fused_qk_norm_rope_min_tokens): below some number of tokens per call a fused call is bound by
+ * host dispatch and a consumer may keep its eager chain. The caller passes the threshold it
+ * measured (`default_tokens`, >= 0); a deployment overrides it for every caller through the
+ * environment variable QKROPE_FUSED_MIN_TOKENS, read at every call (nothing is cached):
+ *   unset, empty or only blanks  -> default_tokens;
+ *   a non-negative decimal integer (surrounding blanks allowed) -> that value, 0 = always fuse;
+ *   anything else -> QKROPE_ERR_INVALID (and *out is left unchanged).
+ * Host-only; touches no device.
+ */
+int qkrope_min_tokens(int64_t default_tokens, int64_t *out);
+
+/*
  * Table form (vLLM-Omni fused_qk_norm_rope).
  *
  *   q          [num_tokens, num_heads_q, head_dim] bf16; token t starts at q + t*q_token_stride
@@ -96,9 +109,9 @@ const char *qkrope_last_error(void);
  *   k_out      q_out == q (with equal strides) works in place, likewise k_out == k; any other
  *              overlap between an output and an input is QKROPE_ERR_INVALID.
  *
- * Limits (else QKROPE_ERR_UNSUPPORTED): head_dim a multiple of 8 and <= 256; half-split needs
- * rotary_dim to be a multiple of 16 (each half a whole number of 16-byte chunks);
- * num_tokens < 2^31.
+ * Limits (else QKROPE_ERR_UNSUPPORTED): head_dim a multiple of 8 and <= 256; num_tokens < 2^31.
+ * Any even rotary_dim works with either pairing (half-split partners that straddle 16-byte
+ * chunks, i.e. rotary_dim % 16 != 0, are exchanged through LDS, a slower path).
  * num_tokens == 0 (or zero heads) is a valid no-op.
  */
 int qkrope_run_table(qkrope_handle h,

@@ -8,6 +8,7 @@ Entry points, with the names of the C ABI:
   qkrope_create / qkrope_destroy / qkrope_run_table / qkrope_run_3d
   qkrope_run_table_ex (split cos/sin tables, float16 activations, E4M3 outputs)
   qkrope_sumsq_3d / qkrope_run_3d_sharded (sequence- and head-sharded 3D form)
+  qkrope_min_tokens (fused-vs-eager threshold, QKROPE_FUSED_MIN_TOKENS)
 and the two page-shaped conveniences that allocate outputs:
   fused_qk_norm_rope      -- vLLM-Omni "vllm_omni.diffusion.layers.fused_qk_norm_rope"
   fused_qk_rmsnorm_rope   -- FlashInfer "flashinfer.norm.fused_qk_rmsnorm_rope"
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.qkrope_run_3d.argtypes = [P, P, P, P, I64, I, I, I, I, I, I, I, I, I, I,
                                     D, D, I, D, D, D, D, I, I, D, D, P, P, P, P]
         L.qkrope_run_3d.restype = I
+        L.qkrope_min_tokens.argtypes = [I64, ctypes.POINTER(I64)]
+        L.qkrope_min_tokens.restype = I
         L.qkrope_run_table_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, D, D, I64, I, I, I, I,
                                           I, I, I64, I64, I64, I64, P, P, I64, I64, P]
         L.qkrope_run_table_ex.restype = I
@@ -109,6 +112,20 @@ def qkrope_create(device: int = 0) -> int:
 
 def qkrope_destroy(handle) -> None:
     _check(lib().qkrope_destroy(handle), "qkrope_destroy")
+
+
+def qkrope_min_tokens(default: int) -> int:
+    """Token count below which a consumer should keep its eager chain: `default` unless the
+    QKROPE_FUSED_MIN_TOKENS environment variable overrides it (read at every call; 0 = always
+    fuse; unset or blank = default; anything but a non-negative integer raises ValueError)."""
+    out = ctypes.c_int64()
+    _check(lib().qkrope_min_tokens(int(default), ctypes.byref(out)), "qkrope_min_tokens")
+    return out.value
+
+
+def fused_qk_norm_rope_min_tokens(default: int) -> int:
+    """vLLM-Omni's fused_qk_norm_rope_min_tokens signature over qkrope_min_tokens."""
+    return qkrope_min_tokens(default)
 
 
 def _handle_for(device: torch.device) -> int:
@@ -411,34 +428,99 @@ class Prepared3D:
 
 
 class PreparedTable:
-    """Arguments of one qkrope_run_table call marshalled once (see Prepared3D)."""
+    """Arguments of one table-form call marshalled once (see Prepared3D): qkrope_run_table for
+    bf16 in and out with a packed table, qkrope_run_table_ex otherwise (float16 activations or
+    E4M3 outputs; the packed table is passed as its cos and sin column views)."""
 
     def __init__(self, q, k, q_weight, k_weight, rope_table, eps, *, q_out, k_out,
                  head_dim=None, rotary_dim=None, interleaved=False, norm_mode="per_head",
-                 stream=None):
-        qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, q_out=q_out, k_out=k_out,
-                         head_dim=head_dim, rotary_dim=rotary_dim, interleaved=interleaved,
-                         norm_mode=norm_mode, stream=stream)
+                 out_scale=1.0, stream=None):
         D = head_dim if head_dim is not None else q.shape[-1]
         Hq = q.shape[1] if q.dim() == 3 else q.shape[1] // D
         Hk = k.shape[1] if k.dim() == 3 else k.shape[1] // D
         T = q.shape[0]
         R = rotary_dim if rotary_dim is not None else rope_table.shape[-1]
-        tdt = QKROPE_TABLE_F32 if rope_table.dtype == torch.float32 else QKROPE_TABLE_BF16
+        common = dict(head_dim=D, rotary_dim=R, interleaved=interleaved, norm_mode=norm_mode,
+                      stream=stream)
         ts = rope_table.stride(0) if T > 1 else rope_table.shape[1]
-        self._fn = lib().qkrope_run_table
-        self._args = (
-            _handle_for(q.device), _ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight),
-            _ptr(rope_table), tdt, float(eps), T, Hq, Hk, D, R, int(bool(interleaved)),
-            NORM_MODES[norm_mode], _rows(q, Hq, D, "q"), _rows(k, Hk, D, "k"), ts, _ptr(q_out),
-            _ptr(k_out), _rows(q_out, Hq, D, "q_out"), _rows(k_out, Hk, D, "k_out"),
-            _stream(q.device, stream))
+        strides = (_rows(q, Hq, D, "q"), _rows(k, Hk, D, "k"))
+        out_strides = (_rows(q_out, Hq, D, "q_out"), _rows(k_out, Hk, D, "k_out"))
+        h, st = _handle_for(q.device), _stream(q.device, stream)
+        if q.dtype == torch.bfloat16 and q_out.dtype == torch.bfloat16:
+            qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, q_out=q_out, k_out=k_out,
+                             **common)
+            tdt = QKROPE_TABLE_F32 if rope_table.dtype == torch.float32 else QKROPE_TABLE_BF16
+            self._fn, self._name = lib().qkrope_run_table, "qkrope_run_table"
+            self._args = (h, _ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight), _ptr(rope_table),
+                          tdt, float(eps), T, Hq, Hk, D, R, int(bool(interleaved)),
+                          NORM_MODES[norm_mode], *strides, ts, _ptr(q_out), _ptr(k_out),
+                          *out_strides, st)
+        else:
+            cos_t, sin_t = rope_table[:, : R // 2], rope_table[:, R // 2: R]
+            qkrope_run_table_ex(q, k, q_weight, k_weight, cos_t, sin_t, eps, q_out=q_out,
+                                k_out=k_out, out_scale=out_scale, **common)
+            self._fn, self._name = lib().qkrope_run_table_ex, "qkrope_run_table_ex"
+            self._args = (h, _ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight), _ptr(cos_t),
+                          _ptr(sin_t), _DTYPE_CODES[rope_table.dtype], _DTYPE_CODES[q.dtype],
+                          _DTYPE_CODES[q_out.dtype], float(out_scale), float(eps), T, Hq, Hk, D,
+                          R, int(bool(interleaved)), NORM_MODES[norm_mode], *strides, ts, ts,
+                          _ptr(q_out), _ptr(k_out), *out_strides, st)
         self._keep = (q, k, q_weight, k_weight, rope_table, q_out, k_out)
 
     def __call__(self) -> None:
         s = self._fn(*self._args)
         if s != QKROPE_OK:
-            _check(s, "qkrope_run_table")
+            _check(s, self._name)
+
+
+class PreparedSharded3D:
+    """One rank's step of a head-sharded 3D run, marshalled once: qkrope_sumsq_3d into `sumsq`,
+    then qkrope_run_3d_sharded normalising with `sumsq_total` over `norm_elems_*` elements.
+    Between the two a multi-rank caller all-reduces sumsq into sumsq_total; with one rank they
+    may be the same tensor. Calling the object runs both; .sumsq() and .apply() run one each."""
+
+    def __init__(self, w, qkv, q_weight, k_weight, q_out, k_out, v_out, sumsq, sumsq_total,
+                 token_offset=0, stream=None):
+        Hq, Hk, Hv, D = w.num_heads_q, w.num_heads_k, w.num_heads_v, w.head_dim
+        T = qkv.numel() // w.row_elems
+        ne_q, ne_k = Hq * D * w.head_shards, Hk * D * w.head_shards
+        qkrope_sumsq_3d(qkv, num_heads_q=Hq, num_heads_k=Hk, num_heads_v=Hv, head_dim=D,
+                        out=sumsq, stream=stream)
+        qkrope_run_3d_sharded(
+            qkv, q_weight, k_weight, token_offset=token_offset, sumsq=sumsq_total,
+            norm_elems_q=ne_q, norm_elems_k=ne_k, ppf=w.ppf, pph=w.pph, ppw=w.ppw,
+            num_frame_channels=w.num_frame_channels, num_height_channels=w.num_height_channels,
+            num_width_channels=w.num_width_channels, num_heads_q=Hq, num_heads_k=Hk,
+            num_heads_v=Hv, head_dim=D, q_out=q_out, k_out=k_out, v_out=v_out, eps=w.eps,
+            base=w.base, interleave=w.interleave, factor=w.factor, low=w.low, high=w.high,
+            attention_factor=w.attention_factor, is_qk_norm=w.is_qk_norm,
+            output_fp8=w.output_fp8, output_quant_scale=w.output_quant_scale,
+            v_quant_scale=w.v_quant_scale, stream=stream)
+        h, st = _handle_for(qkv.device), _stream(qkv.device, stream)
+        L = lib()
+        self._s = (L.qkrope_sumsq_3d, (h, _ptr(qkv), T, Hq, Hk, Hv, D, _ptr(sumsq), st))
+        self._a = (L.qkrope_run_3d_sharded, (
+            h, _ptr(qkv), _ptr(q_weight), _ptr(k_weight), T, int(token_offset), _ptr(sumsq_total),
+            ne_q, ne_k, w.ppf, w.pph, w.ppw, w.num_frame_channels, w.num_height_channels,
+            w.num_width_channels, Hq, Hk, Hv, D, float(w.eps), float(w.base), int(w.interleave),
+            float(w.factor), float(w.low), float(w.high), float(w.attention_factor),
+            int(w.is_qk_norm), int(w.output_fp8), float(w.output_quant_scale),
+            float(w.v_quant_scale), _ptr(q_out), _ptr(k_out), _ptr(v_out), st))
+        self._keep = (qkv, q_weight, k_weight, q_out, k_out, v_out, sumsq, sumsq_total)
+
+    def sumsq(self) -> None:
+        s = self._s[0](*self._s[1])
+        if s != QKROPE_OK:
+            _check(s, "qkrope_sumsq_3d")
+
+    def apply(self) -> None:
+        s = self._a[0](*self._a[1])
+        if s != QKROPE_OK:
+            _check(s, "qkrope_run_3d_sharded")
+
+    def __call__(self) -> None:
+        self.sumsq()
+        self.apply()
 
 
 def run_workload_3d(w, qkv, q_weight, k_weight, q_out=None, k_out=None, v_out=None):

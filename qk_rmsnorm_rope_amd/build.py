@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(PKG, "libqkrope.so")
 SOURCES = ["qkrope_kernels_3d_d64.hip", "qkrope_kernels_3d_d128.hip", "qkrope_kernels_3d_d256.hip",
            "qkrope_kernels_table_interleaved_bf16.hip", "qkrope_kernels_table_halfsplit_bf16.hip",
            "qkrope_kernels_table_interleaved_f16.hip", "qkrope_kernels_table_halfsplit_f16.hip",
+           "qkrope_kernels_table_halfsplit_any_bf16.hip", "qkrope_kernels_table_halfsplit_any_f16.hip",
            "qkrope_kernels_sumsq.hip", "qkrope_api.cpp"]
 
 HIP_FLAGS = [

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -158,9 +159,13 @@ hipError_t launch(const KernelKey &k, const LaunchShape &s, const KernelArgs &a,
         default: return hipErrorInvalidValue;
         }
     }
-    if (k.act == kActF16)
-        return k.half_split ? launch_table_halfsplit_f16(k, s, a, st) : launch_table_interleaved_f16(k, s, a, st);
-    return k.half_split ? launch_table_halfsplit_bf16(k, s, a, st) : launch_table_interleaved_bf16(k, s, a, st);
+    const bool f16 = k.act == kActF16;
+    switch (k.pairing) {
+    case kPairInterleaved: return f16 ? launch_table_interleaved_f16(k, s, a, st) : launch_table_interleaved_bf16(k, s, a, st);
+    case kPairHalf: return f16 ? launch_table_halfsplit_f16(k, s, a, st) : launch_table_halfsplit_bf16(k, s, a, st);
+    case kPairHalfAny: return f16 ? launch_table_halfsplit_any_f16(k, s, a, st) : launch_table_halfsplit_any_bf16(k, s, a, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 // Device guard: make h->device current for the launch and restore the caller's device after.
@@ -227,8 +232,9 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     if (!(c.eps >= 0.0) || !std::isfinite(c.eps)) return fail(QKROPE_ERR_INVALID, "eps must be finite and >= 0");
     if (D % 8 || D > 256) return fail(QKROPE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and <= 256");
     const bool half = !c.interleaved;
-    if (half && R % 16)
-        return fail(QKROPE_ERR_UNSUPPORTED, "half-split pairing needs rotary_dim to be a multiple of 16");
+    // half-split partners are whole 16-byte chunks when R/2 is a multiple of 8; otherwise they
+    // are exchanged element by element through LDS
+    const int pairing = !half ? kPairInterleaved : (R % 16 == 0 ? kPairHalf : kPairHalfAny);
     if (T >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "num_tokens must be < 2^31");
     if (T == 0 || Hq + Hk == 0) return ok();
 
@@ -303,6 +309,15 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     a.table_sin = c.sin_table;
     a.cos_stride = c.cos_stride;
     a.sin_stride = c.sin_stride;
+    {
+        // whole-vector table reads: a lane's pairs (4 interleaved, 8 half-split) never straddle
+        // R/2, and both tables' rows are aligned for loads of min(16, pairs * size) bytes
+        const int pairs = half ? 8 : 4;
+        const int64_t vb = std::min(16, pairs * tsize);
+        a.table_vec = R > 0 && (R / 2) % pairs == 0 && aligned(c.cos_table, vb) &&
+                      aligned(c.sin_table, vb) && (c.cos_stride * tsize) % vb == 0 &&
+                      (c.sin_stride * tsize) % vb == 0;
+    }
     a.num_tokens = T;
     a.head_dim = D;
     a.rotary_dim = R;
@@ -314,10 +329,11 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     a.qk_scale = fp8 ? (float)c.out_scale : 1.0f;
     a.v_scale = 1.0f;
     shape.blocks = T;
+    shape.lds_bytes = pairing == kPairHalfAny ? shape.threads * 32 : 0;
 
     KernelKey key;
     key.head_dim_tpl = 0;
-    key.half_split = half;
+    key.pairing = pairing;
     key.norm = c.norm_mode == QKROPE_NORM_NONE ? kNormNone
              : c.norm_mode == QKROPE_NORM_PER_HEAD ? kNormPerHead : kNormAcross;
     key.src = c.table_dtype == QKROPE_DTYPE_F32 ? kSrcTableF32
@@ -474,10 +490,11 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
         a.axis[k] = (uint8_t)axis;
     }
     shape.blocks = T;
+    shape.lds_bytes = 0;
 
     KernelKey key;
     key.head_dim_tpl = D;
-    key.half_split = half;
+    key.pairing = half ? kPairHalf : kPairInterleaved;     // R/2 = D/2 is a multiple of 8
     key.norm = !c.is_qk_norm ? kNormNone : (ext ? kNormAcrossExt : kNormAcross);
     key.src = kSrc3D;
     key.act = kActBF16;
@@ -504,6 +521,34 @@ const char *qkrope_status_str(int status)
 }
 
 const char *qkrope_last_error(void) { return g_last_error.c_str(); }
+
+int qkrope_min_tokens(int64_t default_tokens, int64_t *out)
+{
+    if (!out) return fail(QKROPE_ERR_INVALID, "out is NULL");
+    if (default_tokens < 0) return fail(QKROPE_ERR_INVALID, "default_tokens must be >= 0");
+    const char *env = std::getenv("QKROPE_FUSED_MIN_TOKENS");
+    if (!env) {
+        *out = default_tokens;
+        return ok();
+    }
+    const char *p = env;
+    while (*p == ' ' || *p == '\t') ++p;
+    const char *end = p + std::strlen(p);
+    while (end > p && (end[-1] == ' ' || end[-1] == '\t' || end[-1] == '\n')) --end;
+    if (p == end) {
+        *out = default_tokens;
+        return ok();
+    }
+    int64_t v = 0;
+    for (const char *c = p; c < end; ++c) {
+        if (*c < '0' || *c > '9' || v > (INT64_MAX - 9) / 10)
+            return fail(QKROPE_ERR_INVALID,
+                        "QKROPE_FUSED_MIN_TOKENS=\"%s\" is not a non-negative integer", env);
+        v = v * 10 + (*c - '0');
+    }
+    *out = v;
+    return ok();
+}
 
 int qkrope_create(int device_ordinal, qkrope_handle *out)
 {

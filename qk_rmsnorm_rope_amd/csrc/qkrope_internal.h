@@ -16,6 +16,9 @@ enum Region { kQ = 0, kK = 1, kV = 2 };
 enum Norm { kNormNone = 0, kNormPerHead = 1, kNormAcross = 2, kNormAcrossExt = 3 };
 enum RopeSrc { kSrcTableF32 = 0, kSrcTableBF16 = 1, kSrcTableF16 = 2, kSrc3D = 3 };
 enum Act { kActBF16 = 0, kActF16 = 1 };   // 16-bit activation (and weight) format
+// Rotation pairing: interleaved (2i, 2i+1); half-split (d, d + R/2) with R/2 a multiple of 8, so
+// partners are whole 16-byte chunks; half-split with any even R, partners exchanged through LDS.
+enum Pairing { kPairInterleaved = 0, kPairHalf = 1, kPairHalfAny = 2 };
 
 // Magic pair for n / d with n < 2^31: q = (mulhi(n, m) + n) >> l.
 struct FastDiv {
@@ -37,6 +40,7 @@ struct KernelArgs {
     const void *table_sin;     // table form: row t holds sin(theta_t,i)
     int64_t cos_stride;        // token strides of the two tables, elements
     int64_t sin_stride;
+    int table_vec;             // rows aligned for whole-vector reads of a lane's pairs (uniform)
     const float *sumsq_in;     // kNormAcrossExt: [T, 2] sums of squares of Q and K rows
 
     int64_t num_tokens;        // = grid size: one workgroup per token
@@ -64,12 +68,13 @@ struct LaunchShape {
     int slots;          // slots per region (region-major) or per lane (mixed)
     bool slot_uniform;  // region-major slot layout
     int64_t blocks;     // grid size
+    int lds_bytes;      // dynamic LDS per workgroup (kPairHalfAny: threads * 32)
 };
 
 // Kernel selection keys.
 struct KernelKey {
     int head_dim_tpl;   // 64/128/256 for the 3D kernels, 0 = runtime head_dim (table form)
-    bool half_split;
+    int pairing;        // Pairing
     int norm;           // Norm
     int src;            // RopeSrc
     int act;            // Act
@@ -87,6 +92,8 @@ hipError_t launch_table_interleaved_bf16(const KernelKey &key, const LaunchShape
 hipError_t launch_table_halfsplit_bf16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
 hipError_t launch_table_interleaved_f16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
 hipError_t launch_table_halfsplit_f16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_table_halfsplit_any_bf16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
+hipError_t launch_table_halfsplit_any_f16(const KernelKey &key, const LaunchShape &shape, const KernelArgs &args, hipStream_t stream);
 
 // Per-token sums of squares of the Q and K rows of packed QKV: out[2t] = sum over the
 // token's q_elems Q values of x^2, out[2t+1] the same over its k_elems K values (fp32).

@@ -237,13 +237,16 @@ __device__ __forceinline__ float sumsq_packed(const uint4 v, float acc)
 // ---- the kernel -------------------------------------------------------------------------------
 
 // DT: head_dim as a compile-time constant (64/128/256), or 0 to read it from the arguments.
-// HALF: half-split (NeoX) pairing; otherwise interleaved. NORM: kNormNone/PerHead/Across/
+// PAIR: kPairInterleaved, kPairHalf (half-split, R/2 a multiple of 8) or kPairHalfAny
+// (half-split, any even R; partners exchanged through LDS). NORM: kNormNone/PerHead/Across/
 // AcrossExt. SRC: cos/sin from a fp32, bf16 or binary16 table, or computed (3D).
 // ACT: 16-bit activation format (bf16 or binary16). FP8: E4M3 outputs.
 // SU: region-major slots (NS per region); otherwise mixed slots (NS in all).
-template <int DT, bool HALF, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
+template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
 __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 {
+    constexpr bool HALF = PAIR != kPairInterleaved;
+    constexpr bool XCH = PAIR == kPairHalfAny;  // partners through LDS, per element
     constexpr bool IS3D = (SRC == kSrc3D);
     constexpr bool ACROSS = NORM == kNormAcross || NORM == kNormAcrossExt;
     constexpr int NREG = IS3D ? 3 : 2;          // regions: Q, K (, V)
@@ -258,6 +261,8 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     // signed pair directly (first half: y = n cos - n' sin, second half: y = n cos + n' sin).
     __shared__ f32x4 s_cs[IS3D ? kMaxPairs : 1];
     __shared__ f32x2 s_red[16];
+    // kPairHalfAny: one area of 64 lanes x 8 floats per wave (launched with threads * 32 bytes)
+    extern __shared__ float s_xch[];
 
     const int D = DT > 0 ? DT : a.head_dim;
     const int R = IS3D ? D : a.rotary_dim;
@@ -278,7 +283,12 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     bool rotated;
     int pair0, partner;
     float half_sign = 1.0f;                     // first half: y = n c - n' s; second: n c + n' s
-    if (HALF) {
+    if (XCH) {
+        // element 8u + e of a head is rotated when below R; its pair and sign are per element
+        rotated = 8 * u < R;
+        pair0 = 0;
+        partner = tid & 63;
+    } else if (HALF) {
         rotated = u < 2 * P;
         const bool first = u < P;
         pair0 = 8 * (first ? u : u - P);
@@ -368,6 +378,87 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                 const float c = __builtin_amdgcn_cosf(rev) * a.attention_factor;
                 const float sn = __builtin_amdgcn_sinf(rev) * a.attention_factor;
                 s_cs[tid] = f32x4{c, -sn, c, sn};
+            }
+        } else if (XCH) {
+            // per element g = 8u + e: angle index g (first half, sign -) or g - R/2 (second
+            // half, sign +); elements at or beyond R keep (1, 0). R >= 2 here, so the loads are
+            // issued unconditionally (index 0 where the element is not rotated).
+            const int half = R / 2;
+#pragma unroll
+            for (int e = 0; e < NPAIR; ++e) {
+                const int g = 8 * u + e;
+                const bool on = unit_ok && g < R;
+                const int i = on ? (g < half ? g : g - half) : 0;
+                float c, sn;
+                {
+                    if (SRC == kSrcTableF32) {
+                        c = (static_cast<const float *>(a.table_cos) + t * a.cos_stride)[i];
+                        sn = (static_cast<const float *>(a.table_sin) + t * a.sin_stride)[i];
+                    } else {
+                        const uint16_t cb = (static_cast<const uint16_t *>(a.table_cos) + t * a.cos_stride)[i];
+                        const uint16_t sb = (static_cast<const uint16_t *>(a.table_sin) + t * a.sin_stride)[i];
+                        if (SRC == kSrcTableBF16) {
+                            c = __uint_as_float((uint32_t)cb << 16);
+                            sn = __uint_as_float((uint32_t)sb << 16);
+                        } else {
+                            c = (float)__builtin_bit_cast(_Float16, cb);
+                            sn = (float)__builtin_bit_cast(_Float16, sb);
+                        }
+                    }
+                }
+                cs_c[e] = on ? c : 1.0f;
+                cs_s[e] = on ? (g < half ? -sn : sn) : 0.0f;
+            }
+        } else if (!XCH && a.table_vec) {
+            // A lane's NPAIR pairs lie all below R/2 or all at/above it (NPAIR divides R/2), and
+            // the rows are aligned: one or two vector loads per table, issued unconditionally
+            // (a lane without rotated pairs reads pair 0 and discards it).
+            const bool on = unit_ok && rotated;
+            const int64_t i0 = on ? pair0 : 0;
+            if (SRC == kSrcTableF32) {
+                const f32x4 *cp = reinterpret_cast<const f32x4 *>(
+                    static_cast<const float *>(a.table_cos) + t * a.cos_stride + i0);
+                const f32x4 *sp = reinterpret_cast<const f32x4 *>(
+                    static_cast<const float *>(a.table_sin) + t * a.sin_stride + i0);
+#pragma unroll
+                for (int v = 0; v < NPAIR / 4; ++v) {
+                    const f32x4 c = cp[v], sn = sp[v];
+                    cs_c[4 * v + 0] = c.x; cs_c[4 * v + 1] = c.y;
+                    cs_c[4 * v + 2] = c.z; cs_c[4 * v + 3] = c.w;
+                    cs_s[4 * v + 0] = sn.x; cs_s[4 * v + 1] = sn.y;
+                    cs_s[4 * v + 2] = sn.z; cs_s[4 * v + 3] = sn.w;
+                }
+            } else {
+                const uint16_t *cp = static_cast<const uint16_t *>(a.table_cos) + t * a.cos_stride + i0;
+                const uint16_t *sp = static_cast<const uint16_t *>(a.table_sin) + t * a.sin_stride + i0;
+                uint32_t cw[NPAIR / 2], sw[NPAIR / 2];
+                if (NPAIR == 8) {
+                    const u32x4 c = *reinterpret_cast<const u32x4 *>(cp);
+                    const u32x4 sn = *reinterpret_cast<const u32x4 *>(sp);
+                    cw[0] = c.x; cw[1] = c.y; cw[NPAIR / 2 - 2] = c.z; cw[NPAIR / 2 - 1] = c.w;
+                    sw[0] = sn.x; sw[1] = sn.y; sw[NPAIR / 2 - 2] = sn.z; sw[NPAIR / 2 - 1] = sn.w;
+                } else {
+                    const u32x2 c = *reinterpret_cast<const u32x2 *>(cp);
+                    const u32x2 sn = *reinterpret_cast<const u32x2 *>(sp);
+                    cw[0] = c.x; cw[1] = c.y;
+                    sw[0] = sn.x; sw[1] = sn.y;
+                }
+#pragma unroll
+                for (int v = 0; v < NPAIR / 2; ++v) {
+                    if (SRC == kSrcTableBF16) {
+                        cs_c[2 * v] = bf16_lo(cw[v]); cs_c[2 * v + 1] = bf16_hi(cw[v]);
+                        cs_s[2 * v] = bf16_lo(sw[v]); cs_s[2 * v + 1] = bf16_hi(sw[v]);
+                    } else {
+                        const f32x2 c = f16x2_to_f32(cw[v]), sn = f16x2_to_f32(sw[v]);
+                        cs_c[2 * v] = c.x; cs_c[2 * v + 1] = c.y;
+                        cs_s[2 * v] = sn.x; cs_s[2 * v + 1] = sn.y;
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < NPAIR; ++e) {
+                cs_c[e] = on ? cs_c[e] : 1.0f;
+                cs_s[e] = on ? (HALF ? cs_s[e] * half_sign : cs_s[e]) : 0.0f;
             }
         } else if (unit_ok && rotated) {
             const int half = R / 2;
@@ -473,7 +564,32 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                 for (int i = 0; i < 8; ++i) n[i] *= scale;
             }
             float y[8];
-            if (HALF) {
+            if (XCH) {
+                // every lane stages its normalised chunk in its wave's LDS area, where a head's
+                // D values sit contiguously, then reads element g +- R/2 of its own head. Only
+                // lanes of one wave touch an area, and LDS executes a wave's accesses in order,
+                // so keeping the compiler from moving the accesses (signal fence, wave barrier)
+                // suffices.
+                float *wx = s_xch + (tid >> 6) * 512;
+                const int lane = tid & 63;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wx[lane * 8 + i] = n[i];
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_wave_barrier();
+                const int hb = (lane & ~(L - 1)) * 8;
+                const int half = R / 2;
+                float np[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int g = 8 * u + e;
+                    const int src = g < R ? (g < half ? g + half : g - half) : g;
+                    np[e] = wx[hb + src];
+                }
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = n[e] * cs_c[e] + np[e] * cs_s[e];
+            } else if (HALF) {
                 // partner chunk's normalised values (all lanes take part in the permute)
                 float np[8];
 #pragma unroll
@@ -562,59 +678,59 @@ __global__ void __launch_bounds__(1024) qkrope_sumsq_kernel(const SumsqArgs a)
 
 // ---- launch helpers ---------------------------------------------------------------------------
 
-template <int DT, bool HALF, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
+template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
 hipError_t go(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL((qkrope_kernel<DT, HALF, NORM, SRC, ACT, FP8, NS, SU>), dim3((unsigned)s.blocks),
-                       dim3(s.threads), 0, st, a);
+    hipLaunchKernelGGL((qkrope_kernel<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU>), dim3((unsigned)s.blocks),
+                       dim3(s.threads), s.lds_bytes, st, a);
     return hipGetLastError();
 }
 
-template <int DT, bool HALF, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
+template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
 hipError_t go_if(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if constexpr (slots_compiled(SRC == kSrc3D ? 3 : 2, SU, NS))
-        return go<DT, HALF, NORM, SRC, ACT, FP8, NS, SU>(s, a, st);
+        return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU>(s, a, st);
     else
         return hipErrorInvalidValue;
 }
 
-template <int DT, bool HALF, int NORM, int SRC, int ACT, bool FP8>
+template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8>
 hipError_t by_slots(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if (k.slot_uniform) {
         switch (k.slots) {
-        case 1: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 1, true>(s, a, st);
-        case 2: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 2, true>(s, a, st);
-        case 3: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 3, true>(s, a, st);
-        case 4: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 4, true>(s, a, st);
+        case 1: return go_if<DT, PAIR, NORM, SRC, ACT, FP8, 1, true>(s, a, st);
+        case 2: return go_if<DT, PAIR, NORM, SRC, ACT, FP8, 2, true>(s, a, st);
+        case 3: return go_if<DT, PAIR, NORM, SRC, ACT, FP8, 3, true>(s, a, st);
+        case 4: return go_if<DT, PAIR, NORM, SRC, ACT, FP8, 4, true>(s, a, st);
         default: return hipErrorInvalidValue;
         }
     }
     switch (k.slots) {
-    case 1: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 1, false>(s, a, st);
-    case 2: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 2, false>(s, a, st);
-    case 4: return go_if<DT, HALF, NORM, SRC, ACT, FP8, 4, false>(s, a, st);
+    case 1: return go_if<DT, PAIR, NORM, SRC, ACT, FP8, 1, false>(s, a, st);
+    case 2: return go_if<DT, PAIR, NORM, SRC, ACT, FP8, 2, false>(s, a, st);
+    case 4: return go_if<DT, PAIR, NORM, SRC, ACT, FP8, 4, false>(s, a, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int DT, bool HALF, int NORM, int SRC, int ACT>
+template <int DT, int PAIR, int NORM, int SRC, int ACT>
 hipError_t by_fp8(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    return k.fp8 ? by_slots<DT, HALF, NORM, SRC, ACT, true>(k, s, a, st)
-                 : by_slots<DT, HALF, NORM, SRC, ACT, false>(k, s, a, st);
+    return k.fp8 ? by_slots<DT, PAIR, NORM, SRC, ACT, true>(k, s, a, st)
+                 : by_slots<DT, PAIR, NORM, SRC, ACT, false>(k, s, a, st);
 }
 
 // 3D form for one compile-time head_dim: pairing x norm (none / across heads / across heads
 // from given sums) x output format. Activations are bf16.
-template <int DT, bool HALF>
+template <int DT, int PAIR>
 hipError_t launch_3d_pairing(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     switch (k.norm) {
-    case kNormNone: return by_fp8<DT, HALF, kNormNone, kSrc3D, kActBF16>(k, s, a, st);
-    case kNormAcross: return by_fp8<DT, HALF, kNormAcross, kSrc3D, kActBF16>(k, s, a, st);
-    case kNormAcrossExt: return by_fp8<DT, HALF, kNormAcrossExt, kSrc3D, kActBF16>(k, s, a, st);
+    case kNormNone: return by_fp8<DT, PAIR, kNormNone, kSrc3D, kActBF16>(k, s, a, st);
+    case kNormAcross: return by_fp8<DT, PAIR, kNormAcross, kSrc3D, kActBF16>(k, s, a, st);
+    case kNormAcrossExt: return by_fp8<DT, PAIR, kNormAcrossExt, kSrc3D, kActBF16>(k, s, a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -623,29 +739,30 @@ template <int DT>
 hipError_t launch_3d(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if (k.src != kSrc3D || k.head_dim_tpl != DT || k.act != kActBF16) return hipErrorInvalidValue;
-    return k.half_split ? launch_3d_pairing<DT, true>(k, s, a, st)
-                        : launch_3d_pairing<DT, false>(k, s, a, st);
+    if (k.pairing == kPairHalf) return launch_3d_pairing<DT, kPairHalf>(k, s, a, st);
+    if (k.pairing == kPairInterleaved) return launch_3d_pairing<DT, kPairInterleaved>(k, s, a, st);
+    return hipErrorInvalidValue;
 }
 
-template <bool HALF, int ACT, int NORM>
+template <int PAIR, int ACT, int NORM>
 hipError_t launch_table_src(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     constexpr int SRC16 = ACT == kActBF16 ? kSrcTableBF16 : kSrcTableF16;
-    if (k.src == kSrcTableF32) return by_fp8<0, HALF, NORM, kSrcTableF32, ACT>(k, s, a, st);
-    if (k.src == SRC16) return by_fp8<0, HALF, NORM, SRC16, ACT>(k, s, a, st);
+    if (k.src == kSrcTableF32) return by_fp8<0, PAIR, NORM, kSrcTableF32, ACT>(k, s, a, st);
+    if (k.src == SRC16) return by_fp8<0, PAIR, NORM, SRC16, ACT>(k, s, a, st);
     return hipErrorInvalidValue;
 }
 
 // Table form (runtime head_dim) for one pairing and activation format: norm mode x table
 // dtype (fp32 or the activation format) x output format (activation format or E4M3).
-template <bool HALF, int ACT>
+template <int PAIR, int ACT>
 hipError_t launch_table(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    if (k.head_dim_tpl != 0 || k.act != ACT || k.half_split != HALF) return hipErrorInvalidValue;
+    if (k.head_dim_tpl != 0 || k.act != ACT || k.pairing != PAIR) return hipErrorInvalidValue;
     switch (k.norm) {
-    case kNormNone: return launch_table_src<HALF, ACT, kNormNone>(k, s, a, st);
-    case kNormPerHead: return launch_table_src<HALF, ACT, kNormPerHead>(k, s, a, st);
-    case kNormAcross: return launch_table_src<HALF, ACT, kNormAcross>(k, s, a, st);
+    case kNormNone: return launch_table_src<PAIR, ACT, kNormNone>(k, s, a, st);
+    case kNormPerHead: return launch_table_src<PAIR, ACT, kNormPerHead>(k, s, a, st);
+    case kNormAcross: return launch_table_src<PAIR, ACT, kNormAcross>(k, s, a, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -5,7 +5,7 @@ namespace qkrope {
 
 hipError_t launch_table_halfsplit_bf16(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    return dev::launch_table<true, kActBF16>(k, s, a, st);
+    return dev::launch_table<kPairHalf, kActBF16>(k, s, a, st);
 }
 
 }  // namespace qkrope

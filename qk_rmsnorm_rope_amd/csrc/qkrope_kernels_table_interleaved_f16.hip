@@ -5,7 +5,7 @@ namespace qkrope {
 
 hipError_t launch_table_interleaved_f16(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    return dev::launch_table<false, kActF16>(k, s, a, st);
+    return dev::launch_table<kPairInterleaved, kActF16>(k, s, a, st);
 }
 
 }  // namespace qkrope

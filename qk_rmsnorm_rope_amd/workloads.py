@@ -91,6 +91,10 @@ class Rope3DWorkload:
     output_quant_scale: float = 1.0
     v_quant_scale: float = 1.0
     sigma: float = 1.0
+    # > 1: the problem is one rank's share of a head-sharded run over this many ranks (the head
+    # counts above are per rank); the across-heads norm spans head_shards times the rank's Q (K)
+    # elements, taking the per-token sums of squares reduced over the ranks.
+    head_shards: int = 1
 
     @property
     def seq_len(self) -> int:
@@ -143,9 +147,30 @@ ROPE3D_YARN_S122880 = Rope3DWorkload(
     factor=4.0, low=1.0, high=32.0, attention_factor=1.0 + 0.1 * float(np.log(4.0)),
     is_qk_norm=False)
 
+# --- further measured workloads (beyond the five above) -----------------------------------------
+
+# The interleaved table form at a token count whose working set (0.8 GB) exceeds the 256 MB
+# memory-side cache, in bf16, in float16, and with E4M3 outputs.
+TABLE_INTERLEAVED_T32768 = TABLE_INTERLEAVED_T4096.with_(
+    name="table_interleaved_t32768_h24_d128_bf16table", num_tokens=32768, seed=SEED_BASE + 60)
+TABLE_INTERLEAVED_T32768_F16 = TABLE_INTERLEAVED_T32768.with_(
+    name="table_interleaved_t32768_h24_d128_f16", act_dtype="f16", table_dtype="f16",
+    seed=SEED_BASE + 70)
+TABLE_INTERLEAVED_T32768_E4M3 = TABLE_INTERLEAVED_T32768.with_(
+    name="table_interleaved_t32768_h24_d128_e4m3out", out_dtype="e4m3", out_scale=0.5,
+    table_dtype="f32", seed=SEED_BASE + 80)
+
+# One rank of the 15360-token, 32-head problem sharded over 4 ranks by heads (8 Q, K and V
+# heads per rank; across-heads norm over all 32).
+ROPE3D_ACROSS_S15360_TP4 = ROPE3D_ACROSS_S15360.with_(
+    name="rope3d_across_interleaved_s15360_h32_d128_tp4rank", num_heads_q=8, num_heads_k=8,
+    num_heads_v=8, head_shards=4, seed=SEED_BASE + 90)
+
 WORKLOADS = {w.name: w for w in (TABLE_HALFSPLIT_T256, TABLE_INTERLEAVED_T4096,
                                  ROPE3D_ACROSS_S15360, ROPE3D_NEOX_FP8_S18480,
-                                 ROPE3D_YARN_S122880)}
+                                 ROPE3D_YARN_S122880, TABLE_INTERLEAVED_T32768,
+                                 TABLE_INTERLEAVED_T32768_F16, TABLE_INTERLEAVED_T32768_E4M3,
+                                 ROPE3D_ACROSS_S15360_TP4)}
 
 
 # --- drawing -----------------------------------------------------------------------------------

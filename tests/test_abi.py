@@ -55,3 +55,48 @@ def test_library_links_torchs_hip_runtime(lib):
     import qk_rmsnorm_rope_amd as qr
     runtimes = qr._hip_runtimes_loaded()
     assert len(runtimes) == 1 and "torch" in next(iter(runtimes)), runtimes
+
+
+def test_new_entry_points_reject_null_handle(lib):
+    rc = lib.qkrope_run_table_ex(None, None, None, None, None, None, None, 0, 0, 0, 1.0, 1e-6, 0,
+                                 1, 1, 64, 64, 1, 1, 64, 64, 32, 32, None, None, 64, 64, None)
+    assert rc == 1 and b"handle" in lib.qkrope_last_error()
+    assert lib.qkrope_sumsq_3d(None, None, 4, 1, 1, 1, 64, None, None) == 1
+    rc = lib.qkrope_run_3d_sharded(None, None, None, None, 0, 0, None, 0, 0, 1, 1, 1, 0, 0, 64,
+                                   1, 1, 1, 64, 1e-6, 1e4, 1, 1.0, 0.0, 0.0, 1.0, 1, 0, 1.0, 1.0,
+                                   None, None, None, None)
+    assert rc == 1 and b"handle" in lib.qkrope_last_error()
+
+
+# --- the fused-vs-eager threshold (vLLM-Omni fused_qk_norm_rope_min_tokens rules) -------------
+
+@pytest.mark.parametrize("env,default,expect", [
+    (None, 2048, 2048), ("", 2048, 2048), ("   ", 512, 512), ("0", 2048, 0),
+    ("4096", 2048, 4096), (" 17 ", 5, 17), ("0007", 1, 7)])
+def test_min_tokens_resolution(monkeypatch, env, default, expect):
+    import qk_rmsnorm_rope_amd as qr
+    if env is None:
+        monkeypatch.delenv("QKROPE_FUSED_MIN_TOKENS", raising=False)
+    else:
+        monkeypatch.setenv("QKROPE_FUSED_MIN_TOKENS", env)
+    assert qr.fused_qk_norm_rope_min_tokens(default) == expect
+
+
+@pytest.mark.parametrize("env", ["-1", "abc", "1.5", "12x", "+3", "1e3", "99999999999999999999"])
+def test_min_tokens_rejects_non_integers(monkeypatch, env):
+    import qk_rmsnorm_rope_amd as qr
+    monkeypatch.setenv("QKROPE_FUSED_MIN_TOKENS", env)
+    with pytest.raises(ValueError, match="QKROPE_FUSED_MIN_TOKENS"):
+        qr.qkrope_min_tokens(2048)
+
+
+def test_min_tokens_resolved_at_call_time(monkeypatch):
+    import qk_rmsnorm_rope_amd as qr
+    monkeypatch.setenv("QKROPE_FUSED_MIN_TOKENS", "100")
+    assert qr.qkrope_min_tokens(2048) == 100
+    monkeypatch.setenv("QKROPE_FUSED_MIN_TOKENS", "0")
+    assert qr.qkrope_min_tokens(2048) == 0
+    monkeypatch.delenv("QKROPE_FUSED_MIN_TOKENS")
+    assert qr.qkrope_min_tokens(2048) == 2048
+    with pytest.raises(ValueError):
+        qr.qkrope_min_tokens(-1)

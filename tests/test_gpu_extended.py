@@ -63,6 +63,7 @@ F16_CASES = [
     (256, 4, 4, 128, 96, False, "per_head", "f32"),
     (97, 8, 2, 64, 32, False, "across_heads", "f16"),
     (64, 3, 5, 256, 200, True, "none", "f32"),
+    (129, 6, 6, 128, 72, False, "per_head", "f16"),     # half-split, rotary_dim % 16 != 0
 ]
 
 
@@ -125,11 +126,13 @@ def test_split_cos_sin_tables(inter, R, tdt):
 
 # --- E4M3 outputs for the table form -----------------------------------------------------------
 
-@pytest.mark.parametrize("act,inter,scale,sigma", [("bf16", True, 0.5, 1.0), ("f16", False, 2.0, 1.0),
-                                                   ("bf16", False, 300.0, 4.0)])
-def test_table_e4m3_outputs(act, inter, scale, sigma):
-    w = table_workload(301, 16, 8, 128, 128 if inter else 96, inter, "per_head", act, "f32",
-                       seed=4300 + int(scale), sigma=sigma)
+@pytest.mark.parametrize("act,inter,scale,sigma,R", [("bf16", True, 0.5, 1.0, 128),
+                                                     ("f16", False, 2.0, 1.0, 96),
+                                                     ("bf16", False, 300.0, 4.0, 96),
+                                                     ("bf16", False, 1.0, 1.0, 52)])
+def test_table_e4m3_outputs(act, inter, scale, sigma, R):
+    w = table_workload(301, 16, 8, 128, R, inter, "per_head", act, "f32",
+                       seed=4300 + int(scale) + R, sigma=sigma)
     inp = wl.table_inputs(w)
     g = {k: _gpu(v) for k, v in inp.items()}
     R = w.rotary_dim

@@ -166,6 +166,13 @@ SWEEP_TABLE = [
     (9, 6, 2, 128, 128, False, "none", "bf16"),
     (1, 1, 1, 24, 2, True, "per_head", "bf16"),
     (40, 48, 8, 64, 32, True, "per_head", "f32"),
+    # half-split with rotary_dim % 16 != 0: partners straddle 16-byte chunks
+    (37, 3, 2, 64, 40, False, "per_head", "f32"),
+    (50, 4, 4, 128, 100, False, "across_heads", "bf16"),
+    (19, 2, 1, 32, 2, False, "none", "f32"),
+    (23, 8, 8, 256, 250, False, "per_head", "bf16"),
+    (11, 1, 3, 24, 8, False, "per_head", "f32"),
+    (300, 24, 24, 128, 120, False, "per_head", "f32"),
 ]
 
 
@@ -312,8 +319,8 @@ def test_contract_violations_raise_value_error():
                          num_heads_k=32, num_heads_v=32, head_dim=128,
                          q_out=flat.view(-1)[:q_alias.numel()].view(q_alias.shape),
                          k_out=torch.empty_like(q_alias), v_out=torch.empty_like(q_alias))
-    # half-split table pairing needs rotary_dim % 16 == 0 in this library: unsupported
-    t = wl.TableWorkload(name="u", num_tokens=4, num_heads_q=1, num_heads_k=1, head_dim=64,
+    # table-form head_dim above 256 is outside this library's kernels: unsupported
+    t = wl.TableWorkload(name="u", num_tokens=4, num_heads_q=1, num_heads_k=1, head_dim=264,
                          rotary_dim=40, interleaved=False, table_dtype="f32", seed=3)
     ti = {n: _gpu(v) for n, v in wl.table_inputs(t).items()}
     with pytest.raises(ValueError, match="unsupported"):
