@@ -110,10 +110,25 @@ __device__ __forceinline__ float sat_e4m3(float y)
 
 // Each conversion writes one 16-bit half of its destination and keeps the other; the first of
 // each pair starts from a register that is live anyway (its bits are overwritten by the second).
-__device__ __forceinline__ uint2 pack8_e4m3(const float y[8])
+// The conversion itself maps NaN to the NaN code, so saturation is only needed where some
+// |y| > 448; that is rare, so lanes test the chunk's largest magnitude (v_max3 ignores NaN)
+// and only those above 448 take the saturating path.
+__device__ __forceinline__ uint2 pack8_e4m3(const float yin[8])
 {
-    const float a0 = sat_e4m3(y[0]), a1 = sat_e4m3(y[1]), a2 = sat_e4m3(y[2]), a3 = sat_e4m3(y[3]);
-    const float b0 = sat_e4m3(y[4]), b1 = sat_e4m3(y[5]), b2 = sat_e4m3(y[6]), b3 = sat_e4m3(y[7]);
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = yin[i];
+    const float m = __builtin_fmaxf(
+        __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1])),
+                        __builtin_fmaxf(__builtin_fabsf(y[2]), __builtin_fabsf(y[3]))),
+        __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[4]), __builtin_fabsf(y[5])),
+                        __builtin_fmaxf(__builtin_fabsf(y[6]), __builtin_fabsf(y[7]))));
+    if (m > 448.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = sat_e4m3(y[i]);
+    }
+    const float a0 = y[0], a1 = y[1], a2 = y[2], a3 = y[3];
+    const float b0 = y[4], b1 = y[5], b2 = y[6], b3 = y[7];
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, __float_as_int(a2), false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, lo, true);
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(b0, b1, __float_as_int(b2), false);
