@@ -95,7 +95,11 @@ int next_pow2(int v)
 // 122880 x 3x16 x 256, and 36960 x 3x20 x 64 at 83% busy lanes, where the best mixed layout was
 // 10% slower). Otherwise the layout that leaves the fewest lanes idle wins, preferring
 // workgroups near 128 lanes.
-bool choose_shape(const int64_t *n, int nreg, LaunchShape *s)
+// A token whose largest region needs a multiple of 32 but not of 64 lanes (one slot per
+// region) leaves half a wave idle; two such tokens share a workgroup instead, filling whole
+// waves (36960 x 3x20 x 64: 160 lanes per token, 83% -> 100% of lanes busy).
+// `min_lanes`: lanes a token needs besides its chunks (3D: one per angle pair, head_dim / 2).
+bool choose_shape(const int64_t *n, int nreg, int min_lanes, LaunchShape *s)
 {
     int64_t total = 0, maxn = 0;
     for (int r = 0; r < nreg; ++r) {
@@ -106,13 +110,23 @@ bool choose_shape(const int64_t *n, int nreg, LaunchShape *s)
         const int64_t ns = (maxn + 1023) / 1024;
         const int64_t threads = ((maxn + ns - 1) / ns + 63) / 64 * 64;
         const double util = (double)total / ((double)nreg * ns * threads);
-        if (util >= 0.75 && slots_compiled(nreg, true, (int)std::min<int64_t>(ns, 1 << 20))) {
-            *s = LaunchShape{(int)threads, (int)ns, true, 0};
+        if (ns == 1) {
+            const int64_t t32 = (maxn + 31) / 32 * 32;
+            const double util2 = (double)total / ((double)nreg * t32);
+            if (t32 % 64 != 0 && 2 * t32 <= 1024 && t32 >= min_lanes && util2 >= 0.75 &&
+                util2 > util + 0.05) {
+                *s = LaunchShape{(int)(2 * t32), 1, true, 0, 0, 2};
+                return true;
+            }
+        }
+        if (util >= 0.75 && threads >= min_lanes &&
+            slots_compiled(nreg, true, (int)std::min<int64_t>(ns, 1 << 20))) {
+            *s = LaunchShape{(int)threads, (int)ns, true, 0, 0, 1};
             return true;
         }
     }
     double best = -1.0;
-    for (int threads = 64; threads <= 1024; threads += 64) {
+    for (int threads = std::max(64, (min_lanes + 63) / 64 * 64); threads <= 1024; threads += 64) {
         const double dist = std::fabs(std::log2(threads / 128.0));
         const int64_t ns_rm = (maxn + threads - 1) / threads;
         if (slots_compiled(nreg, true, (int)std::min<int64_t>(ns_rm, 1 << 20))) {
@@ -120,7 +134,7 @@ bool choose_shape(const int64_t *n, int nreg, LaunchShape *s)
             const double score = util - 0.01 * dist;
             if (score > best) {
                 best = score;
-                *s = LaunchShape{threads, (int)ns_rm, true, 0};
+                *s = LaunchShape{threads, (int)ns_rm, true, 0, 0, 1};
             }
         }
         const int64_t need = (total + threads - 1) / threads;
@@ -130,7 +144,7 @@ bool choose_shape(const int64_t *n, int nreg, LaunchShape *s)
             const double score = util - 0.01 * dist + 0.001;
             if (score > best) {
                 best = score;
-                *s = LaunchShape{threads, ns, false, 0};
+                *s = LaunchShape{threads, ns, false, 0, 0, 1};
             }
             break;
         }
@@ -287,7 +301,7 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     const int L = next_pow2(D / 8);           // lanes per head: one 16-byte chunk each
     const int64_t n_units[2] = {(int64_t)Hq * L, (int64_t)Hk * L};
     LaunchShape shape;
-    if (!choose_shape(n_units, 2, &shape))
+    if (!choose_shape(n_units, 2, 1, &shape))
         return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
 
     KernelArgs a;
@@ -328,7 +342,7 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     a.inv_count[1] = (float)(1.0 / (double)(across ? (int64_t)Hk * D : D));
     a.qk_scale = fp8 ? (float)c.out_scale : 1.0f;
     a.v_scale = 1.0f;
-    shape.blocks = T;
+    shape.blocks = (T + shape.tpw - 1) / shape.tpw;
     shape.lds_bytes = pairing == kPairHalfAny ? shape.threads * 32 : 0;
 
     KernelKey key;
@@ -430,7 +444,7 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
     const int units = D / 8;                   // 16-byte chunks per head: 8, 16 or 32
     const int64_t n_units[3] = {(int64_t)Hq * units, (int64_t)Hk * units, (int64_t)Hv * units};
     LaunchShape shape;
-    if (!choose_shape(n_units, 3, &shape))
+    if (!choose_shape(n_units, 3, D / 2, &shape))
         return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
 
     KernelArgs a;
@@ -489,7 +503,7 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
         a.omega_rev[k] = (float)(omega / two_pi);
         a.axis[k] = (uint8_t)axis;
     }
-    shape.blocks = T;
+    shape.blocks = (T + shape.tpw - 1) / shape.tpw;
     shape.lds_bytes = 0;
 
     KernelKey key;

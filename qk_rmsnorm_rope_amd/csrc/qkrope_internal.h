@@ -43,7 +43,7 @@ struct KernelArgs {
     int table_vec;             // rows aligned for whole-vector reads of a lane's pairs (uniform)
     const float *sumsq_in;     // kNormAcrossExt: [T, 2] sums of squares of Q and K rows
 
-    int64_t num_tokens;        // = grid size: one workgroup per token
+    int64_t num_tokens;        // tokens; the grid has one workgroup per token (per 2 with TPW 2)
     int head_dim;              // D
     int rotary_dim;            // R (== D for the 3D form)
     int lanes_per_head;        // L: power of two >= head_dim / 8 (16-byte chunks per head)
@@ -69,6 +69,7 @@ struct LaunchShape {
     bool slot_uniform;  // region-major slot layout
     int64_t blocks;     // grid size
     int lds_bytes;      // dynamic LDS per workgroup (kPairHalfAny: threads * 32)
+    int tpw;            // tokens per workgroup: 1, or 2 (region-major, one slot per region)
 };
 
 // Kernel selection keys.

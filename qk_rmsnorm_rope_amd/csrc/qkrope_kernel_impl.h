@@ -257,9 +257,12 @@ __device__ __forceinline__ float sumsq_packed(const uint4 v, float acc)
 // AcrossExt. SRC: cos/sin from a fp32, bf16 or binary16 table, or computed (3D).
 // ACT: 16-bit activation format (bf16 or binary16). FP8: E4M3 outputs.
 // SU: region-major slots (NS per region); otherwise mixed slots (NS in all).
-template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
+// TPW: tokens per workgroup, 1, or 2 (region-major, one slot per region) when a token needs a
+// multiple of 32 but not of 64 lanes, so that two tokens fill whole waves.
+template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU, int TPW>
 __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 {
+    static_assert(TPW == 1 || (TPW == 2 && SU && NS == 1), "two tokens per workgroup: region-major, one slot");
     constexpr bool HALF = PAIR != kPairInterleaved;
     constexpr bool XCH = PAIR == kPairHalfAny;  // partners through LDS, per element
     constexpr bool IS3D = (SRC == kSrc3D);
@@ -274,8 +277,8 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 
     // 3D angles of the token: per pair (cos, -sin, cos, sin), so a half-split lane reads its
     // signed pair directly (first half: y = n cos - n' sin, second half: y = n cos + n' sin).
-    __shared__ f32x4 s_cs[IS3D ? kMaxPairs : 1];
-    __shared__ f32x2 s_red[16];
+    __shared__ f32x4 s_cs[IS3D ? TPW * kMaxPairs : 1];
+    __shared__ f32x2 s_red[32];
     // kPairHalfAny: one area of 64 lanes x 8 floats per wave (launched with threads * 32 bytes)
     extern __shared__ float s_xch[];
 
@@ -286,6 +289,12 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     const int lgL = __builtin_ctz(L);
     const int tid = threadIdx.x;
     const int nth = blockDim.x;
+    // Token of this lane: with two tokens per workgroup, lanes [0, LT) take the first and
+    // [LT, 2 LT) the second; LT is a multiple of 32 and of L, so neither a head nor a 32-lane
+    // group straddles the two.
+    const int LT = nth / TPW;
+    const int ts = (TPW == 2 && tid >= LT) ? 1 : 0;
+    const int tl = tid - ts * LT;               // lane index within its token
     const int u = tid & (L - 1);                // this lane's chunk inside every head it covers
     const bool unit_ok = u < units;
     const uint32_t off0 = 8 * u;                // element offset of the chunk inside a head
@@ -324,7 +333,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     for (int j = 0; j < NSLOT; ++j) {
         if (SU) {
             const int r = j / NS;                       // compile-time after unrolling
-            const int hh = (tid + (j % NS) * nth) >> lgL;
+            const int hh = (tl + (j % NS) * LT) >> lgL;
             reg[j] = r;
             ok[j] = unit_ok && hh < sel3(r, Hq, Hk, Hv);
             hoff[j] = (uint32_t)(hh * D);
@@ -348,12 +357,17 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     // 3D: this lane's pair (tid < D/2) frequency in revolutions and its position axis.
     float omega_rev = 0.0f;
     int axis = 0;
-    if (IS3D && tid < D / 2) {
-        omega_rev = a.omega_rev[tid];
-        axis = a.axis[tid];
+    if (IS3D && tl < D / 2) {
+        omega_rev = a.omega_rev[tl];
+        axis = a.axis[tl];
     }
 
-    const int64_t t = blockIdx.x;              // one token per workgroup
+    // The workgroup's first token, and this lane's: a missing second token (odd token count)
+    // re-reads the first token's row and stores nothing.
+    const int64_t t0 = (int64_t)blockIdx.x * TPW;
+    const bool tok_ok = TPW == 1 || t0 + ts < a.num_tokens;
+    const int ts_eff = tok_ok ? ts : 0;
+    const int64_t t = t0 + ts_eff;
     {
         // -- loads: every chunk of every slot, and the across-heads weights. Issued
         // unconditionally from one basic block so all are in flight together; an idle slot
@@ -361,17 +375,20 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         uint4 x[NSLOT], wa[NSLOT];
         (void)wa;
         {
-            const uint16_t *in_q = a.in[kQ] + t * a.in_stride[kQ];
-            const uint16_t *in_k = a.in[kK] + t * a.in_stride[kK];
-            const uint16_t *in_v = NREG == 3 ? a.in[kV] + t * a.in_stride[kV] : in_k;
+            // rows of the workgroup's first token (uniform); a second token's row is one token
+            // stride further, added to the lane's 32-bit byte offset
+            const uint16_t *in_q = a.in[kQ] + t0 * a.in_stride[kQ];
+            const uint16_t *in_k = a.in[kK] + t0 * a.in_stride[kK];
+            const uint16_t *in_v = NREG == 3 ? a.in[kV] + t0 * a.in_stride[kV] : in_k;
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 const int r = reg[j] < 3 ? reg[j] : 0;
-                const uint32_t o = ok[j] ? 2 * (hoff[j] + off0) : 0u;
-                x[j] = ld16_stream<true>(sel3(r, in_q, in_k, in_v), o);
+                const uint32_t oh = ok[j] ? 2 * (hoff[j] + off0) : 0u;
+                const uint32_t tok = TPW == 2 ? (uint32_t)ts_eff * (uint32_t)(2 * a.in_stride[r]) : 0u;
+                x[j] = ld16_stream<true>(sel3(r, in_q, in_k, in_v), oh + tok);
                 if (ACROSS && (SU ? r < 2 : true)) {
                     const uint16_t *w = r == 1 ? a.weight[1] : a.weight[0];
-                    wa[j] = ld16(w, (ok[j] && r < 2) ? o : 0u);
+                    wa[j] = ld16(w, (ok[j] && r < 2) ? oh : 0u);
                 }
             }
         }
@@ -379,20 +396,34 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         // -- cos/sin: the table row, or the 3D angle of pair `tid` into LDS
         float cs_c[NPAIR], cs_s[NPAIR];
         if (IS3D) {
-            // grid position of the token (uniform across the workgroup; t < 2^31)
-            const uint32_t tt = (uint32_t)t + a.token_offset;
-            const uint32_t s = tt - fast_div(tt, a.div_seq.m, a.div_seq.l) * a.seq_len;
-            const uint32_t pf = fast_div(s, a.div_hw.m, a.div_hw.l);
-            const uint32_t rem = s - pf * a.hw;
-            const uint32_t ph = fast_div(rem, a.div_w.m, a.div_w.l);
-            const uint32_t pw = rem - ph * a.ppw;
-            if (tid < D / 2) {
+            // grid positions of the workgroup's tokens (uniform; t < 2^31), this lane's selected
+            uint32_t pf, ph, pw;
+            {
+                const uint32_t tt = (uint32_t)t0 + a.token_offset;
+                const uint32_t s = tt - fast_div(tt, a.div_seq.m, a.div_seq.l) * a.seq_len;
+                pf = fast_div(s, a.div_hw.m, a.div_hw.l);
+                const uint32_t rem = s - pf * a.hw;
+                ph = fast_div(rem, a.div_w.m, a.div_w.l);
+                pw = rem - ph * a.ppw;
+            }
+            if (TPW == 2) {
+                const uint32_t tt = (uint32_t)t0 + 1u + a.token_offset;
+                const uint32_t s = tt - fast_div(tt, a.div_seq.m, a.div_seq.l) * a.seq_len;
+                const uint32_t pf1 = fast_div(s, a.div_hw.m, a.div_hw.l);
+                const uint32_t rem = s - pf1 * a.hw;
+                const uint32_t ph1 = fast_div(rem, a.div_w.m, a.div_w.l);
+                const uint32_t pw1 = rem - ph1 * a.ppw;
+                pf = ts ? pf1 : pf;
+                ph = ts ? ph1 : ph;
+                pw = ts ? pw1 : pw;
+            }
+            if (tl < D / 2) {               // the host gives every token >= D/2 lanes
                 const uint32_t pos = axis == 0 ? pf : (axis == 1 ? ph : pw);
                 // angle in revolutions, reduced to [0, 1): sin/cos(2*pi*rev) in hardware
                 const float rev = __builtin_amdgcn_fractf((float)pos * omega_rev);
                 const float c = __builtin_amdgcn_cosf(rev) * a.attention_factor;
                 const float sn = __builtin_amdgcn_sinf(rev) * a.attention_factor;
-                s_cs[tid] = f32x4{c, -sn, c, sn};
+                s_cs[ts * kMaxPairs + tl] = f32x4{c, -sn, c, sn};
             }
         } else if (XCH) {
             // per element g = 8u + e: angle index g (first half, sign -) or g - R/2 (second
@@ -522,9 +553,16 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                 sq += reg[j] == kQ ? ss[j] : 0.0f;
                 sk += reg[j] == kK ? ss[j] : 0.0f;
             }
-            sq = wave_sum(sq);
-            sk = wave_sum(sk);
-            if ((tid & 63) == 0) s_red[tid >> 6] = f32x2{sq, sk};
+            if (TPW == 1) {
+                sq = wave_sum(sq);
+                sk = wave_sum(sk);
+                if ((tid & 63) == 0) s_red[tid >> 6] = f32x2{sq, sk};
+            } else {
+                // per 32-lane group (each belongs to one token)
+                sq = group_sum(sq, 32);
+                sk = group_sum(sk, 32);
+                if ((tid & 31) == 0) s_red[tid >> 5] = f32x2{sq, sk};
+            }
         }
 
         if (NEED_BARRIER) __syncthreads();
@@ -532,20 +570,31 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         float rq = 1.0f, rk = 1.0f;
         if (NORM == kNormAcrossExt) {
             // sums over every head of the token, reduced by the caller (uniform scalar load)
-            const f32x2 p = reinterpret_cast<const f32x2 *>(a.sumsq_in)[t];
+            const f32x2 p = reinterpret_cast<const f32x2 *>(a.sumsq_in)[t];   // per lane's token
             rq = __builtin_amdgcn_rsqf(p.x * a.inv_count[0] + a.eps);
             rk = __builtin_amdgcn_rsqf(p.y * a.inv_count[1] + a.eps);
         } else if (NORM == kNormAcross) {
-            // every wave sums the per-wave partials: lane w of each 16-lane row reads wave w's
-            const int w = tid & 15;
-            const f32x2 p = w < (nth >> 6) ? s_red[w] : f32x2{0.0f, 0.0f};
-            const float sq = group_sum(p.x, 16), sk = group_sum(p.y, 16);
+            // every wave sums its token's partials: one token, lane w of each 16-lane row reads
+            // wave w's; two tokens, lane w of each 32-lane group reads its token's group w
+            float sq, sk;
+            if (TPW == 1) {
+                const int w = tid & 15;
+                const f32x2 p = w < (nth >> 6) ? s_red[w] : f32x2{0.0f, 0.0f};
+                sq = group_sum(p.x, 16);
+                sk = group_sum(p.y, 16);
+            } else {
+                const int ng = LT >> 5, w = tid & 31;
+                const f32x2 p = w < ng ? s_red[ts * ng + w] : f32x2{0.0f, 0.0f};
+                sq = group_sum(p.x, 32);
+                sk = group_sum(p.y, 32);
+            }
             rq = __builtin_amdgcn_rsqf(sq * a.inv_count[0] + a.eps);
             rk = __builtin_amdgcn_rsqf(sk * a.inv_count[1] + a.eps);
         }
         if (IS3D && unit_ok) {
             // interleaved and second-half lanes read (cos, sin), first-half lanes (cos, -sin)
-            const f32x2 *tab = reinterpret_cast<const f32x2 *>(s_cs) + (HALF && half_sign < 0.0f ? 0 : 1);
+            const f32x2 *tab = reinterpret_cast<const f32x2 *>(s_cs + ts * kMaxPairs) +
+                               (HALF && half_sign < 0.0f ? 0 : 1);
 #pragma unroll
             for (int e = 0; e < NPAIR; ++e) {
                 const f32x2 cs = tab[2 * (pair0 + e)];
@@ -636,14 +685,16 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         }
 
         // -- all stores last
-        uint8_t *out_q = static_cast<uint8_t *>(a.out[kQ]) + t * a.out_stride[kQ] * ESIZE;
-        uint8_t *out_k = static_cast<uint8_t *>(a.out[kK]) + t * a.out_stride[kK] * ESIZE;
-        uint8_t *out_v = NREG == 3 ? static_cast<uint8_t *>(a.out[kV]) + t * a.out_stride[kV] * ESIZE
+        uint8_t *out_q = static_cast<uint8_t *>(a.out[kQ]) + t0 * a.out_stride[kQ] * ESIZE;
+        uint8_t *out_k = static_cast<uint8_t *>(a.out[kK]) + t0 * a.out_stride[kK] * ESIZE;
+        uint8_t *out_v = NREG == 3 ? static_cast<uint8_t *>(a.out[kV]) + t0 * a.out_stride[kV] * ESIZE
                                    : out_k;
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
-            if (!ok[j]) continue;
-            uint8_t *orow = sel3(reg[j], out_q, out_k, out_v);
+            if (!ok[j] || !tok_ok) continue;
+            const int r = reg[j] < 3 ? reg[j] : 0;
+            const uint32_t tok = TPW == 2 ? (uint32_t)ts * (uint32_t)(a.out_stride[r] * ESIZE) : 0u;
+            uint8_t *orow = sel3(reg[j], out_q, out_k, out_v) + tok;
             const uint32_t e0 = hoff[j] + off0;
             if (FP8) st8_stream(orow + e0, make_uint2(pk[j].x, pk[j].y));
             else st16_stream(orow + 2 * e0, pk[j]);
@@ -693,10 +744,10 @@ __global__ void __launch_bounds__(1024) qkrope_sumsq_kernel(const SumsqArgs a)
 
 // ---- launch helpers ---------------------------------------------------------------------------
 
-template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
+template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU, int TPW>
 hipError_t go(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL((qkrope_kernel<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU>), dim3((unsigned)s.blocks),
+    hipLaunchKernelGGL((qkrope_kernel<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, TPW>), dim3((unsigned)s.blocks),
                        dim3(s.threads), s.lds_bytes, st, a);
     return hipGetLastError();
 }
@@ -704,10 +755,15 @@ hipError_t go(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU>
 hipError_t go_if(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    if constexpr (slots_compiled(SRC == kSrc3D ? 3 : 2, SU, NS))
-        return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU>(s, a, st);
-    else
+    if constexpr (slots_compiled(SRC == kSrc3D ? 3 : 2, SU, NS)) {
+        if constexpr (SU && NS == 1) {
+            if (s.tpw == 2) return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, 2>(s, a, st);
+        }
+        if (s.tpw != 1) return hipErrorInvalidValue;
+        return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, 1>(s, a, st);
+    } else {
         return hipErrorInvalidValue;
+    }
 }
 
 template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8>

@@ -128,6 +128,13 @@ SWEEP_3D = [
     (128, 32, 32, 32, (1, 2, 3), (16, 56, 56), 2, True, True, False, False),
     (64, 20, 20, 20, (2, 3, 2), (16, 24, 24), 1, True, True, True, False),
     (128, 8, 0, 8, (1, 1, 4), (128, 0, 0), 1, True, True, False, False),
+    # two tokens per workgroup (160 lanes a token), odd token count: the last workgroup has one
+    (64, 20, 20, 20, (1, 3, 5), (16, 24, 24), 1, False, True, True, False),
+    (128, 10, 6, 10, (1, 1, 7), (32, 48, 48), 1, True, True, False, True),
+    # head_dim 256 with few heads: fewer chunk lanes per token than angle pairs (128)
+    (256, 1, 1, 0, (1, 2, 3), (64, 96, 96), 1, True, True, False, True),
+    (256, 2, 2, 2, (2, 1, 3), (64, 96, 96), 1, False, True, True, False),
+    (256, 2, 0, 0, (1, 1, 5), (0, 128, 128), 1, False, False, True, False),
 ]
 
 
@@ -166,6 +173,8 @@ SWEEP_TABLE = [
     (9, 6, 2, 128, 128, False, "none", "bf16"),
     (1, 1, 1, 24, 2, True, "per_head", "bf16"),
     (40, 48, 8, 64, 32, True, "per_head", "f32"),
+    (7, 5, 3, 256, 256, True, "per_head", "f32"),        # two tokens per workgroup, odd count
+    (9, 10, 10, 128, 96, False, "across_heads", "bf16"),  # the same with across-heads norm
     # half-split with rotary_dim % 16 != 0: partners straddle 16-byte chunks
     (37, 3, 2, 64, 40, False, "per_head", "f32"),
     (50, 4, 4, 128, 100, False, "across_heads", "bf16"),
