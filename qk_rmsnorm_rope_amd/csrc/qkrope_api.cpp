@@ -319,6 +319,20 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     a.heads[kV] = 0;
     a.weight[0] = static_cast<const uint16_t *>(c.q_weight);
     a.weight[1] = static_cast<const uint16_t *>(c.k_weight);
+    // Idle slots issue their loads unconditionally at the start of their region's token row (and
+    // drop the result); a region without heads may have NULL pointers, so it borrows the other
+    // region's row, stride and weights. Every address the kernel forms then lies inside a
+    // caller's tensor (Hq + Hk > 0 here).
+    if (Hq == 0) {
+        a.in[kQ] = a.in[kK];
+        a.in_stride[kQ] = a.in_stride[kK];
+        a.weight[0] = a.weight[1];
+    }
+    if (Hk == 0) {
+        a.in[kK] = a.in[kQ];
+        a.in_stride[kK] = a.in_stride[kQ];
+        a.weight[1] = a.weight[0];
+    }
     a.table_cos = c.cos_table;
     a.table_sin = c.sin_table;
     a.cos_stride = c.cos_stride;
@@ -450,9 +464,11 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
     KernelArgs a;
     std::memset(&a, 0, sizeof a);
     const uint16_t *base_in = static_cast<const uint16_t *>(c.qkv);
+    // a region without heads points at the row start, so its idle-slot loads stay inside the
+    // row (its own offset could be the end of qkv)
     a.in[kQ] = base_in;
-    a.in[kK] = base_in + (int64_t)Hq * D;
-    a.in[kV] = base_in + (int64_t)(Hq + Hk) * D;
+    a.in[kK] = Hk ? base_in + (int64_t)Hq * D : base_in;
+    a.in[kV] = Hv ? base_in + (int64_t)(Hq + Hk) * D : base_in;
     a.out[kQ] = c.q_out;
     a.out[kK] = c.k_out;
     a.out[kV] = c.v_out;
@@ -465,6 +481,11 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
     a.heads[kV] = Hv;
     a.weight[0] = static_cast<const uint16_t *>(c.q_weight);
     a.weight[1] = static_cast<const uint16_t *>(c.k_weight);
+    // as for the table form: an empty Q or K region borrows the other's weights for its idle
+    // loads; with neither, there is nothing to normalise (and the weights may be NULL)
+    const bool norm = c.is_qk_norm && Hq + Hk > 0;
+    if (Hq == 0) a.weight[0] = a.weight[1];
+    if (Hk == 0) a.weight[1] = a.weight[0];
     a.sumsq_in = ext ? c.sumsq : nullptr;
     a.num_tokens = T;
     a.head_dim = D;
@@ -509,7 +530,7 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
     KernelKey key;
     key.head_dim_tpl = D;
     key.pairing = half ? kPairHalf : kPairInterleaved;     // R/2 = D/2 is a multiple of 8
-    key.norm = !c.is_qk_norm ? kNormNone : (ext ? kNormAcrossExt : kNormAcross);
+    key.norm = !norm ? kNormNone : (ext ? kNormAcrossExt : kNormAcross);
     key.src = kSrc3D;
     key.act = kActBF16;
     key.fp8 = c.output_fp8 != 0;

@@ -716,19 +716,21 @@ __global__ void __launch_bounds__(1024) qkrope_sumsq_kernel(const SumsqArgs a)
     const int64_t t = blockIdx.x;
     const uint16_t *row = a.qkv + t * a.row;
     const int nq = a.q_chunks, nall = a.q_chunks + a.k_chunks;
-    uint4 x[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int c = tid + i * nth;
-        x[i] = ld16_stream<true>(row, c < nall ? 16u * (uint32_t)c : 0u);
-    }
     float sq = 0.0f, sk = 0.0f;
+    if (nall > 0) {                 // uniform; with no Q or K heads the row may hold nothing
+        uint4 x[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int c = tid + i * nth;
-        const float v = sumsq_packed<kActBF16>(x[i], 0.0f);
-        sq += c < nq ? v : 0.0f;
-        sk += (c >= nq && c < nall) ? v : 0.0f;
+        for (int i = 0; i < NI; ++i) {
+            const int c = tid + i * nth;
+            x[i] = ld16_stream<true>(row, c < nall ? 16u * (uint32_t)c : 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int c = tid + i * nth;
+            const float v = sumsq_packed<kActBF16>(x[i], 0.0f);
+            sq += c < nq ? v : 0.0f;
+            sk += (c >= nq && c < nall) ? v : 0.0f;
+        }
     }
     sq = wave_sum(sq);
     sk = wave_sum(sk);
@@ -841,7 +843,7 @@ hipError_t launch_table(const KernelKey &k, const LaunchShape &s, const KernelAr
 inline hipError_t launch_sumsq_impl(const SumsqArgs &a, int64_t tokens, int threads, hipStream_t st)
 {
     const int n = a.q_chunks + a.k_chunks;
-    const int ni = (n + threads - 1) / threads;
+    const int ni = n > 0 ? (n + threads - 1) / threads : 1;   // no Q/K heads: one pass writing 0
     const dim3 grid((unsigned)tokens), block(threads);
     switch (ni) {
     case 1: hipLaunchKernelGGL(qkrope_sumsq_kernel<1>, grid, block, 0, st, a); break;
