@@ -363,3 +363,57 @@ def test_3d_empty_regions_null_weights(H, norm):
     ref_s = oracle.sumsq_3d(inp["qkv"].reshape(w.num_tokens, -1), num_heads_q=H[0],
                             num_heads_k=H[1], num_heads_v=H[2], head_dim=128)
     np.testing.assert_allclose(s.cpu().numpy(), ref_s, rtol=1e-5)
+
+
+# --- streams and graphs --------------------------------------------------------------------------
+
+def test_concurrent_streams_one_handle():
+    # the handle is immutable: calls on two streams at once give the single-stream results
+    ws = [wl.ROPE3D_ACROSS_S15360.with_(ppf=1, pph=4), wl.ROPE3D_NEOX_FP8_S18480.with_(ppf=1, pph=5)]
+    ins = [wl.rope3d_inputs(w) for w in ws]
+    g = [{k: _gpu(v) for k, v in i.items()} for i in ins]
+    ref = [qr.run_workload_3d(w, x["qkv"], x["q_weight"], x["k_weight"]) for w, x in zip(ws, g)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(o) for o in r] for r in ref]
+    for rep in range(5):
+        for w, x, o, st in zip(ws, g, outs, streams):
+            with torch.cuda.stream(st):
+                qr.run_workload_3d(w, x["qkv"], x["q_weight"], x["k_weight"], *o)
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            for a, b in zip(o, r):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_graph_capture_and_replay():
+    # both forms captured in one HIP graph; every replay matches the eager launch bit for bit
+    w3 = wl.ROPE3D_ACROSS_S15360.with_(ppf=1, pph=6)
+    wt = wl.TABLE_INTERLEAVED_T4096.with_(num_tokens=777)
+    i3 = {k: _gpu(v) for k, v in wl.rope3d_inputs(w3).items()}
+    it = {k: _gpu(v) for k, v in wl.table_inputs(wt).items()}
+    o3 = qr.run_workload_3d(w3, i3["qkv"], i3["q_weight"], i3["k_weight"])
+    qo, ko = torch.empty_like(it["q"]), torch.empty_like(it["k"])
+    eager = lambda: (qr.run_workload_3d(w3, i3["qkv"], i3["q_weight"], i3["k_weight"], *o3),
+                     qr.qkrope_run_table(it["q"], it["k"], it["q_weight"], it["k_weight"],
+                                         it["rope_table"], wt.eps, q_out=qo, k_out=ko,
+                                         interleaved=True))
+    eager()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (*o3, qo, ko)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        eager()                                   # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            eager()
+    for rep in range(4):
+        for t in (*o3, qo, ko):
+            t.zero_()                             # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((*o3, qo, ko), ref):
+            assert torch.equal(t, r), f"replay {rep}"
