@@ -4,7 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step is one launch of the whole prologue (norm, rotation, V copy, output rounding) over one
-batch of the workload. The default workload is the 15360-token, 32-head, head_dim-128 3D problem
+batch of the workload. The timed steps are captured once into a HIP graph and replayed (the way
+a fixed-shape prologue that runs in every layer and denoising step is launched in production);
+--stream launches them one by one from the host instead.
+The default workload is the 15360-token, 32-head, head_dim-128 3D problem
 with across-heads norm and interleaved pairs (LTX-2's video self-attention shape). Inputs are
 seeded synthetic bf16 drawn by qk_rmsnorm_rope_amd.workloads, resident in HBM before timing.
 Prints one JSON line with tokens/s, the HBM roofline of the kernel and a CPU baseline (the fp64
@@ -15,6 +18,8 @@ Other modes (used to produce the committed profiles):
     --copy-calibration  launches a plain elementwise copy of known size (counter calibration)
     --crossover         fused table-form call vs an eager torch chain over 64..65536 tokens (the
                         fused-vs-eager threshold of vLLM-Omni's fused_qk_norm_rope_min_tokens)
+    --stream            launch each step on the stream from the host instead of replaying the
+                        timed steps as one HIP graph (the default)
 """
 from __future__ import annotations
 
@@ -159,6 +164,29 @@ def time_launches(launch, steps, warmup):
     return wall, start.elapsed_time(end) * 1e-3 / steps
 
 
+def time_graph(launch, steps, warmup):
+    """Capture `steps` launches in one HIP graph on the current stream and time one replay:
+    (wall_s, gpu_s_per_launch), like time_launches."""
+    import torch
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.current_stream()):
+        for i in range(steps):
+            launch(warmup + i)
+    graph.replay()                                  # warm replay
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) * 1e-3 / steps
+
+
 def cpu_baseline(w, cpu_inputs, budget_s: float = 12.0) -> dict:
     """The fp64 oracle, as it stands, on the first tokens of the same workload (output encoding
     included), on every host core OpenMP gives it, until `budget_s` of work."""
@@ -297,6 +325,7 @@ def main() -> int:
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--crossover", action="store_true")
+    ap.add_argument("--stream", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -315,17 +344,22 @@ def main() -> int:
         crossover(dev, args.warmup)
         return 0
     w = wl.WORKLOADS[args.workload]
+    use_graph = not args.stream
+    if use_graph:
+        # launchers bind the stream they are prepared on: prepare them on the capture stream
+        capture = torch.cuda.Stream()
+        capture.wait_stream(torch.cuda.current_stream())
+        torch.cuda.set_stream(capture)
+    timer = time_graph if use_graph else time_launches
     cpu_inputs, launch, calls = make_launcher(w, dev, args.sets)
     torch.cuda.synchronize()
-    total, mean_step = time_launches(launch, args.steps, args.warmup)
+    total, mean_step = timer(launch, args.steps, args.warmup)
     mean_launch = mean_step
     extra = {}
     if is_sharded(w):
         # the step is two kernels: time each on its own for the per-kernel rooflines
-        _, mean_launch = time_launches(lambda i: calls[i % args.sets].apply(), args.steps,
-                                       args.warmup)
-        _, mean_sumsq = time_launches(lambda i: calls[i % args.sets].sumsq(), args.steps,
-                                      args.warmup)
+        _, mean_launch = timer(lambda i: calls[i % args.sets].apply(), args.steps, args.warmup)
+        _, mean_sumsq = timer(lambda i: calls[i % args.sets].sumsq(), args.steps, args.warmup)
         extra = {"sumsq_kernel": {"achieved": sumsq_bytes(w) / mean_sumsq / 1e9,
                                   "unit": "GB/s", "mean_launch_us": mean_sumsq * 1e6,
                                   "algorithmic_bytes": sumsq_bytes(w)},
@@ -357,7 +391,8 @@ def main() -> int:
                    "head_dim": w.head_dim,
                    "parallelism": (f"one rank of {w.head_shards} head shards"
                                    if is_sharded(w) else "single-gpu"),
-                   "buffer_sets": args.sets},
+                   "buffer_sets": args.sets,
+                   "launch": "hip_graph" if use_graph else "stream"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
