@@ -359,7 +359,19 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 
     // The workgroup's first token, and this lane's: a missing second token (odd token count)
     // re-reads the first token's row and stores nothing.
-    const int64_t t0 = (int64_t)blockIdx.x * TPW;
+    // Workgroups are dealt to the 8 XCDs round-robin (block b to XCD b % 8). With xcd_group G,
+    // XCD x takes runs of G consecutive token blocks instead of every 8th block, so a page of
+    // the streams is touched by one XCD's translation caches, not all eight; blocks past the
+    // last whole run of 8G keep their own index.
+    uint32_t blk = blockIdx.x;
+    if (a.xcd_group) {
+        const uint32_t G = a.xcd_group, S = 8u * G, full = gridDim.x / S * S;
+        if (blk < full) {
+            const uint32_t j = blk >> 3, x = blk & 7u;
+            blk = (j / G) * S + x * G + j % G;
+        }
+    }
+    const int64_t t0 = (int64_t)blk * TPW;
     const bool tok_ok = TPW == 1 || t0 + ts < a.num_tokens;
     const int ts_eff = tok_ok ? ts : 0;
     const int64_t t = t0 + ts_eff;
