@@ -720,7 +720,7 @@ __global__ void __launch_bounds__(1024) qkrope_sumsq_kernel(const SumsqArgs a)
     __shared__ f32x2 s_red[16];
     const int tid = threadIdx.x;
     const int nth = blockDim.x;
-    const int64_t t = blockIdx.x;
+    const int64_t t = blockIdx.x;           // plain order (measured faster here than XCD runs)
     const uint16_t *row = a.qkv + t * a.row;
     const int nq = a.q_chunks, nall = a.q_chunks + a.k_chunks;
     float sq = 0.0f, sk = 0.0f;
