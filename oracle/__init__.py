@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_run_table_split.restype = I
         L.oracle_sumsq_3d.argtypes = [P, I64, I, I, I, I, P]
         L.oracle_sumsq_3d.restype = I
+        L.oracle_cam_prep.argtypes = [P, P, P, I, P, P, P, P, D, I64, I64, I, I, I64, I64, I64,
+                                      P, P, P, P]
+        L.oracle_cam_prep.restype = I
         L.oracle_f16_encode.argtypes = [D]
         L.oracle_f16_encode.restype = ctypes.c_uint16
         L.oracle_f16_decode.argtypes = [ctypes.c_uint16]
@@ -234,6 +237,58 @@ def sumsq_3d(qkv, *, num_heads_q, num_heads_k, num_heads_v, head_dim) -> np.ndar
     if rc != 0:
         raise ValueError(f"oracle_sumsq_3d rejected its arguments (code {rc})")
     return out
+
+
+def _f32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().cpu()
+        if x.dtype != torch.float32:
+            raise TypeError(f"expected a float32 tensor, got {x.dtype}")
+        x = x.numpy()
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.float32:
+        raise TypeError(f"expected float32, got {x.dtype}")
+    return x
+
+
+def cam_prep(q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, *, num_heads=None,
+             head_dim=None):
+    """fp64 camera prologue (UCPE page, cam_prep_func) under the readings in oracle.c.
+
+    q, k, v: [B, N, H, D] bf16 or float16 (or [B, N, S] rows of S >= H*D elements with
+    num_heads and head_dim given); proj_q, proj_kv: [B, N, 4, 4] float32; rope_cos, rope_sin:
+    [N, D/2] float32. Returns q_out, k_out, v_out fp64 [B, H, D, N] and inflation_sq fp64
+    [B, H, N], unrounded."""
+    xs = [_act_bits(t) for t in (q, k, v)]
+    acts = {a for _, a in xs}
+    if len(acts) != 1:
+        raise ValueError("q, k and v must share the activation dtype")
+    act = acts.pop()
+    bits = [b for b, _ in xs]
+    if bits[0].ndim == 4:
+        B, N, H, D = bits[0].shape
+    else:
+        B, N = bits[0].shape[:2]
+        H, D = int(num_heads), int(head_dim)
+    strides = [int(np.prod(b.shape[2:])) for b in bits]
+    if any(st < H * D for st in strides) or any(b.shape[:2] != (B, N) for b in bits):
+        raise ValueError("q, k, v must be [B, N, H, D] (or rows of at least H*D elements)")
+    pq, pkv = _f32(proj_q), _f32(proj_kv)
+    tc, ts = _f32(rope_cos), _f32(rope_sin)
+    if pq.shape != (B, N, 4, 4) or pkv.shape != (B, N, 4, 4):
+        raise ValueError("projections must be [B, N, 4, 4]")
+    if tc.shape != (N, D // 2) or ts.shape != (N, D // 2):
+        raise ValueError("rope tables must be [N, D/2]")
+    outs = [np.empty((B, H, D, N), np.float64) for _ in range(3)]
+    infl = np.empty((B, H, N), np.float64)
+    rc = lib().oracle_cam_prep(_ptr(bits[0]), _ptr(bits[1]), _ptr(bits[2]), act, _ptr(pq),
+                               _ptr(pkv), _ptr(tc), _ptr(ts), float(k_scale), B, N, H, D,
+                               strides[0], strides[1], strides[2], _ptr(outs[0]),
+                               _ptr(outs[1]), _ptr(outs[2]), _ptr(infl))
+    if rc != 0:
+        raise ValueError(f"oracle_cam_prep rejected its arguments (code {rc})")
+    return outs[0], outs[1], outs[2], infl
 
 
 def run_3d_workload(w, qkv, q_weight, k_weight, token_offset=0):

@@ -38,6 +38,22 @@
  *   - "Activation dtype" covers bf16 and IEEE binary16; weights share the activation dtype.
  *   - A head-sharded across-heads norm uses the sums of squares of the whole row (every shard's
  *     heads), i.e. it equals the unsharded norm; oracle_sumsq_3d gives those per-token sums.
+ *   [camera prologue] vLLM-Omni API docs, "vllm_omni.diffusion.models.sana_wm.ucpe",
+ *       cam_prep_func: Q, K (already normalised) and raw V are (B, N, H, D); proj_q and proj_kv
+ *       are per-token (B, N, 4, 4) ray projection matrices; rope_cos / rope_sin are (N, D/2)
+ *       interleaved-pair tables; k_scale multiplies K; the steps are ReLU, the K scale, the ray
+ *       projection and RoPE; outputs are (B, H, D, N) plus inflation_sq (B, H, N). The page
+ *       names these but leaves open how they compose; the readings taken here:
+ *   - Q: ReLU, projection by proj_q, RoPE. K: ReLU, times k_scale, projection by proj_kv, RoPE.
+ *     V: projection by proj_kv, RoPE (the K/V matrices are one transform shared by K and V).
+ *     ReLU(x) = x if x > 0 else 0.
+ *   - A 4x4 matrix P acts on a head vector as D/4 independent groups of four consecutive
+ *     channels: y[4g + i] = sum_j P[i][j] * x[4g + j], P stored row-major.
+ *   - RoPE rotates the adjacent pairs (2i, 2i+1) of the projected vector by the angle whose
+ *     cosine and sine are row n, column i of the tables (rotation by +theta as above).
+ *   - inflation_sq(b, h, n) = |P_kv applied to k'|^2 / |k'|^2 for the key head vector
+ *     k' = k_scale * ReLU(k) that enters the projection (how much the projection grows its
+ *     squared norm), and 1 where |k'| = 0.
  *
  * Everything is computed in double from the exact decoded inputs and rounded once at the output.
  */
@@ -454,6 +470,93 @@ int oracle_sumsq_3d(const uint16_t *qkv, int64_t num_tokens, int num_heads_q, in
         out[2 * t + 1] = sk;
     }
     return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Camera prologue (UCPE page, cam_prep_func). q, k, v: [B, N, H, D] 16-bit activations with
+ * token strides q_stride, k_stride, v_stride (elements; batch stride N * token stride).
+ * proj_q, proj_kv: [B, N, 4, 4] float32, row-major per token. rope_cos, rope_sin: [N, D/2]
+ * float32. Outputs, fp64 unrounded: q_out, k_out, v_out [B, H, D, N]; inflation_sq [B, H, N].
+ * ------------------------------------------------------------------------------------------- */
+
+/* p = P applied to each group of four channels of a (D values). */
+static void project_groups(const float *P, const double *a, int D, double *p)
+{
+    for (int g = 0; g < D / 4; ++g)
+        for (int i = 0; i < 4; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < 4; ++j)
+                acc += (double)P[4 * i + j] * a[4 * g + j];
+            p[4 * g + i] = acc;
+        }
+}
+
+/* One head vector through the camera transform: ReLU if relu, times scale, projection, RoPE.
+ * Writes y[0..D) and returns |p|^2 / |a|^2 (1 when |a| = 0), a and p as in the header. */
+static double cam_head(const uint16_t *x, int act, int relu, double scale, const float *P,
+                       const float *cos_row, const float *sin_row, int D, double *a, double *p,
+                       double *y)
+{
+    double na = 0.0, np_ = 0.0;
+    for (int d = 0; d < D; ++d) {
+        double v = act_decode(act, x[d]);
+        if (relu) v = v > 0.0 ? v : 0.0;
+        a[d] = scale * v;
+        na += a[d] * a[d];
+    }
+    project_groups(P, a, D, p);
+    for (int d = 0; d < D; ++d) np_ += p[d] * p[d];
+    for (int i = 0; i < D / 2; ++i) {
+        double c = (double)cos_row[i], s = (double)sin_row[i];
+        y[2 * i] = p[2 * i] * c - p[2 * i + 1] * s;
+        y[2 * i + 1] = p[2 * i + 1] * c + p[2 * i] * s;
+    }
+    return na > 0.0 ? np_ / na : 1.0;
+}
+
+int oracle_cam_prep(const uint16_t *q, const uint16_t *k, const uint16_t *v, int act_dtype,
+                    const float *proj_q, const float *proj_kv, const float *rope_cos,
+                    const float *rope_sin, double k_scale, int64_t batch, int64_t num_tokens,
+                    int num_heads, int head_dim, int64_t q_stride, int64_t k_stride,
+                    int64_t v_stride, double *q_out, double *k_out, double *v_out,
+                    double *inflation_sq)
+{
+    if (batch < 0 || num_tokens < 0 || num_heads < 0 || head_dim <= 0 || head_dim % 4)
+        return ORACLE_BAD_ARG;
+    if (act_dtype != ORACLE_ACT_BF16 && act_dtype != ORACLE_ACT_F16) return ORACLE_BAD_ARG;
+    const int D = head_dim, H = num_heads;
+    const int64_t N = num_tokens, BN = batch * num_tokens;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *scratch = (double *)malloc(sizeof(double) * 3 * (size_t)D);
+        if (!scratch) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t bn = 0; bn < BN; ++bn) {
+            if (!scratch) continue;
+            const int64_t b = bn / N, n = bn % N;
+            double *a = scratch, *p = scratch + D, *y = scratch + 2 * D;
+            const float *cr = rope_cos + n * (D / 2), *sr = rope_sin + n * (D / 2);
+            for (int h = 0; h < H; ++h) {
+                const int64_t o = (b * H + h) * (int64_t)D * N + n;  /* out[b][h][0][n] */
+                cam_head(q + bn * q_stride + (int64_t)h * D, act_dtype, 1, 1.0, proj_q + bn * 16,
+                         cr, sr, D, a, p, y);
+                for (int d = 0; d < D; ++d) q_out[o + (int64_t)d * N] = y[d];
+                double infl = cam_head(k + bn * k_stride + (int64_t)h * D, act_dtype, 1, k_scale,
+                                       proj_kv + bn * 16, cr, sr, D, a, p, y);
+                for (int d = 0; d < D; ++d) k_out[o + (int64_t)d * N] = y[d];
+                inflation_sq[(b * H + h) * N + n] = infl;
+                cam_head(v + bn * v_stride + (int64_t)h * D, act_dtype, 0, 1.0, proj_kv + bn * 16,
+                         cr, sr, D, a, p, y);
+                for (int d = 0; d < D; ++d) v_out[o + (int64_t)d * N] = y[d];
+            }
+        }
+        free(scratch);
+    }
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
 /* Threads an OpenMP parallel region of this library will use. */
