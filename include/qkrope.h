@@ -240,6 +240,44 @@ int qkrope_run_3d_sharded(qkrope_handle h,
                           double output_quant_scale, double v_quant_scale,
                           void *q_out, void *k_out, void *v_out, void *stream);
 
+/*
+ * Camera prologue of the SANA-WM UCPE branch: vLLM-Omni "vllm_omni.diffusion.models.sana_wm.ucpe",
+ * cam_prep_func (parameters and returns). The page lists the steps (ReLU, the K scale, the
+ * per-token 4x4 ray projection, interleaved RoPE from separate cos and sin tables) and the
+ * shapes, but not how they compose; this library takes the reading
+ *     q_trans = RoPE(P_q . ReLU(q))
+ *     k_trans = RoPE(P_kv . (k_scale * ReLU(k)))
+ *     v_trans = RoPE(P_kv . v)
+ *     inflation_sq = |P_kv . k'|^2 / |k'|^2 with k' = k_scale * ReLU(k)   (1 where k' = 0)
+ * per batch b, token n and head h, where P . x applies the token's 4x4 matrix to each group of
+ * four consecutive channels, y[4g+i] = sum_j P[i][j] * x[4g+j], and RoPE rotates the pairs
+ * (2i, 2i+1) by +theta: (a, b) -> (a cos - b sin, b cos + a sin) with cos = rope_cos[n][i],
+ * sin = rope_sin[n][i]. ReLU(x) = x for x > 0, else 0. The RMSNorm of q and k is the caller's.
+ *
+ *   q, k, v        device, [batch, num_tokens, num_heads, head_dim] activations (act_dtype bf16
+ *                  or binary16); token (b, n) starts at (b*num_tokens + n) * x_stride elements;
+ *                  16-byte aligned; strides multiples of 8, >= num_heads*head_dim, < 2^24.
+ *                  The three may alias (all are read-only).
+ *   proj_q, proj_kv  device float32 [batch, num_tokens, 4, 4], row-major per token, 16-byte
+ *                  aligned.
+ *   rope_cos, rope_sin  device float32 [num_tokens, head_dim/2], 16-byte aligned.
+ *   k_scale        multiplies K (the page's head_dim^-1/2 * spatial_tokens^-1/2).
+ *   q_out, k_out, v_out  device, [batch, num_heads, head_dim, num_tokens] in act_dtype,
+ *                  contiguous, 2-byte aligned (16-byte aligned with num_tokens % 8 == 0 takes
+ *                  the fast store path).
+ *   inflation_sq   device float32 [batch, num_heads, num_tokens], contiguous, or NULL to skip.
+ * No output may overlap an input or another output. head_dim must be a multiple of 4
+ * (QKROPE_ERR_INVALID otherwise); this library handles multiples of 8 up to 256, and
+ * batch * num_tokens < 2^31 (QKROPE_ERR_UNSUPPORTED). An empty problem (batch, num_tokens or
+ * num_heads 0) is a no-op.
+ */
+int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v, int act_dtype,
+                    const float *proj_q, const float *proj_kv, const float *rope_cos,
+                    const float *rope_sin, float k_scale, int64_t batch, int64_t num_tokens,
+                    int num_heads, int head_dim, int64_t q_stride, int64_t k_stride,
+                    int64_t v_stride, void *q_out, void *k_out, void *v_out,
+                    float *inflation_sq, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

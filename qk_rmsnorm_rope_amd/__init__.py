@@ -9,9 +9,11 @@ Entry points, with the names of the C ABI:
   qkrope_run_table_ex (split cos/sin tables, float16 activations, E4M3 outputs)
   qkrope_sumsq_3d / qkrope_run_3d_sharded (sequence- and head-sharded 3D form)
   qkrope_min_tokens (fused-vs-eager threshold, QKROPE_FUSED_MIN_TOKENS)
-and the two page-shaped conveniences that allocate outputs:
+  qkrope_cam_prep (camera prologue of the SANA-WM UCPE branch)
+and the page-shaped conveniences that allocate outputs:
   fused_qk_norm_rope      -- vLLM-Omni "vllm_omni.diffusion.layers.fused_qk_norm_rope"
   fused_qk_rmsnorm_rope   -- FlashInfer "flashinfer.norm.fused_qk_rmsnorm_rope"
+  cam_prep_func           -- vLLM-Omni "vllm_omni.diffusion.models.sana_wm.ucpe"
 
 There is no fallback: if the library is missing or the device is not gfx950, calls raise.
 """
@@ -83,6 +85,9 @@ def lib() -> ctypes.CDLL:
                                             I, I, I, I, D, D, I, D, D, D, D, I, I, D, D,
                                             P, P, P, P]
         L.qkrope_run_3d_sharded.restype = I
+        L.qkrope_cam_prep.argtypes = [P, P, P, P, I, P, P, P, P, ctypes.c_float, I64, I64, I, I,
+                                      I64, I64, I64, P, P, P, P, P]
+        L.qkrope_cam_prep.restype = I
         runtimes = _hip_runtimes_loaded()
         if len(runtimes) > 1:
             raise RuntimeError(f"two HIP runtimes are loaded ({sorted(runtimes)}); "
@@ -521,6 +526,96 @@ class PreparedSharded3D:
     def __call__(self) -> None:
         self.sumsq()
         self.apply()
+
+
+_ACT_CODES = {torch.bfloat16: QKROPE_DTYPE_BF16, torch.float16: QKROPE_DTYPE_F16}
+
+
+def _cam_rows(t: torch.Tensor, shape, name: str) -> int:
+    """Token stride of a [B, N, H, D] view whose heads and dims are contiguous and whose batch
+    stride is N token strides (the layout the C ABI takes)."""
+    B, N, H, D = shape
+    if t.dim() != 4 or tuple(t.shape) != (B, N, H, D):
+        raise ValueError(f"{name} must be [batch, tokens, heads, head_dim] = {(B, N, H, D)}")
+    if (H > 1 and t.stride(2) != D) or (D > 1 and t.stride(3) != 1):
+        raise ValueError(f"{name} must have contiguous heads and dims")
+    if N > 1:
+        st = t.stride(1)
+    else:                       # one token: its stride is the batch stride
+        st = t.stride(0) if B > 1 else H * D
+    if B > 1 and N > 0 and t.stride(0) != N * st:
+        raise ValueError(f"{name}: batch stride must be tokens * token stride")
+    return st
+
+
+def qkrope_cam_prep(q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, *, q_out, k_out,
+                    v_out, inflation_sq=None, stream=None) -> None:
+    """Camera prologue into caller-provided outputs: q, k, v [B, N, H, D] (bf16 or float16),
+    proj_q / proj_kv float32 [B, N, 4, 4], rope_cos / rope_sin float32 [N, D/2]; q_out, k_out,
+    v_out contiguous [B, H, D, N] of the activation dtype; inflation_sq contiguous float32
+    [B, H, N] or None."""
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, tokens, heads, head_dim]")
+    shape = tuple(q.shape)
+    B, N, H, D = shape
+    act = _ACT_CODES.get(q.dtype)
+    if act is None or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a bfloat16 or float16 dtype")
+    strides = [_cam_rows(t, shape, n) for t, n in ((q, "q"), (k, "k"), (v, "v"))]
+    for t, n, want in ((proj_q, "proj_q", (B, N, 4, 4)), (proj_kv, "proj_kv", (B, N, 4, 4)),
+                       (rope_cos, "rope_cos", (N, D // 2)), (rope_sin, "rope_sin", (N, D // 2))):
+        if t.dtype != torch.float32 or tuple(t.shape) != want or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous float32 tensor of shape {want}")
+    for t, n in ((q_out, "q_out"), (k_out, "k_out"), (v_out, "v_out")):
+        if t.dtype != q.dtype or tuple(t.shape) != (B, H, D, N) or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous [batch, heads, head_dim, tokens] tensor "
+                             "of the activation dtype")
+    if inflation_sq is not None and (inflation_sq.dtype != torch.float32 or
+                                     tuple(inflation_sq.shape) != (B, H, N) or
+                                     not inflation_sq.is_contiguous()):
+        raise ValueError("inflation_sq must be a contiguous float32 [batch, heads, tokens] tensor")
+    s = lib().qkrope_cam_prep(_handle_for(q.device), _ptr(q), _ptr(k), _ptr(v), act,
+                              _ptr(proj_q), _ptr(proj_kv), _ptr(rope_cos), _ptr(rope_sin),
+                              float(k_scale), B, N, H, D, strides[0], strides[1], strides[2],
+                              _ptr(q_out), _ptr(k_out), _ptr(v_out), _ptr(inflation_sq),
+                              _stream(q.device, stream))
+    _check(s, "qkrope_cam_prep")
+
+
+def cam_prep_func(q_normed, k_normed, v_raw, *, proj_q, proj_kv, rope_cos, rope_sin, k_scale):
+    """vLLM-Omni's cam_prep_func signature: returns q_trans, k_trans, v_trans [B, H, D, N] and
+    inflation_sq [B, H, N] (the library header states how the steps compose)."""
+    B, N, H, D = q_normed.shape
+    outs = [torch.empty((B, H, D, N), dtype=q_normed.dtype, device=q_normed.device)
+            for _ in range(3)]
+    infl = torch.empty((B, H, N), dtype=torch.float32, device=q_normed.device)
+    qkrope_cam_prep(q_normed, k_normed, v_raw, proj_q, proj_kv, rope_cos, rope_sin, k_scale,
+                    q_out=outs[0], k_out=outs[1], v_out=outs[2], inflation_sq=infl)
+    return outs[0], outs[1], outs[2], infl
+
+
+class PreparedCam:
+    """One qkrope_cam_prep call marshalled once for repeated launches (tensors must stay alive
+    and unmoved)."""
+
+    def __init__(self, q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, q_out, k_out,
+                 v_out, inflation_sq, stream=None):
+        qkrope_cam_prep(q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, q_out=q_out,
+                        k_out=k_out, v_out=v_out, inflation_sq=inflation_sq, stream=stream)
+        B, N, H, D = q.shape
+        st = [_cam_rows(t, tuple(q.shape), "x") for t in (q, k, v)]
+        self._fn = lib().qkrope_cam_prep
+        self._args = (_handle_for(q.device), _ptr(q), _ptr(k), _ptr(v), _ACT_CODES[q.dtype],
+                      _ptr(proj_q), _ptr(proj_kv), _ptr(rope_cos), _ptr(rope_sin),
+                      float(k_scale), B, N, H, D, st[0], st[1], st[2], _ptr(q_out), _ptr(k_out),
+                      _ptr(v_out), _ptr(inflation_sq), _stream(q.device, stream))
+        self._keep = (q, k, v, proj_q, proj_kv, rope_cos, rope_sin, q_out, k_out, v_out,
+                      inflation_sq)
+
+    def __call__(self) -> None:
+        s = self._fn(*self._args)
+        if s != QKROPE_OK:
+            _check(s, "qkrope_cam_prep")
 
 
 def run_workload_3d(w, qkv, q_weight, k_weight, q_out=None, k_out=None, v_out=None):

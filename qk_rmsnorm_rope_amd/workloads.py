@@ -19,6 +19,11 @@ Value recipe (stated once, used everywhere):
   * rope table (table form only): theta_i = t * base**(-2i/rotary_dim) for token t, cos/sin taken
     in float64 and rounded to float32 (and then to bf16 or binary16 for a 16-bit table). The
     table is an input of the table form; the pages leave its contents to the caller.
+  * camera prologue (vLLM-Omni "vllm_omni.diffusion.models.sana_wm.ucpe", cam_prep_func):
+    q, k, v [B, N, H, D] drawn as activations (q and k stand for already-normalised values,
+    unit RMS); proj_q and proj_kv are per-token rigid camera transforms [[R, t], [0, 0, 0, 1]]
+    with R from a normalised N(0,1) quaternion and t = 0.5*N(0,1)^3, in float32; the split
+    tables are cos/sin of theta_i = n * base**(-2i/D), float64 rounded to float32.
 Every array is dense and contiguous, with no padding and no special values.
 """
 from __future__ import annotations
@@ -37,6 +42,9 @@ ROLE_QKV = 0   # packed qkv (3D form) or q (table form)
 ROLE_K = 1     # k (table form)
 ROLE_WQ = 2
 ROLE_WK = 3
+ROLE_V = 4     # v (camera prologue)
+ROLE_PQ = 5    # proj_q
+ROLE_PKV = 6   # proj_kv
 
 
 @dataclass(frozen=True)
@@ -112,6 +120,34 @@ class Rope3DWorkload:
         return dataclasses.replace(self, **kw)
 
 
+@dataclass(frozen=True)
+class CamWorkload:
+    """Camera prologue: q, k, v [B, N, H, D]; projections [B, N, 4, 4]; tables [N, D/2] fp32.
+    The N tokens form a ppf x pph x ppw latent grid; k_scale = D^-1/2 * (pph*ppw)^-1/2 (the page's
+    D^-0.5 * spatial_tokens^-0.5 with the spatial tokens of one frame)."""
+    name: str
+    batch: int
+    ppf: int
+    pph: int
+    ppw: int
+    num_heads: int
+    head_dim: int
+    seed: int
+    act_dtype: str = "bf16"
+    base: float = 10000.0
+
+    @property
+    def num_tokens(self) -> int:
+        return self.ppf * self.pph * self.ppw
+
+    @property
+    def k_scale(self) -> float:
+        return float(self.head_dim ** -0.5 * (self.pph * self.ppw) ** -0.5)
+
+    def with_(self, **kw) -> "CamWorkload":
+        return dataclasses.replace(self, **kw)
+
+
 # --- the five named workloads ------------------------------------------------------------------
 
 # MiniMax-H3 geometry of the table form's half-split kernel (head_dim 128, rotary_dim 96).
@@ -166,11 +202,16 @@ ROPE3D_ACROSS_S15360_TP4 = ROPE3D_ACROSS_S15360.with_(
     name="rope3d_across_interleaved_s15360_h32_d128_tp4rank", num_heads_q=8, num_heads_k=8,
     num_heads_v=8, head_shards=4, seed=SEED_BASE + 90)
 
+# The SANA-WM camera branch on the same 2 x 18480-token grid (two CFG branches), 20 heads of 64.
+CAM_PREP_S18480 = CamWorkload(
+    name="cam_prep_b2_s18480_h20_d64", batch=2, ppf=20, pph=33, ppw=28, num_heads=20,
+    head_dim=64, seed=SEED_BASE + 100)
+
 WORKLOADS = {w.name: w for w in (TABLE_HALFSPLIT_T256, TABLE_INTERLEAVED_T4096,
                                  ROPE3D_ACROSS_S15360, ROPE3D_NEOX_FP8_S18480,
                                  ROPE3D_YARN_S122880, TABLE_INTERLEAVED_T32768,
                                  TABLE_INTERLEAVED_T32768_F16, TABLE_INTERLEAVED_T32768_E4M3,
-                                 ROPE3D_ACROSS_S15360_TP4)}
+                                 ROPE3D_ACROSS_S15360_TP4, CAM_PREP_S18480)}
 
 
 # --- drawing -----------------------------------------------------------------------------------
@@ -233,3 +274,40 @@ def rope3d_inputs(w: Rope3DWorkload) -> dict:
     return dict(qkv=qkv.view(w.batch, w.seq_len, w.row_elems),
                 q_weight=bf16_weights(w.seed + ROLE_WQ, w.num_heads_q * w.head_dim),
                 k_weight=bf16_weights(w.seed + ROLE_WK, w.num_heads_k * w.head_dim))
+
+
+def rigid_transforms(seed: int, count: int) -> torch.Tensor:
+    """count float32 4x4 matrices [[R, t], [0, 0, 0, 1]]: R from a normalised N(0,1)
+    quaternion, t = 0.5*N(0,1)^3 (drawn in float64)."""
+    rng = _rng(seed)
+    qt = rng.standard_normal((count, 4))
+    qt /= np.linalg.norm(qt, axis=1, keepdims=True)
+    w, x, y, z = qt.T
+    M = np.zeros((count, 4, 4))
+    M[:, 0, 0] = 1 - 2 * (y * y + z * z)
+    M[:, 0, 1] = 2 * (x * y - w * z)
+    M[:, 0, 2] = 2 * (x * z + w * y)
+    M[:, 1, 0] = 2 * (x * y + w * z)
+    M[:, 1, 1] = 1 - 2 * (x * x + z * z)
+    M[:, 1, 2] = 2 * (y * z - w * x)
+    M[:, 2, 0] = 2 * (x * z - w * y)
+    M[:, 2, 1] = 2 * (y * z + w * x)
+    M[:, 2, 2] = 1 - 2 * (x * x + y * y)
+    M[:, :3, 3] = 0.5 * rng.standard_normal((count, 3))
+    M[:, 3, 3] = 1.0
+    return torch.from_numpy(M.astype(np.float32))
+
+
+def cam_inputs(w: CamWorkload) -> dict:
+    """CPU tensors for a camera-prologue workload: q, k, v [B, N, H, D]; proj_q, proj_kv
+    [B, N, 4, 4] float32; rope_cos, rope_sin [N, D/2] float32."""
+    B, N, H, D, a = w.batch, w.num_tokens, w.num_heads, w.head_dim, w.act_dtype
+    shape = (B, N, H, D)
+    n = B * N * H * D
+    tab = rope_table(N, D, w.base, "f32")
+    return dict(q=bf16_normal(w.seed + ROLE_QKV, n, 1.0, a).view(shape),
+                k=bf16_normal(w.seed + ROLE_K, n, 1.0, a).view(shape),
+                v=bf16_normal(w.seed + ROLE_V, n, 1.0, a).view(shape),
+                proj_q=rigid_transforms(w.seed + ROLE_PQ, B * N).view(B, N, 4, 4),
+                proj_kv=rigid_transforms(w.seed + ROLE_PKV, B * N).view(B, N, 4, 4),
+                rope_cos=tab[:, :D // 2].contiguous(), rope_sin=tab[:, D // 2:].contiguous())

@@ -9,6 +9,13 @@ Match criteria (element by element against the fp64 oracle on the same seeded in
     One rounding to binary16 costs at most half an ulp (2^-11 relative for normal values); fp32
     arithmetic before it can move a value across one rounding boundary, hence one ulp (2^-10);
     the absolute term is the smallest normal binary16 (subnormal outputs have a fixed quantum).
+  * camera prologue outputs (16-bit): |gpu - ref| <= u * |ref| + 2^-16 * max|ref|, u = 2^-7
+    (bf16) or 2^-10 (binary16): one ulp of the output format as above, plus the fp32
+    accumulation of the 4-term projection and the rotation (a few 2^-24 of the largest
+    intermediate, bounded by the tensor's largest magnitude), so that tensors of small
+    magnitude (K after k_scale ~ 0.004) are held to the same relative standard; binary16 adds
+    its subnormal quantum 2^-24.
+  * inflation_sq (fp32): relative 2^-16 (fp32 sums of head_dim squares and one division).
 """
 from __future__ import annotations
 
@@ -120,3 +127,34 @@ def check_3d_outputs(w, outs, ref, tokens=None) -> None:
 def check_table_outputs(name, q_out, k_out, ref_q, ref_k) -> None:
     assert_bf16_close(q_out, ref_q, f"{name} q")
     assert_bf16_close(k_out, ref_k, f"{name} k")
+
+
+def assert_cam_close(gpu: torch.Tensor, ref: np.ndarray, what: str) -> None:
+    """Camera prologue 16-bit outputs against the oracle's fp64 values (criteria above)."""
+    g = to_f64(gpu).reshape(ref.shape)
+    rel = 2.0 ** -10 if gpu.dtype == torch.float16 else 2.0 ** -7
+    floor = 2.0 ** -16 * (np.abs(ref).max() if ref.size else 0.0)
+    if gpu.dtype == torch.float16:
+        floor += 2.0 ** -24
+    err = np.abs(g - ref)
+    bound = rel * np.abs(ref) + floor
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        idx = np.unravel_index(i, ref.shape)
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; first at {idx}: "
+            f"gpu={g[idx]!r} ref={ref[idx]!r} err={err[idx]:.3g} bound={bound[idx]:.3g}")
+
+
+def assert_inflation_close(gpu: torch.Tensor, ref: np.ndarray, what: str) -> None:
+    g = to_f64(gpu).reshape(ref.shape)
+    err = np.abs(g - ref)
+    bound = 2.0 ** -16 * np.abs(ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        idx = np.unravel_index(i, ref.shape)
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} values out of tolerance; first at {idx}: "
+            f"gpu={g[idx]!r} ref={ref[idx]!r}")

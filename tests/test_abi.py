@@ -66,6 +66,9 @@ def test_new_entry_points_reject_null_handle(lib):
                                    1, 1, 1, 64, 1e-6, 1e4, 1, 1.0, 0.0, 0.0, 1.0, 1, 0, 1.0, 1.0,
                                    None, None, None, None)
     assert rc == 1 and b"handle" in lib.qkrope_last_error()
+    rc = lib.qkrope_cam_prep(None, None, None, None, 0, None, None, None, None, 1.0, 1, 1, 1, 64,
+                             64, 64, 64, None, None, None, None, None)
+    assert rc == 1 and b"handle" in lib.qkrope_last_error()
 
 
 # --- the fused-vs-eager threshold (vLLM-Omni fused_qk_norm_rope_min_tokens rules) -------------

@@ -1,0 +1,223 @@
+"""GPU parity of the camera prologue (qkrope_cam_prep; vLLM-Omni "vllm_omni.diffusion.models.
+sana_wm.ucpe", cam_prep_func) against the fp64 oracle, through the C ABI.
+
+Shapes cover several 64-token tiles with a ragged tail, token counts that are and are not
+multiples of 8 (16-byte and element stores), one and two chunks per lane, chunk counts that
+do not fill a power-of-two lane group, uneven head groups, a single token, binary16, padded
+token strides, no inflation output, empty problems, argument errors, graph replay, and the
+full 2 x 18480-token SANA-WM shape on sampled tokens.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import assert_cam_close, assert_inflation_close
+
+pytestmark = pytest.mark.gpu
+
+qr = pytest.importorskip("qk_rmsnorm_rope_amd")
+from qk_rmsnorm_rope_amd import workloads as wl  # noqa: E402
+
+DEV = "cuda"
+
+
+def workload(B, N, H, D, act="bf16", seed=0):
+    return wl.CamWorkload(name=f"cam_b{B}_n{N}_h{H}_d{D}_{act}", batch=B, ppf=1, pph=1, ppw=N,
+                          num_heads=H, head_dim=D, seed=wl.SEED_BASE + 500 + seed, act_dtype=act)
+
+
+def gpu_inputs(inp):
+    return {k: v.to(DEV) for k, v in inp.items()}
+
+
+def run_gpu(g, k_scale, inflation=True):
+    B, N, H, D = g["q"].shape
+    outs = [torch.full((B, H, D, N), float("nan"), dtype=g["q"].dtype, device=DEV)
+            for _ in range(3)]
+    infl = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV) \
+        if inflation else None
+    qr.qkrope_cam_prep(g["q"], g["k"], g["v"], g["proj_q"], g["proj_kv"], g["rope_cos"],
+                       g["rope_sin"], k_scale, q_out=outs[0], k_out=outs[1], v_out=outs[2],
+                       inflation_sq=infl)
+    return outs, infl
+
+
+def check(name, outs, infl, ref):
+    for o, r, n in zip(outs, ref[:3], ("q", "k", "v")):
+        assert_cam_close(o, r, f"{name} {n}")
+    if infl is not None:
+        assert_inflation_close(infl, ref[3], f"{name} inflation_sq")
+
+
+CASES = [
+    # (B, N, H, D, act): what the case exercises
+    (2, 200, 5, 64, "bf16"),    # 4 tiles with an 8-token tail, 16-byte stores, groups of 3 + 2
+    (1, 130, 3, 128, "bf16"),   # N % 8 = 2: element stores; 1024-lane workgroups
+    (2, 64, 4, 256, "bf16"),    # two chunks per lane, exactly one tile
+    (1, 77, 2, 8, "bf16"),      # one lane per token
+    (1, 1, 1, 16, "bf16"),      # a single token
+    (3, 65, 7, 24, "bf16"),     # 3 chunks in 4-lane groups; a 1-token tail tile
+    (1, 100, 6, 200, "bf16"),   # 25 chunks: two per lane, 13 of 16 lanes busy
+    (2, 136, 4, 64, "f16"),     # binary16 activations and outputs
+    (1, 96, 9, 32, "bf16"),     # 9 heads in 3 groups of 3
+    (2, 18480 // 20, 20, 64, "bf16"),   # one frame of the SANA-WM grid, all 20 heads
+]
+
+
+@pytest.mark.parametrize("B,N,H,D,act", CASES)
+def test_cam_matches_oracle(B, N, H, D, act):
+    w = workload(B, N, H, D, act, seed=B * 1000 + N + H + D)
+    print(f"\ncam parity {w.name}", flush=True)
+    inp = wl.cam_inputs(w)
+    outs, infl = run_gpu(gpu_inputs(inp), w.k_scale)
+    torch.cuda.synchronize()
+    ref = oracle.cam_prep(inp["q"], inp["k"], inp["v"], inp["proj_q"], inp["proj_kv"],
+                          inp["rope_cos"], inp["rope_sin"], w.k_scale)
+    check(w.name, outs, infl, ref)
+
+
+def test_cam_hand_case_on_gpu():
+    """The oracle's hand-worked single-head case, padded to head_dim 8 with a second group of
+    four channels that the identity-like parts of the matrices leave alone."""
+    x = torch.tensor([1.0, -2.0, 3.0, 4.0, 0.5, 0.25, -1.0, 2.0], dtype=torch.bfloat16)
+    x = x.view(1, 1, 1, 8).to(DEV)
+    pq = torch.tensor([[0, 1, 0, 0], [0, 0, 1, 0], [0, 0, 0, 1], [1, 0, 0, 0]],
+                      dtype=torch.float32).view(1, 1, 4, 4).to(DEV)
+    pkv = torch.diag(torch.tensor([2.0, 1.0, 1.0, 1.0])).view(1, 1, 4, 4).to(DEV)
+    c = torch.tensor([[0.0, 1.0, 1.0, 1.0]], device=DEV)
+    s = torch.tensor([[1.0, 0.0, 0.0, 0.0]], device=DEV)
+    g = dict(q=x, k=x, v=x, proj_q=pq, proj_kv=pkv, rope_cos=c, rope_sin=s)
+    outs, infl = run_gpu(g, 0.5)
+    torch.cuda.synchronize()
+    assert outs[0].float().cpu().view(8)[:4].tolist() == [-3.0, 0.0, 4.0, 1.0]
+    assert outs[1].float().cpu().view(8)[:4].tolist() == [0.0, 1.0, 1.5, 2.0]
+    assert outs[2].float().cpu().view(8)[:4].tolist() == [2.0, 2.0, 3.0, 4.0]
+    # inflation over all 8 channels: second group of K: ReLU -> [0.5, 0.25, 0, 2] * 0.5,
+    # diag(2,1,1,1) doubles its first channel
+    a = 0.5 * np.array([1, 0, 3, 4, 0.5, 0.25, 0, 2.0])
+    p = a * np.array([2, 1, 1, 1, 2, 1, 1, 1.0])
+    assert infl.cpu().item() == pytest.approx((p @ p) / (a @ a), rel=2 ** -20)
+
+
+def test_cam_full_shape_sampled_tokens():
+    """The 2 x 18480-token, 20-head, head_dim-64 SANA-WM shape as bench.py runs it; the oracle
+    checks 300 sampled tokens (tile edges, the last tile, random ones) of both batches."""
+    w = wl.CAM_PREP_S18480
+    print(f"\ncam full shape {w.name}", flush=True)
+    inp = wl.cam_inputs(w)
+    g = gpu_inputs(inp)
+    outs, infl = run_gpu(g, w.k_scale)
+    torch.cuda.synchronize()
+    N = w.num_tokens
+    rng = np.random.default_rng(7)
+    edges = [0, 1, 63, 64, 65, 127, 128, N // 2, N - 65, N - 64, N - 48, N - 2, N - 1]
+    S = np.unique(np.concatenate([edges, rng.choice(N, 287, replace=False)]))
+    St = torch.as_tensor(S)
+    sub = dict(q=inp["q"][:, St], k=inp["k"][:, St], v=inp["v"][:, St],
+               proj_q=inp["proj_q"][:, St].contiguous(), proj_kv=inp["proj_kv"][:, St].contiguous(),
+               rope_cos=inp["rope_cos"][St].contiguous(), rope_sin=inp["rope_sin"][St].contiguous())
+    ref = oracle.cam_prep(sub["q"].contiguous(), sub["k"].contiguous(), sub["v"].contiguous(),
+                          sub["proj_q"], sub["proj_kv"], sub["rope_cos"], sub["rope_sin"],
+                          w.k_scale)
+    Sd = St.to(DEV)
+    check(w.name, [o[..., Sd] for o in outs], infl[..., Sd], ref)
+    assert all(torch.isfinite(o.float()).all().item() for o in outs)
+    assert torch.isfinite(infl).all().item()
+
+
+def test_cam_strided_rows_no_inflation_and_repeatability():
+    """Padded token strides give the same bits as dense rows; inflation_sq=None changes no
+    other output; two launches agree bit for bit."""
+    w = workload(2, 150, 3, 64, seed=31)
+    inp = gpu_inputs(wl.cam_inputs(w))
+    dense, infl = run_gpu(inp, w.k_scale)
+    B, N, H, D = inp["q"].shape
+    padded = dict(inp)
+    for name, extra in (("q", 8), ("k", 24), ("v", 64)):
+        buf = torch.zeros((B, N, H * D + extra), dtype=inp[name].dtype, device=DEV)
+        buf[:, :, :H * D] = inp[name].reshape(B, N, H * D)
+        padded[name] = buf[:, :, :H * D].view(B, N, H, D)
+    strided, _ = run_gpu(padded, w.k_scale, inflation=False)
+    again, infl2 = run_gpu(inp, w.k_scale)
+    torch.cuda.synchronize()
+    for a, b, c in zip(dense, strided, again):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert torch.equal(infl, infl2)
+
+
+@pytest.mark.parametrize("B,N,H", [(0, 10, 2), (2, 0, 2), (2, 10, 0)])
+def test_cam_empty_is_noop(B, N, H):
+    D = 64
+    x = torch.zeros((B, N, H, D), dtype=torch.bfloat16, device=DEV)
+    P = torch.zeros((B, N, 4, 4), dtype=torch.float32, device=DEV)
+    t = torch.zeros((N, D // 2), dtype=torch.float32, device=DEV)
+    outs = [torch.zeros((B, H, D, N), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    infl = torch.zeros((B, H, N), dtype=torch.float32, device=DEV)
+    qr.qkrope_cam_prep(x, x, x, P, P, t, t, 1.0, q_out=outs[0], k_out=outs[1], v_out=outs[2],
+                       inflation_sq=infl)
+    torch.cuda.synchronize()
+
+
+def test_cam_argument_errors():
+    h = qr._handle_for(torch.device(DEV))
+    L = qr.lib()
+    B, N, H, D = 1, 16, 2, 64
+    x = torch.zeros((B, N, H, D + 8), dtype=torch.bfloat16, device=DEV)
+    P = torch.zeros((B, N, 4, 4), dtype=torch.float32, device=DEV)
+    t = torch.zeros((N, 128), dtype=torch.float32, device=DEV)
+    o = torch.zeros((3, B * H * (D + 8) * N + 64), dtype=torch.bfloat16, device=DEV)
+    infl = torch.zeros(B * H * N, dtype=torch.float32, device=DEV)
+    s = 0
+
+    def call(D_, xs=None, q_out=None, act=qr.QKROPE_DTYPE_BF16, stride=H * (D + 8)):
+        xp = x.data_ptr() if xs is None else xs
+        return L.qkrope_cam_prep(h, xp, x.data_ptr(), x.data_ptr(), act, P.data_ptr(),
+                                 P.data_ptr(), t.data_ptr(), t.data_ptr(), 1.0, B, N, H, D_,
+                                 stride, stride, stride,
+                                 o[0].data_ptr() if q_out is None else q_out,
+                                 o[1].data_ptr(), o[2].data_ptr(), infl.data_ptr(), s)
+
+    assert call(64) == qr.QKROPE_OK
+    assert call(6) == qr.QKROPE_ERR_INVALID            # not a multiple of 4
+    assert call(12) == qr.QKROPE_ERR_UNSUPPORTED       # multiple of 4, not of 8
+    assert call(264, stride=H * 264) == qr.QKROPE_ERR_UNSUPPORTED   # beyond 256
+    assert call(64, act=qr.QKROPE_DTYPE_F32) == qr.QKROPE_ERR_INVALID
+    assert call(64, xs=x.data_ptr() + 2) == qr.QKROPE_ERR_UNSUPPORTED   # misaligned q
+    assert call(64, stride=H * 64 - 8) == qr.QKROPE_ERR_INVALID          # rows too short
+    assert call(64, q_out=x.data_ptr()) == qr.QKROPE_ERR_INVALID         # output over q
+    assert call(64, q_out=o[1].data_ptr() + 64) == qr.QKROPE_ERR_INVALID  # outputs overlap
+    torch.cuda.synchronize()
+
+
+def test_cam_graph_replay():
+    """Captured in a HIP graph and replayed three times, with eager work between the replays;
+    every replay matches the eager launch bit for bit."""
+    w = workload(2, 192, 4, 64, seed=41)
+    inp = gpu_inputs(wl.cam_inputs(w))
+    eager, einfl = run_gpu(inp, w.k_scale)
+    B, N, H, D = inp["q"].shape
+    outs = [torch.empty_like(e) for e in eager]
+    infl = torch.empty_like(einfl)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            qr.qkrope_cam_prep(inp["q"], inp["k"], inp["v"], inp["proj_q"], inp["proj_kv"],
+                               inp["rope_cos"], inp["rope_sin"], w.k_scale, q_out=outs[0],
+                               k_out=outs[1], v_out=outs[2], inflation_sq=infl)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        infl.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, outs):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(einfl, infl), f"replay {rep}"
