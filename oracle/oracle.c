@@ -46,7 +46,9 @@
  *       names these but leaves open how they compose; the readings taken here:
  *   - Q: ReLU, projection by proj_q, RoPE. K: ReLU, times k_scale, projection by proj_kv, RoPE.
  *     V: projection by proj_kv, RoPE (the K/V matrices are one transform shared by K and V).
- *     ReLU(x) = x if x > 0 else 0.
+ *     ReLU(x) = 0 if the sign bit of x is set, else x: max(x, 0) for every non-NaN x (also
+ *     -0 -> +0); the page does not say what a NaN becomes, and this reading keeps one whose
+ *     sign bit is clear and zeroes one whose sign bit is set.
  *   - A 4x4 matrix P acts on a head vector as D/4 independent groups of four consecutive
  *     channels: y[4g + i] = sum_j P[i][j] * x[4g + j], P stored row-major.
  *   - RoPE rotates the adjacent pairs (2i, 2i+1) of the projected vector by the angle whose
@@ -500,7 +502,7 @@ static double cam_head(const uint16_t *x, int act, int relu, double scale, const
     double na = 0.0, np_ = 0.0;
     for (int d = 0; d < D; ++d) {
         double v = act_decode(act, x[d]);
-        if (relu) v = v > 0.0 ? v : 0.0;
+        if (relu) v = signbit(v) ? 0.0 : v;
         a[d] = scale * v;
         na += a[d] * a[d];
     }
