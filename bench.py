@@ -39,11 +39,13 @@ DEFAULT_WORKLOAD = "rope3d_across_interleaved_s15360_h32_d128"
 KERNEL_SOURCES = ["qk_rmsnorm_rope_amd/csrc/qkrope_kernel_impl.h",
                   "qk_rmsnorm_rope_amd/csrc/qkrope_internal.h",
                   "qk_rmsnorm_rope_amd/csrc/qkrope_api.cpp"]
+CAM_SOURCES = ["qk_rmsnorm_rope_amd/csrc/qkrope_kernels_cam.hip"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(w=None) -> str:
+    """Hash of the sources that decide a workload's kernel and launch shape."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES + (CAM_SOURCES if w is not None and is_cam(w) else []):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -53,6 +55,20 @@ def is_3d(w) -> bool:
     return hasattr(w, "row_elems")
 
 
+def is_cam(w) -> bool:
+    return hasattr(w, "k_scale")
+
+
+def total_tokens(w) -> int:
+    """Tokens one step processes (the camera prologue's batch counts its tokens once each)."""
+    return w.batch * w.num_tokens if is_cam(w) else w.num_tokens
+
+
+def kernel_name(w) -> str:
+    """Name fragment of the step's dominant kernel in profiler output."""
+    return "qkrope_cam_kernel" if is_cam(w) else "qkrope_kernel"
+
+
 def is_sharded(w) -> bool:
     return is_3d(w) and w.head_shards > 1
 
@@ -60,7 +76,11 @@ def is_sharded(w) -> bool:
 def algorithmic_bytes(w) -> int:
     """Bytes the method itself must move per launch of the step's dominant kernel: inputs read
     once, outputs written once (for a head-sharded rank: the apply kernel, which also reads the
-    [T, 2] fp32 sums)."""
+    [T, 2] fp32 sums; for the camera prologue: Q, K, V in and out, the per-token 4x4 fp32
+    matrices, the [N, D/2] fp32 cos and sin tables once, inflation_sq out)."""
+    if is_cam(w):
+        BN, H, D = w.batch * w.num_tokens, w.num_heads, w.head_dim
+        return BN * (12 * H * D + 4 * H + 2 * 64) + w.num_tokens * 4 * D
     if is_3d(w):
         T = w.num_tokens
         out_b = 1 if w.output_fp8 else 2
@@ -76,6 +96,17 @@ def algorithmic_bytes(w) -> int:
     wts = 0 if w.norm_mode == "none" else 2 * D * 2
     out = qk // 2 if w.out_dtype == "e4m3" else qk
     return qk + tab + wts + out
+
+
+def output_bytes(w) -> int:
+    """The part of algorithmic_bytes(w) that is written."""
+    if is_cam(w):
+        BN, H, D = w.batch * w.num_tokens, w.num_heads, w.head_dim
+        return BN * (6 * H * D + 4 * H)
+    if is_3d(w):
+        return w.num_tokens * w.row_elems * (1 if w.output_fp8 else 2)
+    return w.num_tokens * (w.num_heads_q + w.num_heads_k) * w.head_dim * \
+        (1 if w.out_dtype == "e4m3" else 2)
 
 
 def sumsq_bytes(w) -> int:
@@ -94,7 +125,7 @@ def traffic_from_profile(w) -> dict | None:
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(w):
         return None
     return rec
 
@@ -110,7 +141,16 @@ def make_launcher(w, dev, sets):
     from qk_rmsnorm_rope_amd import workloads as wl
 
     calls = []
-    if is_sharded(w):
+    if is_cam(w):
+        cpu = wl.cam_inputs(w)
+        B, N, H, D = w.batch, w.num_tokens, w.num_heads, w.head_dim
+        for _ in range(sets):
+            g = {k: v.to(dev) for k, v in cpu.items()}
+            outs = [torch.empty((B, H, D, N), dtype=g["q"].dtype, device=dev) for _ in range(3)]
+            infl = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+            calls.append(qr.PreparedCam(g["q"], g["k"], g["v"], g["proj_q"], g["proj_kv"],
+                                        g["rope_cos"], g["rope_sin"], w.k_scale, *outs, infl))
+    elif is_sharded(w):
         # one rank: the all-reduce of the sums over the head group is the identity, so the
         # apply kernel reads the rank's own sums (same bytes and arithmetic as the reduced ones)
         cpu = wl.rope3d_inputs(w)
@@ -197,11 +237,19 @@ def cpu_baseline(w, cpu_inputs, budget_s: float = 12.0) -> dict:
     done, t_used, chunk = 0, 0.0, 64
     if is_3d(w):
         x = cpu_inputs["qkv"].reshape(-1, w.row_elems)
-    limit = w.num_tokens
+    limit = w.num_tokens                # per batch for the camera prologue (all batches run)
     while t_used < budget_s and done < limit:
         n = min(chunk, limit - done)
         t0 = time.perf_counter()
-        if is_3d(w):
+        if is_cam(w):
+            sl = slice(done, done + n)
+            outs = oracle.cam_prep(*(cpu_inputs[k][:, sl].contiguous() for k in
+                                     ("q", "k", "v", "proj_q", "proj_kv")),
+                                   cpu_inputs["rope_cos"][sl].contiguous(),
+                                   cpu_inputs["rope_sin"][sl].contiguous(), w.k_scale)
+            enc = oracle.f16_encode if w.act_dtype == "f16" else oracle.bf16_encode
+            enc(outs[0]), enc(outs[1]), enc(outs[2])
+        elif is_3d(w):
             if is_sharded(w):
                 oracle.sumsq_3d(x[done:done + n], num_heads_q=w.num_heads_q,
                                 num_heads_k=w.num_heads_k, num_heads_v=w.num_heads_v,
@@ -229,8 +277,10 @@ def cpu_baseline(w, cpu_inputs, budget_s: float = 12.0) -> dict:
         t_used += time.perf_counter() - t0
         done += n
         chunk = min(chunk * 2, 4096)
-    return {"value": done / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {done} of {limit} tokens of {w.name}, fp64 oracle incl. output "
+    nb = w.batch if is_cam(w) else 1
+    what = f"first {done} of {limit} tokens" + (f" of each of {nb} batches" if is_cam(w) else "")
+    return {"value": nb * done / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what} of {w.name}, fp64 oracle incl. output "
                       f"encoding, {t_used:.1f} s on {threads} OpenMP threads",
             "gbs": algorithmic_bytes(w) * done / limit / t_used / 1e9}
 
@@ -374,7 +424,7 @@ def main() -> int:
     traffic = traffic_from_profile(w)
     result = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak) for fused QK-RMSNorm+RoPE+V",
-        "value": w.num_tokens / (total / args.steps),
+        "value": total_tokens(w) / (total / args.steps),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -385,9 +435,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": w.num_tokens,
+        "config": {"workload": w.name, "tokens": total_tokens(w),
                    "io_dtype": getattr(w, "act_dtype", "bf16"),
-                   "heads": [w.num_heads_q, w.num_heads_k, getattr(w, "num_heads_v", 0)],
+                   "heads": ([w.num_heads] * 3 if is_cam(w) else
+                             [w.num_heads_q, w.num_heads_k, getattr(w, "num_heads_v", 0)]),
                    "head_dim": w.head_dim,
                    "parallelism": (f"one rank of {w.head_shards} head shards"
                                    if is_sharded(w) else "single-gpu"),

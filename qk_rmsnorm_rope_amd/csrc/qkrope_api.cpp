@@ -809,26 +809,24 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
     const int cpl = D / 8 > 16 ? 2 : 1;
     const int lanes = next_pow2((D / 8 + cpl - 1) / cpl);
     a.lanes_per_token = lanes;
-    a.lpt_shift = 0;
-    while ((1 << a.lpt_shift) < lanes) ++a.lpt_shift;
-    // Heads per workgroup: groups of at most 4, as even as possible. A group shares one load
-    // of each token's matrices and table row across its heads; more groups give more, shorter
-    // workgroups (20 heads: 5 groups of 4).
-    const int ngroups = (H + 3) / 4;
+    // Heads per workgroup: groups of at most kCamMaxHeads / cpl, as even as possible. A group
+    // shares its tokens' matrices and table values over 3 tensors x its heads; measured on
+    // MI355X (2 x 18480 tokens x 20 heads x 64), 2 heads per group beat 1, 3 and 4.
+    const int max_heads = std::max(1, kCamMaxHeads / cpl);
+    const int ngroups = (H + max_heads - 1) / max_heads;
     a.heads_per_group = (H + ngroups - 1) / ngroups;
     a.groups = (H + a.heads_per_group - 1) / a.heads_per_group;
     a.tiles = (int)((N + kCamTile - 1) / kCamTile);
-    const int64_t blocks = B * a.tiles * a.groups;
+    const int64_t blocks = B * a.tiles * (int64_t)a.groups;
     if (blocks >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "grid too large");
     a.xcd_group = xcd_group_for(blocks);
     a.vec_store = (N % 8 == 0) && aligned(q_out, 16) && aligned(k_out, 16) && aligned(v_out, 16);
     a.k_scale = k_scale;
-    const int threads = 64 * lanes;
     const int lds_bytes = 2 * kCamTile * D * 2;
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(QKROPE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(g.err));
-    const hipError_t e = launch_cam(a, act_dtype == QKROPE_DTYPE_F16 ? kActF16 : kActBF16, cpl, blocks,
-                                    threads, lds_bytes, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_cam(a, act_dtype == QKROPE_DTYPE_F16 ? kActF16 : kActBF16, cpl,
+                                    blocks, lds_bytes, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -7,27 +7,43 @@
 //   Q' = RoPE(P_q . ReLU(q)),  K' = RoPE(P_kv . (k_scale * ReLU(k))),  V' = RoPE(P_kv . v),
 // where P . x applies the token's 4x4 matrix to each group of four consecutive channels
 // (y[4g+i] = sum_j P[i][j] x[4g+j]) and RoPE rotates the adjacent pairs (2i, 2i+1) by +theta;
-// inflation_sq = |P_kv . k'|^2 / |k'|^2 for k' = k_scale * ReLU(k), 1 where k' = 0.
+// inflation_sq = |P_kv . k'|^2 / |k'|^2 for k' = k_scale * ReLU(k), 1 where k' = 0. ReLU keeps
+// x when its sign bit is clear and gives 0 otherwise (max(x, 0) for every non-NaN x).
 //
 // Work decomposition. The op streams 4 bytes per element (16-bit in, 16-bit out) for ~12 flops,
-// so it is HBM-bound; what costs is the layout change: a token's heads arrive as contiguous
+// and turns a token-major layout into a dim-major one: a token's heads arrive as contiguous
 // 16-byte chunks, but each output row (b, h, d) runs along the tokens. A workgroup owns one
-// batch, a tile of 64 consecutive tokens and a group of heads:
-//   * lane (token nl, chunk dl) loads its token's two 4x4 matrices and its four (cos, sin)
-//     pairs once, then for each head of the group and each of Q, K, V: one 16-byte load,
-//     ReLU / scale / projection / rotation in fp32 registers, round to 16 bits, and one 16-byte
-//     LDS write of the token's chunk (the next iteration's load is already in flight);
-//   * after a barrier, lane (row d, token segment s) gathers 8 consecutive tokens of dim d
-//     from LDS and writes them with one 16-byte non-temporal store: eight lanes cover a row's
-//     64-token run, so every store instruction writes whole 128-byte lines;
-//   * the LDS tile is double-buffered (one barrier per tensor) and its chunks are rotated by
-//     token/8, which makes the column reads of the 8 segments of a wave fall in distinct banks;
-//   * K's squared norms before and after the projection are summed over the token's lanes
-//     with DPP, giving inflation_sq without another pass.
+// batch, one tile of 64 consecutive tokens and a group of at most kCamMaxHeads heads, with Q,
+// K and V of each:
+//   * lane (token nl, chunk dl) loads its token's two 4x4 matrices and four (cos, sin) pairs
+//     per chunk once (the fp32 tables are twice the size of a bf16 head, so sharing them over
+//     the group's heads and tensors matters), then issues the 16-byte loads of all its chunks;
+//   * per head and tensor: ReLU (Q, K) on the packed 16-bit pairs (one integer max per two
+//     values), the K scale, the projection and the rotation in fp32, rounding to 16 bits, one
+//     16-byte LDS write of the chunk into the token's row of a [64 tokens][D] tile whose chunks
+//     are rotated by token/8 (so the column reads below hit distinct banks);
+//   * after a barrier, lane (row d, token segment s) gathers 8 consecutive tokens of dim d for
+//     one 16-byte store (issued after the last tensor): 8 lanes cover a row's 64-token run. The
+//     tile is double-buffered, one barrier per tensor;
+//   * K also sums the key's squared norms before and after the projection over the token's
+//     lanes with DPP, for inflation_sq.
+// Block order: token tiles fastest, so the workgroups that run together on one XCD write
+// adjacent runs of the same output rows (measured on MI355X: 20% faster than head groups
+// fastest), in XCD runs of 16 blocks.
 #include "qkrope_kernel_impl.h"
 
 namespace qkrope {
 namespace dev {
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// ReLU of two packed 16-bit floats (bf16 or binary16): a value whose sign bit is set is a
+// negative integer when read as int16, so an integer max with 0 zeroes exactly those.
+__device__ __forceinline__ uint32_t relu2(uint32_t u)
+{
+    const s16x2 v = __builtin_bit_cast(s16x2, u);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, s16x2{0, 0}));
+}
 
 // y = P . x on each group of four channels of an 8-element chunk.
 __device__ __forceinline__ void project8(const float P[16], const float x[8], float p[8])
@@ -43,11 +59,14 @@ __device__ __forceinline__ void project8(const float P[16], const float x[8], fl
         }
 }
 
-template <int ACT, int CPL>
-__global__ void __launch_bounds__(1024) qkrope_cam_kernel(const CamArgs a)
+// ACT: activation format. CPL: 16-byte chunks per lane per head (1 for head_dim <= 128, else
+// 2). LT: lanes per token (power of two >= head_dim / 8 / CPL); workgroups are 64 * LT lanes.
+template <int ACT, int CPL, int LT>
+__global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
 {
     extern __shared__ __align__(16) uint8_t s_tile[];   // 2 x [64 tokens][D] 16-bit values
-    const int tid = threadIdx.x, nth = blockDim.x;
+    const int tid = threadIdx.x;
+    constexpr int NTH = 64 * LT;
 
     uint32_t blk = blockIdx.x;
     if (a.xcd_group) {
@@ -57,21 +76,50 @@ __global__ void __launch_bounds__(1024) qkrope_cam_kernel(const CamArgs a)
             blk = (j / G) * S + x * G + j % G;
         }
     }
-    const uint32_t grp = blk % (uint32_t)a.groups;
-    const uint32_t bt = blk / (uint32_t)a.groups;
-    const uint32_t tile = bt % (uint32_t)a.tiles;
-    const uint32_t b = bt / (uint32_t)a.tiles;
+    const uint32_t tile = blk % (uint32_t)a.tiles;
+    const uint32_t bg = blk / (uint32_t)a.tiles;
+    const uint32_t grp = bg % (uint32_t)a.groups;
+    const uint32_t b = bg / (uint32_t)a.groups;
 
     const int D = a.head_dim, C = D >> 3, H = a.heads;
     const int64_t N = a.num_tokens;
     const int64_t n0 = (int64_t)tile * kCamTile;
     const int nvalid = (int)(N - n0 < kCamTile ? N - n0 : kCamTile);
-    const int LT = a.lanes_per_token;
-    const int nl = tid >> a.lpt_shift, dl = tid & (LT - 1);
+    const int nl = tid / LT, dl = tid % LT;
     const int nlc = nl < nvalid ? nl : nvalid - 1;          // loads stay inside the tile's tokens
     const int64_t bn = (int64_t)b * N + n0 + nlc;
+    const int h0 = (int)grp * a.heads_per_group;
+    const int nh = a.heads_per_group < H - h0 ? a.heads_per_group : H - h0;
+    const int iters = 3 * nh;
 
-    // the token's projections (normal loads: every head group of the tile re-reads them)
+    // data loads first (every address valid: iterations past the group's heads reload its last
+    // head, so the loads are unconditional and the compiler can wait for each one exactly)
+    constexpr int MH = kCamMaxHeads / CPL > 0 ? kCamMaxHeads / CPL : 1;
+    constexpr int MI = 3 * MH;
+    const uint8_t *wg_in[3];
+    uint32_t row_off[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        wg_in[r] = reinterpret_cast<const uint8_t *>(a.in[r] + ((int64_t)b * N + n0) * a.in_stride[r]);
+        row_off[r] = (uint32_t)(nlc * a.in_stride[r] * 2) + (uint32_t)(h0 * D * 2);
+    }
+    bool chv[CPL];
+    int chi[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = dl + c * LT;
+        chv[c] = ch < C;
+        chi[c] = chv[c] ? ch : 0;
+    }
+    uint4 v[MI][CPL];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        const int r = i % 3, hi = i / 3 < nh ? i / 3 : nh - 1;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            v[i][c] = ld16_stream<true>(wg_in[r], row_off[r] + (uint32_t)(hi * D * 2) + 16u * (uint32_t)chi[c]);
+    }
+    // the token's matrices and the chunk's table values (normal loads: re-read by other groups)
     float pq[16], pk[16];
     {
         const f32x4 *P = reinterpret_cast<const f32x4 *>(a.proj[0] + bn * 16);
@@ -83,145 +131,147 @@ __global__ void __launch_bounds__(1024) qkrope_cam_kernel(const CamArgs a)
             pk[4 * i] = w.x; pk[4 * i + 1] = w.y; pk[4 * i + 2] = w.z; pk[4 * i + 3] = w.w;
         }
     }
-    // the lane's chunks: pairs 4*ch .. 4*ch+3 of the token's table row
     float tc[CPL][4], ts[CPL][4];
-    bool chv[CPL];
-    uint32_t choff[CPL];     // byte offset of the chunk inside a head
     uint32_t ldsw[CPL];      // LDS byte offset of the chunk in the token's row (rotated)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const int ch = dl + c * LT;
-        chv[c] = ch < C;
-        const int chc = chv[c] ? ch : 0;
-        choff[c] = 16u * (uint32_t)chc;
-        ldsw[c] = (uint32_t)(nl * D * 2 + ((chc + (nl >> 3)) % C) * 16);
-        const f32x4 cv = *reinterpret_cast<const f32x4 *>(a.cos_table + (n0 + nlc) * (D / 2) + 4 * chc);
-        const f32x4 sv = *reinterpret_cast<const f32x4 *>(a.sin_table + (n0 + nlc) * (D / 2) + 4 * chc);
+        const f32x4 cv = *reinterpret_cast<const f32x4 *>(a.cos_table + (n0 + nlc) * (D / 2) + 4 * chi[c]);
+        const f32x4 sv = *reinterpret_cast<const f32x4 *>(a.sin_table + (n0 + nlc) * (D / 2) + 4 * chi[c]);
         tc[c][0] = cv.x; tc[c][1] = cv.y; tc[c][2] = cv.z; tc[c][3] = cv.w;
         ts[c][0] = sv.x; ts[c][1] = sv.y; ts[c][2] = sv.z; ts[c][3] = sv.w;
+        ldsw[c] = (uint32_t)(nl * D * 2 + ((chi[c] + (nl >> 3)) % C) * 16);
     }
-    // the lane's output units (row d, 8-token segment s) and their rotated LDS reads
+    // the lane's output units (row d, 8-token segment s), 8 * D of them, and their LDS reads
     int ud[CPL], us[CPL];
     uint32_t ldsr[CPL];
+    int64_t st_off[CPL];     // byte offset inside an output plane (b, h)
     bool uv[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int u = tid + j * nth;
+        const int u = tid + j * NTH;
         uv[j] = u < 8 * D;
         const int uu = uv[j] ? u : 0;
         us[j] = uu & 7;
         ud[j] = uu >> 3;
-        const int ch = ud[j] >> 3, e = ud[j] & 7;
-        ldsr[j] = (uint32_t)((us[j] * 8 * D + ((ch + us[j]) % C) * 8 + e) * 2);
+        ldsr[j] = (uint32_t)((us[j] * 8 * D + (((ud[j] >> 3) + us[j]) % C) * 8 + (ud[j] & 7)) * 2);
+        st_off[j] = (ud[j] * N + n0 + us[j] * 8) * 2;
     }
+    // whole tiles of a row-aligned output: 16-byte stores, issued after the loop (measured
+    // slightly faster than storing each tensor as it is gathered); partial tiles and unaligned
+    // rows store elements as they go
+    const bool fast = a.vec_store && nvalid == kCamTile;
+    uint4 o[MI][CPL];
 
-    const int h0 = (int)grp * a.heads_per_group;
-    const int nh = a.heads_per_group < H - h0 ? a.heads_per_group : H - h0;
-    const int iters = 3 * nh;
-    const uint8_t *wg_in[3];
-    uint32_t row_off[3];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-        wg_in[r] = reinterpret_cast<const uint8_t *>(a.in[r] + ((int64_t)b * N + n0) * a.in_stride[r]);
-        row_off[r] = (uint32_t)(nlc * a.in_stride[r] * 2);
-    }
-
-    auto load = [&](int it, uint4 v[CPL]) {
-        const int hi = it / 3, r = it - 3 * hi;
-        const uint8_t *base = sel3(r, wg_in[0], wg_in[1], wg_in[2]);
-        const uint32_t off = sel3(r, row_off[0], row_off[1], row_off[2]) +
-                             (uint32_t)((h0 + hi) * D * 2);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) v[c] = ld16_stream<true>(base, off + choff[c]);
-    };
-
-    uint4 cur[CPL];
-    load(0, cur);
-    for (int it = 0; it < iters; ++it) {
-        const int hi = it / 3, r = it - 3 * hi, h = h0 + hi;
-        uint4 nxt[CPL];
-        if (it + 1 < iters) load(it + 1, nxt);
-        uint8_t *buf = s_tile + (it & 1) * (kCamTile * D * 2);
+    for (int i = 0; i < MI; ++i) {
+        if (i >= iters) continue;          // uniform
+        const int r = i % 3, h = h0 + i / 3;
+        uint8_t *buf = s_tile + (i & 1) * (kCamTile * D * 2);
 
         float na = 0.0f, np = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
+            uint4 raw = v[i][c];
+            if (r < 2) raw = make_uint4(relu2(raw.x), relu2(raw.y), relu2(raw.z), relu2(raw.w));
             float x[8], p[8], y[8];
-            unpack8<ACT>(cur[c], x);
+            unpack8<ACT>(raw, x);
             if (r == 0) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = x[i] > 0.0f ? x[i] : 0.0f;
                 project8(pq, x, p);
             } else if (r == 1) {
+                // |ReLU(k)|^2 from the packed pairs (products of 16-bit values are exact in
+                // fp32); k_scale^2 is applied to the sum below
+                if (chv[c]) na = sumsq_packed<ACT>(raw, na);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = (x[i] > 0.0f ? x[i] : 0.0f) * a.k_scale;
+                for (int e = 0; e < 8; ++e) x[e] *= a.k_scale;
                 project8(pk, x, p);
                 if (chv[c]) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        na = __builtin_fmaf(x[i], x[i], na);
-                        np = __builtin_fmaf(p[i], p[i], np);
-                    }
+                    for (int e = 0; e < 8; ++e) np = __builtin_fmaf(p[e], p[e], np);
                 }
             } else {
                 project8(pk, x, p);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                y[2 * i] = __builtin_fmaf(p[2 * i], tc[c][i], -p[2 * i + 1] * ts[c][i]);
-                y[2 * i + 1] = __builtin_fmaf(p[2 * i + 1], tc[c][i], p[2 * i] * ts[c][i]);
+            for (int e = 0; e < 4; ++e) {
+                y[2 * e] = __builtin_fmaf(p[2 * e], tc[c][e], -p[2 * e + 1] * ts[c][e]);
+                y[2 * e + 1] = __builtin_fmaf(p[2 * e + 1], tc[c][e], p[2 * e] * ts[c][e]);
             }
             if (chv[c]) *reinterpret_cast<uint4 *>(buf + ldsw[c]) = pack8<ACT>(y);
         }
-        if (r == 1 && a.inflation) {
-            na = group_sum(na, LT);
+        if (r == 1 && a.inflation) {       // uniform
+            na = group_sum(na, LT) * (a.k_scale * a.k_scale);
             np = group_sum(np, LT);
             if (dl == 0 && nl < nvalid)
-                a.inflation[((int64_t)b * H + h) * N + n0 + nl] = na > 0.0f ? np / na : 1.0f;
+                a.inflation[((int64_t)b * H + h) * N + n0 + nl] = na > 0.0f ? np * __builtin_amdgcn_rcpf(na) : 1.0f;
         }
         __syncthreads();
 
-        uint16_t *out = sel3(r, a.out[0], a.out[1], a.out[2]);
+        uint16_t *out = a.out[r];
+        uint8_t *plane = reinterpret_cast<uint8_t *>(out + ((int64_t)b * H + h) * D * N);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             if (!uv[j]) continue;
             const uint16_t *src = reinterpret_cast<const uint16_t *>(buf + ldsr[j]);
-            uint16_t v[8];
+            uint16_t e8[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = src[k * D];
-            uint16_t *dst = out + (((int64_t)b * H + h) * D + ud[j]) * N + n0 + us[j] * 8;
-            if (a.vec_store && us[j] * 8 + 8 <= nvalid) {
-                const uint4 w = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
-                                           v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
-                st16_stream(reinterpret_cast<uint8_t *>(dst), w);
+            for (int k = 0; k < 8; ++k) e8[k] = src[k * D];
+            if (fast) {
+                const uint4 w = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16,
+                                           e8[4] | (uint32_t)e8[5] << 16, e8[6] | (uint32_t)e8[7] << 16);
+                o[i][j] = w;
             } else {
+                uint16_t *dst = reinterpret_cast<uint16_t *>(plane) + ud[j] * N + n0 + us[j] * 8;
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
-                    if (us[j] * 8 + k < nvalid) dst[k] = v[k];
+                    if (us[j] * 8 + k < nvalid) dst[k] = e8[k];
             }
         }
+    }
+    if (fast) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) cur[c] = nxt[c];
+        for (int i = 0; i < MI; ++i) {
+            if (i >= iters) continue;
+            const int r = i % 3, h = h0 + i / 3;
+            uint8_t *plane = reinterpret_cast<uint8_t *>(a.out[r] + ((int64_t)b * H + h) * D * N);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j)
+                if (uv[j]) *reinterpret_cast<uint4 *>(plane + st_off[j]) = o[i][j];
+        }
+    }
+}
+
+template <int ACT, int CPL, int LT>
+hipError_t go_cam(const CamArgs &a, int64_t blocks, int lds_bytes, hipStream_t st)
+{
+    hipLaunchKernelGGL((qkrope_cam_kernel<ACT, CPL, LT>), dim3((unsigned)blocks), dim3(64 * LT),
+                       lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_cam_act(const CamArgs &a, int cpl, int64_t blocks, int lds_bytes, hipStream_t st)
+{
+    const int lt = a.lanes_per_token;
+    if (cpl == 2) return lt == 16 ? go_cam<ACT, 2, 16>(a, blocks, lds_bytes, st) : hipErrorInvalidValue;
+    if (cpl != 1) return hipErrorInvalidValue;
+    switch (lt) {
+    case 1: return go_cam<ACT, 1, 1>(a, blocks, lds_bytes, st);
+    case 2: return go_cam<ACT, 1, 2>(a, blocks, lds_bytes, st);
+    case 4: return go_cam<ACT, 1, 4>(a, blocks, lds_bytes, st);
+    case 8: return go_cam<ACT, 1, 8>(a, blocks, lds_bytes, st);
+    case 16: return go_cam<ACT, 1, 16>(a, blocks, lds_bytes, st);
+    default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace dev
 
-hipError_t launch_cam(const CamArgs &a, int act, int cpl, int64_t blocks, int threads,
-                      int lds_bytes, hipStream_t st)
+hipError_t launch_cam(const CamArgs &a, int act, int cpl, int64_t blocks, int lds_bytes,
+                      hipStream_t st)
 {
-    const dim3 grid((unsigned)blocks), block((unsigned)threads);
-    if (act == kActBF16 && cpl == 1)
-        hipLaunchKernelGGL((dev::qkrope_cam_kernel<kActBF16, 1>), grid, block, lds_bytes, st, a);
-    else if (act == kActBF16 && cpl == 2)
-        hipLaunchKernelGGL((dev::qkrope_cam_kernel<kActBF16, 2>), grid, block, lds_bytes, st, a);
-    else if (act == kActF16 && cpl == 1)
-        hipLaunchKernelGGL((dev::qkrope_cam_kernel<kActF16, 1>), grid, block, lds_bytes, st, a);
-    else if (act == kActF16 && cpl == 2)
-        hipLaunchKernelGGL((dev::qkrope_cam_kernel<kActF16, 2>), grid, block, lds_bytes, st, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (act == kActBF16) return dev::launch_cam_act<kActBF16>(a, cpl, blocks, lds_bytes, st);
+    if (act == kActF16) return dev::launch_cam_act<kActF16>(a, cpl, blocks, lds_bytes, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace qkrope
