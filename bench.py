@@ -36,16 +36,19 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 DEFAULT_WORKLOAD = "rope3d_across_interleaved_s15360_h32_d128"
-KERNEL_SOURCES = ["qk_rmsnorm_rope_amd/csrc/qkrope_kernel_impl.h",
-                  "qk_rmsnorm_rope_amd/csrc/qkrope_internal.h",
-                  "qk_rmsnorm_rope_amd/csrc/qkrope_api.cpp"]
-CAM_SOURCES = ["qk_rmsnorm_rope_amd/csrc/qkrope_kernels_cam.hip"]
+_CSRC = "qk_rmsnorm_rope_amd/csrc/"
+COMMON_SOURCES = [_CSRC + "qkrope_kernel_impl.h", _CSRC + "qkrope_internal.h",
+                  _CSRC + "qkrope_host.h"]
+PROLOGUE_SOURCES = [_CSRC + "qkrope_api.cpp"]
+CAM_SOURCES = [_CSRC + "qkrope_cam.h", _CSRC + "qkrope_api_cam.cpp",
+               _CSRC + "qkrope_kernels_cam.hip"]
 
 
 def kernel_source_hash(w=None) -> str:
     """Hash of the sources that decide a workload's kernel and launch shape."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES + (CAM_SOURCES if w is not None and is_cam(w) else []):
+    cam = w is not None and is_cam(w)
+    for rel in COMMON_SOURCES + (CAM_SOURCES if cam else PROLOGUE_SOURCES):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

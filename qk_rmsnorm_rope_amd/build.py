@@ -23,7 +23,8 @@ SOURCES = ["qkrope_kernels_3d_d64.hip", "qkrope_kernels_3d_d128.hip", "qkrope_ke
            "qkrope_kernels_table_interleaved_bf16.hip", "qkrope_kernels_table_halfsplit_bf16.hip",
            "qkrope_kernels_table_interleaved_f16.hip", "qkrope_kernels_table_halfsplit_f16.hip",
            "qkrope_kernels_table_halfsplit_any_bf16.hip", "qkrope_kernels_table_halfsplit_any_f16.hip",
-           "qkrope_kernels_sumsq.hip", "qkrope_kernels_cam.hip", "qkrope_api.cpp"]
+           "qkrope_kernels_sumsq.hip", "qkrope_kernels_cam.hip", "qkrope_api.cpp",
+           "qkrope_api_cam.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

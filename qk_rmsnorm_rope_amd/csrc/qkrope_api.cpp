@@ -16,18 +16,14 @@
 #include <string>
 
 #include "qkrope_internal.h"
+#include "qkrope_host.h"
 
-struct qkrope_ctx {
-    int device;
-    int num_cus;
-    char arch[64];
-};
+namespace qkrope {
+namespace host {
 
 namespace {
-
-using namespace qkrope;
-
 thread_local std::string g_last_error;
+}
 
 int fail(int status, const char *fmt, ...)
 {
@@ -46,45 +42,15 @@ int ok()
     return QKROPE_OK;
 }
 
-bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+const char *last_error() { return g_last_error.c_str(); }
 
-// Bytes touched by a strided [tokens, span] tensor: rows of `span` elements every `stride`.
-struct Range {
-    uintptr_t lo, hi;          // bounding interval [lo, hi)
-    int64_t stride_b, span_b;  // row stride and row length in bytes
-};
+}  // namespace host
+}  // namespace qkrope
 
-Range span_of(const void *p, int64_t tokens, int64_t stride, int64_t span, int64_t esize)
-{
-    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    if (tokens <= 0 || span <= 0) return {lo, lo, 0, 0};
-    return {lo, lo + (uintptr_t)(((tokens - 1) * stride + span) * esize), stride * esize,
-            span * esize};
-}
+namespace {
 
-// Whether two strided tensors share a byte. Exact when both have the same row stride (rows of
-// one sit in a gap of the other's period, as for column slices of one packed buffer);
-// otherwise the bounding intervals decide.
-bool overlap(Range a, Range b)
-{
-    if (a.lo == a.hi || b.lo == b.hi) return false;
-    if (!(a.lo < b.hi && b.lo < a.hi)) return false;
-    if (a.stride_b == b.stride_b && a.stride_b > 0 && a.span_b <= a.stride_b &&
-        b.span_b <= b.stride_b) {
-        const int64_t period = a.stride_b;
-        const int64_t diff = (int64_t)(b.lo - a.lo);
-        const int64_t d = ((diff % period) + period) % period;  // b's row start in a's period
-        if (d >= a.span_b && d + b.span_b <= period) return false;
-    }
-    return true;
-}
-
-int next_pow2(int v)
-{
-    int p = 1;
-    while (p < v) p <<= 1;
-    return p;
-}
+using namespace qkrope;
+using namespace qkrope::host;
 
 // Workgroup size and slot layout for a token whose regions hold n[r] lane-units (16-byte
 // chunks) each. Region-major gives every region `slots` slots per lane (compiled 1..4); mixed
@@ -193,25 +159,6 @@ hipError_t launch(const KernelKey &k, const LaunchShape &s, const KernelArgs &a,
     default: return hipErrorInvalidValue;
     }
 }
-
-// Device guard: make h->device current for the launch and restore the caller's device after.
-struct DeviceGuard {
-    int prev = -1;
-    bool switched = false;
-    hipError_t err = hipSuccess;
-    explicit DeviceGuard(int dev)
-    {
-        err = hipGetDevice(&prev);
-        if (err == hipSuccess && prev != dev) {
-            err = hipSetDevice(dev);
-            switched = err == hipSuccess;
-        }
-    }
-    ~DeviceGuard()
-    {
-        if (switched) (void)hipSetDevice(prev);
-    }
-};
 
 int do_launch(qkrope_handle h, const KernelKey &key, const LaunchShape &shape,
               const KernelArgs &args, void *stream)
@@ -569,7 +516,7 @@ const char *qkrope_status_str(int status)
     }
 }
 
-const char *qkrope_last_error(void) { return g_last_error.c_str(); }
+const char *qkrope_last_error(void) { return qkrope::host::last_error(); }
 
 int qkrope_min_tokens(int64_t default_tokens, int64_t *out)
 {
@@ -735,98 +682,6 @@ int qkrope_sumsq_3d(qkrope_handle h, const void *qkv, int64_t num_tokens, int nu
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(QKROPE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(g.err));
     const hipError_t e = launch_sumsq(a, T, threads, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
-}
-
-int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v, int act_dtype,
-                    const float *proj_q, const float *proj_kv, const float *rope_cos,
-                    const float *rope_sin, float k_scale, int64_t batch, int64_t num_tokens,
-                    int num_heads, int head_dim, int64_t q_stride, int64_t k_stride,
-                    int64_t v_stride, void *q_out, void *k_out, void *v_out,
-                    float *inflation_sq, void *stream)
-{
-    if (!h) return fail(QKROPE_ERR_INVALID, "handle is NULL");
-    const int64_t B = batch, N = num_tokens;
-    const int H = num_heads, D = head_dim;
-    if (B < 0 || N < 0 || H < 0 || D <= 0)
-        return fail(QKROPE_ERR_INVALID, "negative size or non-positive head_dim");
-    if (D % 4) return fail(QKROPE_ERR_INVALID, "head_dim must be a multiple of 4 (4x4 projection groups)");
-    if (act_dtype != QKROPE_DTYPE_BF16 && act_dtype != QKROPE_DTYPE_F16)
-        return fail(QKROPE_ERR_INVALID, "act_dtype must be QKROPE_DTYPE_BF16 or QKROPE_DTYPE_F16");
-    if (D % 8 || D > 256) return fail(QKROPE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and <= 256");
-    if (N >= (int64_t(1) << 31) || B >= (int64_t(1) << 31) || B * N >= (int64_t(1) << 31))
-        return fail(QKROPE_ERR_UNSUPPORTED, "batch * num_tokens must be < 2^31");
-    const int64_t strides[3] = {q_stride, k_stride, v_stride};
-    for (int r = 0; r < 3; ++r) {
-        if (strides[r] < (int64_t)H * D) return fail(QKROPE_ERR_INVALID, "token stride smaller than num_heads * head_dim");
-        if (strides[r] % 8 || strides[r] >= (int64_t(1) << 24))
-            return fail(QKROPE_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements and < 2^24");
-    }
-    if (B * N == 0 || H == 0) return ok();
-    const void *ins[3] = {q, k, v};
-    void *outs[3] = {q_out, k_out, v_out};
-    if (!q || !k || !v || !proj_q || !proj_kv || !rope_cos || !rope_sin || !q_out || !k_out || !v_out)
-        return fail(QKROPE_ERR_INVALID, "a required pointer is NULL");
-    for (int r = 0; r < 3; ++r) {
-        if (!aligned(ins[r], 16)) return fail(QKROPE_ERR_UNSUPPORTED, "q, k, v must be 16-byte aligned");
-        if (!aligned(outs[r], 2)) return fail(QKROPE_ERR_INVALID, "outputs must be 2-byte aligned");
-    }
-    if (!aligned(proj_q, 16) || !aligned(proj_kv, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16))
-        return fail(QKROPE_ERR_UNSUPPORTED, "projections and tables must be 16-byte aligned");
-    if (inflation_sq && !aligned(inflation_sq, 4)) return fail(QKROPE_ERR_INVALID, "inflation_sq must be 4-byte aligned");
-    // outputs must not overlap an input or one another (bounding intervals)
-    const int64_t out_elems = B * H * (int64_t)D * N;
-    Range ro[4] = {span_of(q_out, 1, out_elems, out_elems, 2), span_of(k_out, 1, out_elems, out_elems, 2),
-                   span_of(v_out, 1, out_elems, out_elems, 2),
-                   span_of(inflation_sq, inflation_sq ? 1 : 0, B * H * N, B * H * N, 4)};
-    Range ri[7] = {span_of(q, B * N, q_stride, (int64_t)H * D, 2), span_of(k, B * N, k_stride, (int64_t)H * D, 2),
-                   span_of(v, B * N, v_stride, (int64_t)H * D, 2), span_of(proj_q, 1, B * N * 16, B * N * 16, 4),
-                   span_of(proj_kv, 1, B * N * 16, B * N * 16, 4), span_of(rope_cos, 1, N * D / 2, N * D / 2, 4),
-                   span_of(rope_sin, 1, N * D / 2, N * D / 2, 4)};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 7; ++j)
-            if (overlap(ro[i], ri[j])) return fail(QKROPE_ERR_INVALID, "an output overlaps an input");
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(ro[i], ro[j])) return fail(QKROPE_ERR_INVALID, "outputs overlap");
-    }
-
-    CamArgs a;
-    for (int r = 0; r < 3; ++r) {
-        a.in[r] = static_cast<const uint16_t *>(ins[r]);
-        a.in_stride[r] = strides[r];
-        a.out[r] = static_cast<uint16_t *>(outs[r]);
-    }
-    a.proj[0] = proj_q;
-    a.proj[1] = proj_kv;
-    a.cos_table = rope_cos;
-    a.sin_table = rope_sin;
-    a.inflation = inflation_sq;
-    a.num_tokens = N;
-    a.batch = (int)B;
-    a.heads = H;
-    a.head_dim = D;
-    const int cpl = D / 8 > 16 ? 2 : 1;
-    const int lanes = next_pow2((D / 8 + cpl - 1) / cpl);
-    a.lanes_per_token = lanes;
-    // Heads per workgroup: groups of at most kCamMaxHeads / cpl, as even as possible. A group
-    // shares its tokens' matrices and table values over 3 tensors x its heads; measured on
-    // MI355X (2 x 18480 tokens x 20 heads x 64), 2 heads per group beat 1, 3 and 4.
-    const int max_heads = std::max(1, kCamMaxHeads / cpl);
-    const int ngroups = (H + max_heads - 1) / max_heads;
-    a.heads_per_group = (H + ngroups - 1) / ngroups;
-    a.groups = (H + a.heads_per_group - 1) / a.heads_per_group;
-    a.tiles = (int)((N + kCamTile - 1) / kCamTile);
-    const int64_t blocks = B * a.tiles * (int64_t)a.groups;
-    if (blocks >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "grid too large");
-    a.xcd_group = xcd_group_for(blocks);
-    a.vec_store = (N % 8 == 0) && aligned(q_out, 16) && aligned(k_out, 16) && aligned(v_out, 16);
-    a.k_scale = k_scale;
-    const int lds_bytes = 2 * kCamTile * D * 2;
-    DeviceGuard g(h->device);
-    if (g.err != hipSuccess) return fail(QKROPE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(g.err));
-    const hipError_t e = launch_cam(a, act_dtype == QKROPE_DTYPE_F16 ? kActF16 : kActBF16, cpl,
-                                    blocks, lds_bytes, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

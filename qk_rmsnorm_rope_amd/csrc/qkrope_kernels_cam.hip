@@ -29,8 +29,11 @@
 //     lanes with DPP, for inflation_sq.
 // Block order: token tiles fastest, so the workgroups that run together on one XCD write
 // adjacent runs of the same output rows (measured on MI355X: 20% faster than head groups
-// fastest), in XCD runs of 16 blocks.
+// fastest); each (batch, head group) has its tiles padded to a multiple of 8 and XCD x takes
+// the x-th contiguous eighth of them, so the tokens' matrices and table rows, re-read by every
+// head group, come from that XCD's L2.
 #include "qkrope_kernel_impl.h"
+#include "qkrope_cam.h"
 
 namespace qkrope {
 namespace dev {
@@ -69,15 +72,13 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
     constexpr int NTH = 64 * LT;
 
     uint32_t blk = blockIdx.x;
-    if (a.xcd_group) {
-        const uint32_t G = a.xcd_group, S = 8u * G, full = gridDim.x / S * S;
-        if (blk < full) {
-            const uint32_t j = blk >> 3, x = blk & 7u;
-            blk = (j / G) * S + x * G + j % G;
-        }
+    if (a.xcd_group) {       // the grid is a whole number of 8*G runs: every block is remapped
+        const uint32_t G = a.xcd_group, j = blk >> 3, x = blk & 7u;
+        blk = (j / G) * (8u * G) + x * G + j % G;
     }
-    const uint32_t tile = blk % (uint32_t)a.tiles;
-    const uint32_t bg = blk / (uint32_t)a.tiles;
+    const uint32_t tile = blk % (uint32_t)a.tiles_padded;
+    if (tile >= (uint32_t)a.tiles) return;           // padding: no work (uniform)
+    const uint32_t bg = blk / (uint32_t)a.tiles_padded;
     const uint32_t grp = bg % (uint32_t)a.groups;
     const uint32_t b = bg / (uint32_t)a.groups;
 
