@@ -20,6 +20,9 @@ Other modes (used to produce the committed profiles):
                         fused-vs-eager threshold of vLLM-Omni's fused_qk_norm_rope_min_tokens)
     --stream            launch each step on the stream from the host instead of replaying the
                         timed steps as one HIP graph (the default)
+    --cold              rotate enough input/output buffer sets that they total at least 512 MB
+                        (twice the 256 MB memory-side cache), so no launch finds its data cached;
+                        the default three sets already exceed that for the large workloads
 """
 from __future__ import annotations
 
@@ -35,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+COLD_BYTES = 512 << 20         # --cold: rotating buffer sets total at least twice the MALL
 DEFAULT_WORKLOAD = "rope3d_across_interleaved_s15360_h32_d128"
 _CSRC = "qk_rmsnorm_rope_amd/csrc/"
 COMMON_SOURCES = [_CSRC + "qkrope_kernel_impl.h", _CSRC + "qkrope_internal.h",
@@ -230,6 +234,18 @@ def time_graph(launch, steps, warmup):
     return wall, start.elapsed_time(end) * 1e-3 / steps
 
 
+def host_cpu() -> str:
+    """The host CPU's model name (Linux), or "unknown CPU"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(w, cpu_inputs, budget_s: float = 12.0) -> dict:
     """The fp64 oracle, as it stands, on the same workload's tokens in order (output encoding
     included, starting again from the first token after the last), on every host core OpenMP
@@ -290,7 +306,8 @@ def cpu_baseline(w, cpu_inputs, budget_s: float = 12.0) -> dict:
             + (f" of each of {nb} batches" if is_cam(w) else "") + ")")
     return {"value": nb * total / t_used, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{what} of {w.name}, fp64 oracle incl. output "
-                      f"encoding, {t_used:.1f} s on {threads} OpenMP threads",
+                      f"encoding, {t_used:.1f} s on {threads} OpenMP threads "
+                      f"({host_cpu()}, {os.cpu_count()} logical CPUs)",
             "gbs": algorithmic_bytes(w) * total / limit / t_used / 1e9}
 
 
@@ -385,6 +402,7 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--crossover", action="store_true")
     ap.add_argument("--stream", action="store_true")
+    ap.add_argument("--cold", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -403,6 +421,9 @@ def main() -> int:
         crossover(dev, args.warmup)
         return 0
     w = wl.WORKLOADS[args.workload]
+    if args.cold:
+        per_set = algorithmic_bytes(w)
+        args.sets = max(args.sets, -(-COLD_BYTES // per_set))
     use_graph = not args.stream
     if use_graph:
         # launchers bind the stream they are prepared on: prepare them on the capture stream
