@@ -155,6 +155,16 @@ def _stream(device, stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _same_device(device: torch.device, **tensors) -> None:
+    """Every given tensor (None skipped) must be a GPU tensor on `device`: the library reads and
+    writes through the raw pointers, so a host tensor or another GPU's must be refused here."""
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != device):
+            raise ValueError(f"{name} must be a GPU tensor on {device}, got {t.device}")
+
+
 def _rows(t: torch.Tensor, heads: int, head_dim: int, name: str) -> int:
     """Token stride (elements) of a [T, H, D] (or [T, H*D]) view with contiguous heads/dims."""
     if t.dim() == 3:
@@ -197,6 +207,9 @@ def qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, *, q_out, k_out,
     for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
         if norm_mode != "none" and (w is None or w.dtype != torch.bfloat16 or not w.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    wq, wk = (q_weight, k_weight) if norm_mode != "none" else (None, None)
+    _same_device(q.device, k=k, q_out=q_out, k_out=k_out, rope_table=rope_table, q_weight=wq,
+                 k_weight=wk)
     s = lib().qkrope_run_table(
         _handle_for(q.device), _ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight), _ptr(rope_table),
         tdt, float(eps), T, Hq, Hk, D, R, int(bool(interleaved)), NORM_MODES[norm_mode],
@@ -248,6 +261,9 @@ def qkrope_run_table_ex(q, k, q_weight, k_weight, cos_table, sin_table, eps, *, 
     for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
         if norm_mode != "none" and (w is None or w.dtype != q.dtype or not w.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous tensor of q's dtype")
+    wq, wk = (q_weight, k_weight) if norm_mode != "none" else (None, None)
+    _same_device(q.device, k=k, q_out=q_out, k_out=k_out, cos_table=cos_table,
+                 sin_table=sin_table, q_weight=wq, k_weight=wk)
     s = lib().qkrope_run_table_ex(
         _handle_for(q.device), _ptr(q), _ptr(k), _ptr(q_weight), _ptr(k_weight),
         _ptr(cos_table), _ptr(sin_table), tdt, act, out, float(out_scale), float(eps), T, Hq, Hk,
@@ -270,6 +286,7 @@ def qkrope_sumsq_3d(qkv, *, num_heads_q, num_heads_k, num_heads_v, head_dim, out
         out = torch.empty((T, 2), dtype=torch.float32, device=qkv.device)
     if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != 2 * T:
         raise ValueError("out must be a contiguous float32 [tokens, 2] tensor")
+    _same_device(qkv.device, out=out)
     s = lib().qkrope_sumsq_3d(_handle_for(qkv.device), _ptr(qkv), T, num_heads_q, num_heads_k,
                               num_heads_v, head_dim, _ptr(out), _stream(qkv.device, stream))
     _check(s, "qkrope_sumsq_3d")
@@ -300,10 +317,14 @@ def qkrope_run_3d_sharded(qkv, q_weight, k_weight, *, token_offset=0, sumsq=None
     if sumsq is not None and (sumsq.dtype != torch.float32 or not sumsq.is_contiguous() or
                               sumsq.numel() != 2 * T or not sumsq.is_cuda):
         raise ValueError("sumsq must be a contiguous float32 GPU tensor [tokens, 2]")
+    _same_device(qkv.device, sumsq=sumsq)
     if is_qk_norm:
         for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
             if w is None or w.dtype != torch.bfloat16 or not w.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    _same_device(qkv.device, q_out=q_out, k_out=k_out, v_out=v_out,
+                 q_weight=q_weight if is_qk_norm else None,
+                 k_weight=k_weight if is_qk_norm else None)
     s = lib().qkrope_run_3d_sharded(
         _handle_for(qkv.device), _ptr(qkv), _ptr(q_weight) if is_qk_norm else None,
         _ptr(k_weight) if is_qk_norm else None, T, int(token_offset), _ptr(sumsq),
@@ -338,6 +359,9 @@ def qkrope_run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
         for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
             if w is None or w.dtype != torch.bfloat16 or not w.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    _same_device(qkv.device, q_out=q_out, k_out=k_out, v_out=v_out,
+                 q_weight=q_weight if is_qk_norm else None,
+                 k_weight=k_weight if is_qk_norm else None)
     s = lib().qkrope_run_3d(
         _handle_for(qkv.device), _ptr(qkv), _ptr(q_weight) if is_qk_norm else None,
         _ptr(k_weight) if is_qk_norm else None, T, ppf, pph, ppw, num_frame_channels,
@@ -570,6 +594,9 @@ def qkrope_cam_prep(q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, *, q_
         if t.dtype != q.dtype or tuple(t.shape) != (B, H, D, N) or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous [batch, heads, head_dim, tokens] tensor "
                              "of the activation dtype")
+    _same_device(q.device, k=k, v=v, proj_q=proj_q, proj_kv=proj_kv, rope_cos=rope_cos,
+                 rope_sin=rope_sin, q_out=q_out, k_out=k_out, v_out=v_out,
+                 inflation_sq=inflation_sq)
     if inflation_sq is not None and (inflation_sq.dtype != torch.float32 or
                                      tuple(inflation_sq.shape) != (B, H, N) or
                                      not inflation_sq.is_contiguous()):

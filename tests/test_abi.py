@@ -103,3 +103,15 @@ def test_min_tokens_resolved_at_call_time(monkeypatch):
     assert qr.qkrope_min_tokens(2048) == 2048
     with pytest.raises(ValueError):
         qr.qkrope_min_tokens(-1)
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """The library dereferences raw device pointers, so the binding must refuse host tensors."""
+    import torch
+    import qk_rmsnorm_rope_amd as qr
+    x = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    P = torch.zeros(1, 8, 4, 4)
+    t = torch.zeros(8, 32)
+    o = [torch.zeros(1, 2, 64, 8, dtype=torch.bfloat16) for _ in range(3)]
+    with pytest.raises(ValueError, match="GPU"):
+        qr.qkrope_cam_prep(x, x, x, P, P, t, t, 1.0, q_out=o[0], k_out=o[1], v_out=o[2])

@@ -417,3 +417,35 @@ def test_graph_capture_and_replay():
         torch.cuda.synchronize()
         for t, r in zip((*o3, qo, ko), ref):
             assert torch.equal(t, r), f"replay {rep}"
+
+
+def test_host_tensor_arguments_are_refused():
+    """A host tensor among GPU ones (weights, tables, outputs, matrices) raises before launch."""
+    wt = wl.TABLE_INTERLEAVED_T4096.with_(num_tokens=64)
+    ti = wl.table_inputs(wt)
+    g = {k: _gpu(v) for k, v in ti.items()}
+    qo, ko = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+    with pytest.raises(ValueError, match="GPU"):
+        qr.qkrope_run_table(g["q"], g["k"], ti["q_weight"], g["k_weight"], g["rope_table"],
+                            wt.eps, q_out=qo, k_out=ko, interleaved=True)
+    with pytest.raises(ValueError, match="GPU"):
+        qr.qkrope_run_table(g["q"], g["k"], g["q_weight"], g["k_weight"], g["rope_table"],
+                            wt.eps, q_out=qo, k_out=ko.cpu(), interleaved=True)
+    w3 = wl.ROPE3D_ACROSS_S15360.with_(ppf=1, pph=1, ppw=8)
+    i3 = wl.rope3d_inputs(w3)
+    outs = [torch.empty((w3.num_tokens, 32, 128), dtype=torch.bfloat16, device=DEV)
+            for _ in range(3)]
+    with pytest.raises(ValueError, match="GPU"):
+        qr.qkrope_run_3d(_gpu(i3["qkv"]), i3["q_weight"], _gpu(i3["k_weight"]), ppf=1, pph=1,
+                         ppw=8, num_frame_channels=16, num_height_channels=56,
+                         num_width_channels=56, num_heads_q=32, num_heads_k=32, num_heads_v=32,
+                         head_dim=128, q_out=outs[0], k_out=outs[1], v_out=outs[2])
+    wc = wl.CAM_PREP_S18480.with_(batch=1, ppf=1, pph=1, ppw=16, num_heads=2)
+    ci = wl.cam_inputs(wc)
+    gc = {k: _gpu(v) for k, v in ci.items()}
+    co = [torch.empty((1, 2, 64, 16), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    with pytest.raises(ValueError, match="GPU"):
+        qr.qkrope_cam_prep(gc["q"], gc["k"], gc["v"], ci["proj_q"], gc["proj_kv"],
+                           gc["rope_cos"], gc["rope_sin"], 1.0, q_out=co[0], k_out=co[1],
+                           v_out=co[2])
+    torch.cuda.synchronize()
