@@ -24,7 +24,7 @@ qr = pytest.importorskip("qk_rmsnorm_rope_amd")
 from qk_rmsnorm_rope_amd import workloads as wl  # noqa: E402
 
 DEV = "cuda"
-N3D, NTAB = 40, 48
+N3D, NTAB = 80, 96
 
 
 def draw_3d(i):
