@@ -34,7 +34,8 @@ struct CamArgs {
     int vec_store;                  // outputs take 16-byte stores (N % 8 == 0, aligned bases)
     float k_scale;
 };
-// cpl: 16-byte chunks per lane (1 for head_dim <= 128, else 2); threads = 64 * lanes_per_token;
+// cpl: 16-byte chunks per lane (1 for head_dim <= 64, else ceil(head_dim / 64), with 8 lanes per
+// token); threads = 64 * lanes_per_token;
 // lds_bytes = 2 * kCamTile * head_dim * 2.
 hipError_t launch_cam(const CamArgs &args, int act, int cpl, int64_t blocks, int lds_bytes,
                       hipStream_t stream);

@@ -62,8 +62,9 @@ __device__ __forceinline__ void project8(const float P[16], const float x[8], fl
         }
 }
 
-// ACT: activation format. CPL: 16-byte chunks per lane per head (1 for head_dim <= 128, else
-// 2). LT: lanes per token (power of two >= head_dim / 8 / CPL); workgroups are 64 * LT lanes.
+// ACT: activation format. CPL: 16-byte chunks per lane per head (1 for head_dim <= 64, else
+// ceil(head_dim / 64)). LT: lanes per token (power of two >= head_dim / 8 / CPL, at most 8);
+// workgroups are 64 * LT <= 512 lanes.
 template <int ACT, int CPL, int LT>
 __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
 {
@@ -161,7 +162,10 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
     // slightly faster than storing each tensor as it is gathered); partial tiles and unaligned
     // rows store elements as they go
     const bool fast = a.vec_store && nvalid == kCamTile;
-    uint4 o[MI][CPL];
+    // buffered outputs cost 4 * MI * CPL registers; past two chunks per lane they would cut the
+    // occupancy below two workgroups per CU, so those variants store as they go
+    constexpr bool kEndStores = CPL <= 2;
+    uint4 o[kEndStores ? MI : 1][CPL];
 
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -219,7 +223,8 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
             if (fast) {
                 const uint4 w = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16,
                                            e8[4] | (uint32_t)e8[5] << 16, e8[6] | (uint32_t)e8[7] << 16);
-                o[i][j] = w;
+                if (kEndStores) o[i][j] = w;
+                else *reinterpret_cast<uint4 *>(plane + st_off[j]) = w;
             } else {
                 uint16_t *dst = reinterpret_cast<uint16_t *>(plane) + ud[j] * N + n0 + us[j] * 8;
 #pragma unroll
@@ -228,7 +233,7 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
             }
         }
     }
-    if (fast) {
+    if (kEndStores && fast) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             if (i >= iters) continue;
@@ -253,14 +258,19 @@ template <int ACT>
 hipError_t launch_cam_act(const CamArgs &a, int cpl, int64_t blocks, int lds_bytes, hipStream_t st)
 {
     const int lt = a.lanes_per_token;
-    if (cpl == 2) return lt == 16 ? go_cam<ACT, 2, 16>(a, blocks, lds_bytes, st) : hipErrorInvalidValue;
-    if (cpl != 1) return hipErrorInvalidValue;
+    if (cpl > 1 && lt != 8) return hipErrorInvalidValue;
+    switch (cpl) {
+    case 1: break;
+    case 2: return go_cam<ACT, 2, 8>(a, blocks, lds_bytes, st);
+    case 3: return go_cam<ACT, 3, 8>(a, blocks, lds_bytes, st);
+    case 4: return go_cam<ACT, 4, 8>(a, blocks, lds_bytes, st);
+    default: return hipErrorInvalidValue;
+    }
     switch (lt) {
     case 1: return go_cam<ACT, 1, 1>(a, blocks, lds_bytes, st);
     case 2: return go_cam<ACT, 1, 2>(a, blocks, lds_bytes, st);
     case 4: return go_cam<ACT, 1, 4>(a, blocks, lds_bytes, st);
     case 8: return go_cam<ACT, 1, 8>(a, blocks, lds_bytes, st);
-    case 16: return go_cam<ACT, 1, 16>(a, blocks, lds_bytes, st);
     default: return hipErrorInvalidValue;
     }
 }
