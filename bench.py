@@ -250,7 +250,6 @@ def cpu_baseline(w, cpu_inputs, budget_s: float = 12.0) -> dict:
     """The fp64 oracle, as it stands, on the same workload's tokens in order (output encoding
     included, starting again from the first token after the last), on every host core OpenMP
     gives it, until `budget_s` of work."""
-    import numpy as np
     import oracle
 
     threads = oracle.num_threads()

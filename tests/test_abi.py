@@ -1,6 +1,5 @@
 """The C-ABI library: it loads, exports every function include/qkrope.h declares, and its
 host-side argument checks answer without a GPU (no compute call is made here)."""
-import ctypes
 import os
 import re
 

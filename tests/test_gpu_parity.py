@@ -7,7 +7,6 @@ degenerate grids, strided and in-place table views).
 """
 from __future__ import annotations
 
-import math
 
 import numpy as np
 import pytest
