@@ -268,9 +268,10 @@ int qkrope_run_3d_sharded(qkrope_handle h,
  *                  the fast store path).
  *   inflation_sq   device float32 [batch, num_heads, num_tokens], contiguous, or NULL to skip.
  * No output may overlap an input or another output. head_dim must be a multiple of 4
- * (QKROPE_ERR_INVALID otherwise); this library handles multiples of 8 up to 256, and
- * batch * num_tokens < 2^31 (QKROPE_ERR_UNSUPPORTED). An empty problem (batch, num_tokens or
- * num_heads 0) is a no-op.
+ * (QKROPE_ERR_INVALID otherwise); this library handles multiples of 8 up to 256,
+ * batch * num_tokens < 2^31, and grids of at most 2^32 - 1 lanes (one launch; first exceeded
+ * with a single head of 64 past 2^29 (b, n) tokens) (QKROPE_ERR_UNSUPPORTED). An empty problem
+ * (batch, num_tokens or num_heads 0) is a no-op.
  */
 int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v, int act_dtype,
                     const float *proj_q, const float *proj_kv, const float *rope_cos,

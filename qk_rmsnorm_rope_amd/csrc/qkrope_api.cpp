@@ -118,6 +118,19 @@ bool choose_shape(const int64_t *n, int nreg, int min_lanes, LaunchShape *s)
     return best > 0.0;
 }
 
+// One region (Q, K or V) of one token per workgroup instead of all of a token's regions in one
+// workgroup: lanes hold one 16-byte chunk each and a token's three workgroups run side by side.
+// Measured on MI355X (graph replay, 512-lane regions): faster only where a workgroup just
+// streams, i.e. the 3D form without norm, interleaved pairs and 16-bit outputs (122880 tokens x
+// 3x16 x 256: 77.6% -> 78.3% of 8 TB/s; 15360 x 3x32 x 128 without norm: 77.6% -> 79.5%).
+// With the across-heads norm (77.0% -> 74.7%), E4M3 outputs (79.6% -> 68%), half-split pairs
+// (75% -> 41%) or the table form (80% -> 68%) one workgroup per token stays faster.
+bool split_regions(const LaunchShape &s, const KernelKey &k)
+{
+    return k.src == kSrc3D && k.norm == kNormNone && k.pairing == kPairInterleaved && !k.fp8 &&
+           s.slot_uniform && s.tpw == 1 && s.slots == 1 && s.threads >= 512;
+}
+
 // Token-block order across XCDs (KernelArgs::xcd_group). Workgroups are dealt to the 8 XCDs
 // round-robin, so in block order every page of the streamed tensors is touched by all eight
 // XCDs. Runs of 16 consecutive blocks per XCD, measured on MI355X (graph replay, G in
@@ -160,13 +173,53 @@ hipError_t launch(const KernelKey &k, const LaunchShape &s, const KernelArgs &a,
     }
 }
 
+// Workgroups one launch of `threads` lanes may have: a dispatch's grid holds at most 2^32 - 1
+// work-items per dimension, and HIP takes at most 2^31 - 1 workgroups.
+int64_t max_grid_blocks(int threads)
+{
+    return std::min<int64_t>(((int64_t(1) << 32) - 1) / threads, (int64_t(1) << 31) - 1);
+}
+
+// The same call restricted to tokens [t0, t0 + n): every per-token pointer moves t0 tokens on,
+// and the 3D positions continue from token_offset + t0.
+KernelArgs token_range(const KernelArgs &a, const KernelKey &key, int64_t t0, int64_t n)
+{
+    KernelArgs b = a;
+    const int64_t esize = key.fp8 ? 1 : 2;
+    const int64_t tsize = key.src == kSrcTableF32 ? 4 : 2;
+    for (int r = 0; r < 3; ++r) {
+        if (b.in[r]) b.in[r] += t0 * b.in_stride[r];
+        if (b.out[r]) b.out[r] = static_cast<uint8_t *>(b.out[r]) + t0 * b.out_stride[r] * esize;
+    }
+    if (key.src != kSrc3D) {
+        if (b.table_cos) b.table_cos = static_cast<const uint8_t *>(b.table_cos) + t0 * b.cos_stride * tsize;
+        if (b.table_sin) b.table_sin = static_cast<const uint8_t *>(b.table_sin) + t0 * b.sin_stride * tsize;
+    }
+    if (b.sumsq_in) b.sumsq_in += 2 * t0;
+    b.token_offset += (uint32_t)t0;
+    b.num_tokens = n;
+    return b;
+}
+
+// Launches the call, as several launches over consecutive token ranges where one grid would
+// exceed the dispatch limits (e.g. 64-lane workgroups past 2^26 tokens).
 int do_launch(qkrope_handle h, const KernelKey &key, const LaunchShape &shape,
               const KernelArgs &args, void *stream)
 {
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(QKROPE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(g.err));
-    hipError_t e = launch(key, shape, args, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    const int64_t per_block = shape.split ? (key.src == kSrc3D ? 3 : 2) : 1;  // workgroups per token block
+    const int64_t T = args.num_tokens;
+    const int64_t chunk = max_grid_blocks(shape.threads) / per_block * shape.tpw;   // tokens per launch
+    for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+        const int64_t n = std::min(chunk, T - t0);
+        LaunchShape s = shape;
+        KernelArgs a = n == T ? args : token_range(args, key, t0, n);
+        s.blocks = (n + s.tpw - 1) / s.tpw * per_block;
+        a.xcd_group = xcd_group_for(s.blocks);
+        const hipError_t e = launch(key, s, a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    }
     return ok();
 }
 
@@ -315,9 +368,7 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     a.inv_count[1] = (float)(1.0 / (double)(across ? (int64_t)Hk * D : D));
     a.qk_scale = fp8 ? (float)c.out_scale : 1.0f;
     a.v_scale = 1.0f;
-    shape.blocks = (T + shape.tpw - 1) / shape.tpw;
     shape.lds_bytes = pairing == kPairHalfAny ? shape.threads * 32 : 0;
-    a.xcd_group = xcd_group_for(shape.blocks);
 
     KernelKey key;
     key.head_dim_tpl = 0;
@@ -484,10 +535,6 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
         a.omega_rev[k] = (float)(omega / two_pi);
         a.axis[k] = (uint8_t)axis;
     }
-    shape.blocks = (T + shape.tpw - 1) / shape.tpw;
-    shape.lds_bytes = 0;
-    a.xcd_group = xcd_group_for(shape.blocks);
-
     KernelKey key;
     key.head_dim_tpl = D;
     key.pairing = half ? kPairHalf : kPairInterleaved;     // R/2 = D/2 is a multiple of 8
@@ -497,6 +544,9 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
     key.fp8 = c.output_fp8 != 0;
     key.slots = shape.slots;
     key.slot_uniform = shape.slot_uniform;
+
+    shape.split = split_regions(shape, key);
+    shape.lds_bytes = 0;
     return do_launch(h, key, shape, a, stream);
 }
 
@@ -681,8 +731,14 @@ int qkrope_sumsq_3d(qkrope_handle h, const void *qkv, int64_t num_tokens, int nu
     const int threads = (int)std::max<int64_t>(64, (per + 63) / 64 * 64);
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(QKROPE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(g.err));
-    const hipError_t e = launch_sumsq(a, T, threads, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    const int64_t chunk = max_grid_blocks(threads);        // one workgroup per token
+    for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+        SumsqArgs b = a;
+        b.qkv += t0 * row;
+        b.out += 2 * t0;
+        const hipError_t e = launch_sumsq(b, std::min(chunk, T - t0), threads, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    }
     return ok();
 }
 

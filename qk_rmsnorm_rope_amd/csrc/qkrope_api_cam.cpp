@@ -107,7 +107,10 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
     // than plain runs of 16 tiles.
     a.tiles_padded = a.tiles >= 8 ? (a.tiles + 7) / 8 * 8 : a.tiles;
     const int64_t blocks = B * a.tiles_padded * (int64_t)a.groups;
-    if (blocks >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "grid too large");
+    // a dispatch holds at most 2^32 - 1 work-items per dimension (first reached with one head:
+    // 2^29 (b, n) tokens at head_dim 64, 206 GB of inputs and outputs)
+    if (blocks >= (int64_t(1) << 31) || blocks * 64 * lanes >= (int64_t(1) << 32))
+        return fail(QKROPE_ERR_UNSUPPORTED, "grid too large");
     a.xcd_group = a.tiles >= 8 ? (uint32_t)(a.tiles_padded / 8) : 0u;
     a.vec_store = (N % 8 == 0) && aligned(q_out, 16) && aligned(k_out, 16) && aligned(v_out, 16);
     a.k_scale = k_scale;

@@ -68,9 +68,10 @@ struct LaunchShape {
     int threads;        // workgroup size, multiple of 64, <= 1024
     int slots;          // slots per region (region-major) or per lane (mixed)
     bool slot_uniform;  // region-major slot layout
-    int64_t blocks;     // grid size
+    int64_t blocks;     // grid size (set per launch by the host's launch loop)
     int lds_bytes;      // dynamic LDS per workgroup (kPairHalfAny: threads * 32)
     int tpw;            // tokens per workgroup: 1, or 2 (region-major, one slot per region)
+    bool split;         // one region of one token per workgroup (region-major, tpw 1)
 };
 
 // Kernel selection keys.

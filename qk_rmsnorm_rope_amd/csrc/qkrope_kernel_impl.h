@@ -256,16 +256,20 @@ __device__ __forceinline__ float sumsq_packed(const uint4 v, float acc)
 // SU: region-major slots (NS per region); otherwise mixed slots (NS in all).
 // TPW: tokens per workgroup, 1, or 2 (region-major, one slot per region) when a token needs a
 // multiple of 32 but not of 64 lanes, so that two tokens fill whole waves.
-template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU, int TPW>
+// RS: one region (Q, K or V) of one token per workgroup, NS slots; workgroup b takes region
+// b mod NREG of token b / NREG (in XCD order). Launched for the 3D form without norm,
+// interleaved pairs and 16-bit outputs, where every workgroup only streams.
+template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU, int TPW, bool RS>
 __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 {
     static_assert(TPW == 1 || (TPW == 2 && SU && NS == 1), "two tokens per workgroup: region-major, one slot");
+    static_assert(!RS || (SU && TPW == 1), "one region per workgroup: region-major, one token");
     constexpr bool HALF = PAIR != kPairInterleaved;
     constexpr bool XCH = PAIR == kPairHalfAny;  // partners through LDS, per element
     constexpr bool IS3D = (SRC == kSrc3D);
     constexpr bool ACROSS = NORM == kNormAcross || NORM == kNormAcrossExt;
     constexpr int NREG = IS3D ? 3 : 2;          // regions: Q, K (, V)
-    constexpr int NSLOT = SU ? NREG * NS : NS;
+    constexpr int NSLOT = SU && !RS ? NREG * NS : NS;
     constexpr int NPAIR = HALF ? 8 : 4;         // rotation pairs a chunk takes part in
     constexpr bool NEED_BARRIER = IS3D || NORM == kNormAcross;
     static_assert(!(SRC == kSrcTableBF16 && ACT == kActF16) && !(SRC == kSrcTableF16 && ACT == kActBF16),
@@ -321,6 +325,23 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         partner = tid & 63;
     }
 
+    // Workgroups are dealt to the 8 XCDs round-robin (block b to XCD b % 8). With xcd_group G,
+    // XCD x takes runs of G consecutive blocks instead of every 8th block, so a page of the
+    // streams is touched by one XCD's translation caches, not all eight; blocks past the last
+    // whole run of 8G keep their own index.
+    uint32_t blk = blockIdx.x;
+    if (a.xcd_group) {
+        const uint32_t G = a.xcd_group, S = 8u * G, full = gridDim.x / S * S;
+        if (blk < full) {
+            const uint32_t j = blk >> 3, x = blk & 7u;
+            blk = (j / G) * S + x * G + j % G;
+        }
+    }
+    // RS: this workgroup's region (uniform); blk becomes its token
+    const int rs = RS ? (int)(blk % (uint32_t)NREG) : 0;
+    if (RS) blk /= (uint32_t)NREG;
+    const bool v_wg = RS && NREG == 3 && rs == kV;   // V only: no norm, no angles, no barrier
+
     // Slot -> region (3 = idle) and the element offset of the slot's head inside its region row.
     const int Hq = a.heads[kQ], Hk = a.heads[kK], Hv = NREG == 3 ? a.heads[kV] : 0;
     int reg[NSLOT];
@@ -328,7 +349,12 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     bool ok[NSLOT];
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-        if (SU) {
+        if (RS) {
+            const int hh = (tl + j * LT) >> lgL;
+            reg[j] = rs;
+            ok[j] = unit_ok && hh < sel3(rs, Hq, Hk, Hv);
+            hoff[j] = (uint32_t)(hh * D);
+        } else if (SU) {
             const int r = j / NS;                       // compile-time after unrolling
             const int hh = (tl + (j % NS) * LT) >> lgL;
             reg[j] = r;
@@ -347,32 +373,20 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     // Per-head norm weights ([head_dim], shared by every head) stay packed in registers.
     uint4 wq = make_uint4(0, 0, 0, 0), wk = wq;
     if (NORM == kNormPerHead && unit_ok) {
-        if (Hq > 0) wq = ld16(a.weight[0], 2 * off0);
-        if (Hk > 0) wk = ld16(a.weight[1], 2 * off0);
+        if (Hq > 0 && (!RS || rs == kQ)) wq = ld16(a.weight[0], 2 * off0);
+        if (Hk > 0 && (!RS || rs == kK)) wk = ld16(a.weight[1], 2 * off0);
     }
 
     // 3D: this lane's pair (tid < D/2) frequency in revolutions and its position axis.
     float omega_rev = 0.0f;
     int axis = 0;
-    if (IS3D && tl < D / 2) {
+    if (IS3D && tl < D / 2 && !v_wg) {
         omega_rev = a.omega_rev[tl];
         axis = a.axis[tl];
     }
 
     // The workgroup's first token, and this lane's: a missing second token (odd token count)
     // re-reads the first token's row and stores nothing.
-    // Workgroups are dealt to the 8 XCDs round-robin (block b to XCD b % 8). With xcd_group G,
-    // XCD x takes runs of G consecutive token blocks instead of every 8th block, so a page of
-    // the streams is touched by one XCD's translation caches, not all eight; blocks past the
-    // last whole run of 8G keep their own index.
-    uint32_t blk = blockIdx.x;
-    if (a.xcd_group) {
-        const uint32_t G = a.xcd_group, S = 8u * G, full = gridDim.x / S * S;
-        if (blk < full) {
-            const uint32_t j = blk >> 3, x = blk & 7u;
-            blk = (j / G) * S + x * G + j % G;
-        }
-    }
     const int64_t t0 = (int64_t)blk * TPW;
     const bool tok_ok = TPW == 1 || t0 + ts < a.num_tokens;
     const int ts_eff = tok_ok ? ts : 0;
@@ -405,34 +419,37 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         // -- cos/sin: the table row, or the 3D angle of pair `tid` into LDS
         float cs_c[NPAIR], cs_s[NPAIR];
         if (IS3D) {
-            // grid positions of the workgroup's tokens (uniform; t < 2^31), this lane's selected
-            uint32_t pf, ph, pw;
-            {
-                const uint32_t tt = (uint32_t)t0 + a.token_offset;
-                const uint32_t s = tt - fast_div(tt, a.div_seq.m, a.div_seq.l) * a.seq_len;
-                pf = fast_div(s, a.div_hw.m, a.div_hw.l);
-                const uint32_t rem = s - pf * a.hw;
-                ph = fast_div(rem, a.div_w.m, a.div_w.l);
-                pw = rem - ph * a.ppw;
-            }
-            if (TPW == 2) {
-                const uint32_t tt = (uint32_t)t0 + 1u + a.token_offset;
-                const uint32_t s = tt - fast_div(tt, a.div_seq.m, a.div_seq.l) * a.seq_len;
-                const uint32_t pf1 = fast_div(s, a.div_hw.m, a.div_hw.l);
-                const uint32_t rem = s - pf1 * a.hw;
-                const uint32_t ph1 = fast_div(rem, a.div_w.m, a.div_w.l);
-                const uint32_t pw1 = rem - ph1 * a.ppw;
-                pf = ts ? pf1 : pf;
-                ph = ts ? ph1 : ph;
-                pw = ts ? pw1 : pw;
-            }
-            if (tl < D / 2) {               // the host gives every token >= D/2 lanes
-                const uint32_t pos = axis == 0 ? pf : (axis == 1 ? ph : pw);
-                // angle in revolutions, reduced to [0, 1): sin/cos(2*pi*rev) in hardware
-                const float rev = __builtin_amdgcn_fractf((float)pos * omega_rev);
-                const float c = __builtin_amdgcn_cosf(rev) * a.attention_factor;
-                const float sn = __builtin_amdgcn_sinf(rev) * a.attention_factor;
-                s_cs[ts * kMaxPairs + tl] = f32x4{c, -sn, c, sn};
+            if (!v_wg) {    // a V-only workgroup rotates nothing
+                // grid positions of the workgroup's tokens (uniform; t < 2^31); the lane picks
+                // its pair's axis below
+                uint32_t pf, ph, pw;
+                {
+                    const uint32_t tt = (uint32_t)t0 + a.token_offset;
+                    const uint32_t s = tt - fast_div(tt, a.div_seq.m, a.div_seq.l) * a.seq_len;
+                    pf = fast_div(s, a.div_hw.m, a.div_hw.l);
+                    const uint32_t rem = s - pf * a.hw;
+                    ph = fast_div(rem, a.div_w.m, a.div_w.l);
+                    pw = rem - ph * a.ppw;
+                }
+                if (TPW == 2) {
+                    const uint32_t tt = (uint32_t)t0 + 1u + a.token_offset;
+                    const uint32_t s = tt - fast_div(tt, a.div_seq.m, a.div_seq.l) * a.seq_len;
+                    const uint32_t pf1 = fast_div(s, a.div_hw.m, a.div_hw.l);
+                    const uint32_t rem = s - pf1 * a.hw;
+                    const uint32_t ph1 = fast_div(rem, a.div_w.m, a.div_w.l);
+                    const uint32_t pw1 = rem - ph1 * a.ppw;
+                    pf = ts ? pf1 : pf;
+                    ph = ts ? ph1 : ph;
+                    pw = ts ? pw1 : pw;
+                }
+                if (tl < D / 2) {               // the host gives every token >= D/2 lanes
+                    const uint32_t pos = axis == 0 ? pf : (axis == 1 ? ph : pw);
+                    // angle in revolutions, reduced to [0, 1): sin/cos(2*pi*rev) in hardware
+                    const float rev = __builtin_amdgcn_fractf((float)pos * omega_rev);
+                    const float c = __builtin_amdgcn_cosf(rev) * a.attention_factor;
+                    const float sn = __builtin_amdgcn_sinf(rev) * a.attention_factor;
+                    s_cs[ts * kMaxPairs + tl] = f32x4{c, -sn, c, sn};
+                }
             }
         } else if (XCH) {
             // per element g = 8u + e: angle index g (first half, sign -) or g - R/2 (second
@@ -547,7 +564,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
             ss[j] = 0.0f;
-            if (NORM == kNormPerHead || NORM == kNormAcross) {
+            if ((NORM == kNormPerHead || NORM == kNormAcross) && !v_wg) {
                 const float v = sumsq_packed<ACT>(x[j], 0.0f);
                 ss[j] = (ok[j] && reg[j] < 2) ? v : 0.0f;
             }
@@ -555,7 +572,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         if (NORM == kNormPerHead) {
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) ss[j] = group_sum(ss[j], L);
-        } else if (NORM == kNormAcross) {
+        } else if (NORM == kNormAcross && !v_wg) {
             float sq = 0.0f, sk = 0.0f;
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
@@ -574,10 +591,12 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             }
         }
 
-        if (NEED_BARRIER) __syncthreads();
+        if (NEED_BARRIER && !v_wg) __syncthreads();   // v_wg is uniform
 
         float rq = 1.0f, rk = 1.0f;
-        if (NORM == kNormAcrossExt) {
+        if (v_wg) {
+            // V only: neither scale is used
+        } else if (NORM == kNormAcrossExt) {
             // sums over every head of the token, reduced by the caller (uniform scalar load)
             const f32x2 p = reinterpret_cast<const f32x2 *>(a.sumsq_in)[t];   // per lane's token
             rq = __builtin_amdgcn_rsqf(p.x * a.inv_count[0] + a.eps);
@@ -600,7 +619,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             rq = __builtin_amdgcn_rsqf(sq * a.inv_count[0] + a.eps);
             rk = __builtin_amdgcn_rsqf(sk * a.inv_count[1] + a.eps);
         }
-        if (IS3D && unit_ok) {
+        if (IS3D && unit_ok && !v_wg) {
             // interleaved and second-half lanes read (cos, sin), first-half lanes (cos, -sin)
             const f32x2 *tab = reinterpret_cast<const f32x2 *>(s_cs + ts * kMaxPairs) +
                                (HALF && half_sign < 0.0f ? 0 : 1);
@@ -620,6 +639,10 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         for (int j = 0; j < NSLOT; ++j) {
             const bool isv = NREG == 3 && reg[j] == kV;   // compile-time in the region-major layout
             const bool isq = reg[j] == 0;
+            if (RS && !FP8 && v_wg) {
+                pk[j] = x[j];                           // V: bit copy (uniform branch)
+                continue;
+            }
             float n[8];
             unpack8<ACT>(x[j], n);
             float scale = FP8 ? (isv ? a.v_scale : a.qk_scale) : 1.0f;
@@ -755,10 +778,10 @@ __global__ void __launch_bounds__(1024) qkrope_sumsq_kernel(const SumsqArgs a)
 
 // ---- launch helpers ---------------------------------------------------------------------------
 
-template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU, int TPW>
+template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU, int TPW, bool RS>
 hipError_t go(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL((qkrope_kernel<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, TPW>), dim3((unsigned)s.blocks),
+    hipLaunchKernelGGL((qkrope_kernel<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, TPW, RS>), dim3((unsigned)s.blocks),
                        dim3(s.threads), s.lds_bytes, st, a);
     return hipGetLastError();
 }
@@ -767,11 +790,20 @@ template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool S
 hipError_t go_if(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if constexpr (slots_compiled(SRC == kSrc3D ? 3 : 2, SU, NS)) {
+        if (s.split) {
+            if constexpr (SU && NS == 1 && SRC == kSrc3D && NORM == kNormNone &&
+                          PAIR == kPairInterleaved && !FP8) {
+                if (s.tpw != 1) return hipErrorInvalidValue;
+                return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, 1, true>(s, a, st);
+            } else {
+                return hipErrorInvalidValue;
+            }
+        }
         if constexpr (SU && NS == 1) {
-            if (s.tpw == 2) return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, 2>(s, a, st);
+            if (s.tpw == 2) return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, 2, false>(s, a, st);
         }
         if (s.tpw != 1) return hipErrorInvalidValue;
-        return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, 1>(s, a, st);
+        return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, 1, false>(s, a, st);
     } else {
         return hipErrorInvalidValue;
     }
