@@ -371,7 +371,13 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     shape.lds_bytes = pairing == kPairHalfAny ? shape.threads * 32 : 0;
 
     KernelKey key;
-    key.head_dim_tpl = 0;
+    // E4M3 outputs at head_dim == rotary_dim == 128 with one slot per region take a kernel with
+    // the head geometry fixed at compile time (fixed lane groups, no per-pair rotation masks).
+    // That path is ALU-bound on MI355X, and measured (graph replay, 32768 tokens x 2x24 heads,
+    // fp32 table) 102.2 -> 95.9 us, 75.9% -> 80.9% of 8 TB/s. With 16-bit outputs, bound by
+    // memory, the run-time kernel was as fast (bf16) or 1.7% faster (float16).
+    key.head_dim_tpl = fp8 && D == 128 && R == 128 && pairing != kPairHalfAny &&
+                       shape.slot_uniform && shape.slots == 1 ? 128 : 0;
     key.pairing = pairing;
     key.norm = c.norm_mode == QKROPE_NORM_NONE ? kNormNone
              : c.norm_mode == QKROPE_NORM_PER_HEAD ? kNormPerHead : kNormAcross;

@@ -76,7 +76,8 @@ struct LaunchShape {
 
 // Kernel selection keys.
 struct KernelKey {
-    int head_dim_tpl;   // 64/128/256 for the 3D kernels, 0 = runtime head_dim (table form)
+    int head_dim_tpl;   // 64/128/256 for the 3D kernels; table form: 0 = run-time head_dim, 128 =
+                        // E4M3 outputs with head_dim == rotary_dim == 128, one slot per region
     int pairing;        // Pairing
     int norm;           // Norm
     int src;            // RopeSrc

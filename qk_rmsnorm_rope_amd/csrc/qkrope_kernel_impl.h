@@ -284,7 +284,8 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     extern __shared__ float s_xch[];
 
     const int D = DT > 0 ? DT : a.head_dim;
-    const int R = IS3D ? D : a.rotary_dim;
+    // a table kernel with a compile-time head_dim is launched only for rotary_dim == head_dim
+    const int R = (IS3D || DT > 0) ? D : a.rotary_dim;
     const int units = D / 8;                    // chunks per head
     const int L = DT > 0 ? units : a.lanes_per_head;
     const int lgL = __builtin_ctz(L);
@@ -370,11 +371,15 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         }
     }
 
-    // Per-head norm weights ([head_dim], shared by every head) stay packed in registers.
+    // Per-head norm weights ([head_dim], shared by every head) stay packed in registers. Under
+    // this norm both pointers are valid (a region without heads borrows the other's weights),
+    // so both loads are issued unconditionally, lanes past the head's chunks reading chunk 0:
+    // a load under a branch has the compiler wait for it before the data loads are issued.
     uint4 wq = make_uint4(0, 0, 0, 0), wk = wq;
-    if (NORM == kNormPerHead && unit_ok) {
-        if (Hq > 0 && (!RS || rs == kQ)) wq = ld16(a.weight[0], 2 * off0);
-        if (Hk > 0 && (!RS || rs == kK)) wk = ld16(a.weight[1], 2 * off0);
+    if (NORM == kNormPerHead) {
+        const uint32_t wo = unit_ok ? 2 * off0 : 0u;
+        wq = ld16(a.weight[0], wo);
+        wk = ld16(a.weight[1], wo);
     }
 
     // 3D: this lane's pair (tid < D/2) frequency in revolutions and its position axis.
@@ -862,6 +867,17 @@ template <int PAIR, int ACT, int NORM>
 hipError_t launch_table_src(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     constexpr int SRC16 = ACT == kActBF16 ? kSrcTableBF16 : kSrcTableF16;
+    if (k.head_dim_tpl == 128) {
+        // E4M3 outputs, head_dim == rotary_dim == 128, one slot per region (see the host)
+        if constexpr (PAIR == kPairHalfAny) {
+            return hipErrorInvalidValue;
+        } else {
+            if (!k.fp8 || !k.slot_uniform || k.slots != 1) return hipErrorInvalidValue;
+            if (k.src == kSrcTableF32) return go_if<128, PAIR, NORM, kSrcTableF32, ACT, true, 1, true>(s, a, st);
+            if (k.src == SRC16) return go_if<128, PAIR, NORM, SRC16, ACT, true, 1, true>(s, a, st);
+            return hipErrorInvalidValue;
+        }
+    }
     if (k.src == kSrcTableF32) return by_fp8<0, PAIR, NORM, kSrcTableF32, ACT>(k, s, a, st);
     if (k.src == SRC16) return by_fp8<0, PAIR, NORM, SRC16, ACT>(k, s, a, st);
     return hipErrorInvalidValue;
@@ -872,7 +888,8 @@ hipError_t launch_table_src(const KernelKey &k, const LaunchShape &s, const Kern
 template <int PAIR, int ACT>
 hipError_t launch_table(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
-    if (k.head_dim_tpl != 0 || k.act != ACT || k.pairing != PAIR) return hipErrorInvalidValue;
+    if ((k.head_dim_tpl != 0 && k.head_dim_tpl != 128) || k.act != ACT || k.pairing != PAIR)
+        return hipErrorInvalidValue;
     switch (k.norm) {
     case kNormNone: return launch_table_src<PAIR, ACT, kNormNone>(k, s, a, st);
     case kNormPerHead: return launch_table_src<PAIR, ACT, kNormPerHead>(k, s, a, st);

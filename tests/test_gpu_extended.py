@@ -150,6 +150,39 @@ def test_table_e4m3_outputs(act, inter, scale, sigma, R):
         assert ((codes & 0x7F) == 0x7E).any(), "the saturation case must reach +-448"
 
 
+# E4M3 outputs at head_dim == rotary_dim == 128 with one slot per region run a kernel whose head
+# geometry is fixed at compile time: every norm, both pairings, both table formats, one token per
+# workgroup (3, 16 or 24 Q heads) and two (2 or 6 heads per region fill 32 + 64k lanes),
+# saturation.
+@pytest.mark.parametrize("inter,norm,act,tdt,hq,hk,scale,sigma", [
+    (True, "per_head", "bf16", "f32", 16, 8, 0.5, 1.0),
+    (False, "across_heads", "bf16", "bf16", 6, 6, 1.0, 1.0),
+    (True, "none", "bf16", "bf16", 2, 2, 1.0, 1.0),
+    (False, "per_head", "f16", "f32", 2, 2, 2.0, 1.0),
+    (True, "across_heads", "f16", "f16", 24, 24, 1.0, 1.0),
+    (False, "none", "bf16", "f32", 3, 3, 300.0, 4.0),
+])
+def test_table_e4m3_head_dim_128(inter, norm, act, tdt, hq, hk, scale, sigma):
+    w = table_workload(301, hq, hk, 128, 128, inter, norm, act, tdt, seed=4350 + hq + hk,
+                       sigma=sigma)
+    w = w.with_(out_dtype="e4m3", out_scale=scale)
+    inp = wl.table_inputs(w)
+    g = {k: _gpu(v) for k, v in inp.items()}
+    qo = torch.empty(g["q"].shape, dtype=torch.float8_e4m3fn, device=DEV)
+    ko = torch.empty(g["k"].shape, dtype=torch.float8_e4m3fn, device=DEV)
+    qr.qkrope_run_table_ex(g["q"], g["k"], g["q_weight"], g["k_weight"],
+                           g["rope_table"][:, :64], g["rope_table"][:, 64:], w.eps,
+                           q_out=qo, k_out=ko, rotary_dim=128, interleaved=inter,
+                           norm_mode=norm, out_scale=scale)
+    torch.cuda.synchronize()
+    rq, rk = oracle_table(w, inp)
+    assert_e4m3_within_one(qo, oracle.e4m3_encode(rq, scale), "q")
+    assert_e4m3_within_one(ko, oracle.e4m3_encode(rk, scale), "k")
+    if scale >= 300:
+        codes = qo.view(torch.uint8).cpu().numpy()
+        assert ((codes & 0x7F) == 0x7E).any(), "the saturation case must reach +-448"
+
+
 def test_table_ex_contract():
     w = table_workload(16, 2, 2, 64, 64, True, "per_head", "f16", "f16", seed=4400)
     inp = wl.table_inputs(w)
