@@ -109,8 +109,8 @@ int qkrope_min_tokens(int64_t default_tokens, int64_t *out);
  *   k_out      q_out == q (with equal strides) works in place, likewise k_out == k; any other
  *              overlap between an output and an input is QKROPE_ERR_INVALID.
  *
- * Limits (else QKROPE_ERR_UNSUPPORTED): head_dim a multiple of 8 and <= 256; num_tokens < 2^31.
- * Any even rotary_dim works with either pairing (half-split partners that straddle 16-byte
+ * Limits (else QKROPE_ERR_UNSUPPORTED): head_dim a multiple of 8 and <= 256; num_tokens < 2^31;
+ * q, k and output token strides multiples of 8 elements and < 2^28. Any even rotary_dim works with either pairing (half-split partners that straddle 16-byte
  * chunks, i.e. rotary_dim % 16 != 0, are exchanged through LDS, a slower path).
  * num_tokens == 0 (or zero heads) is a valid no-op.
  */

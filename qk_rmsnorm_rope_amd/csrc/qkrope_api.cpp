@@ -140,7 +140,7 @@ bool split_regions(const LaunchShape &s, const KernelKey &k)
 // plain order (the remap leaves blocks past the last whole 8G run in place).
 uint32_t xcd_group_for(int64_t blocks)
 {
-    return blocks >= 128 ? 16u : 0u;
+    return blocks >= 128 ? 16u : 0u;    // a power of two (the kernel shifts by its log)
 }
 
 // Magic pair for n / d, n < 2^31 (round-up method): with l = ceil(log2 d) and
@@ -278,6 +278,11 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
         return fail(QKROPE_ERR_INVALID, "table token strides must be >= rotary_dim/2");
     if (c.q_stride % 8 || c.k_stride % 8 || c.q_out_stride % 8 || c.k_out_stride % 8)
         return fail(QKROPE_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements");
+    // a workgroup addresses its tokens' rows with 32-bit byte offsets from the first one's
+    const int64_t kMaxStride = int64_t(1) << 28;
+    if (c.q_stride >= kMaxStride || c.k_stride >= kMaxStride || c.q_out_stride >= kMaxStride ||
+        c.k_out_stride >= kMaxStride)
+        return fail(QKROPE_ERR_UNSUPPORTED, "token strides must be < 2^28 elements");
     const uintptr_t oalign = fp8 ? 8 : 16;
     if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.q_weight, 16) || !aligned(c.k_weight, 16))
         return fail(QKROPE_ERR_UNSUPPORTED, "q, k and weights must be 16-byte aligned");

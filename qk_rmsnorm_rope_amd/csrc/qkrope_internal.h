@@ -44,7 +44,7 @@ struct KernelArgs {
     const float *sumsq_in;     // kNormAcrossExt: [T, 2] sums of squares of Q and K rows
 
     int64_t num_tokens;        // tokens; the grid has one workgroup per token (per 2 with TPW 2)
-    uint32_t xcd_group;        // 0: block b takes token block b; G > 0: XCD-chunked order (below)
+    uint32_t xcd_group;        // 0: block b takes token block b; G > 0 (a power of two): XCD runs
     int head_dim;              // D
     int rotary_dim;            // R (== D for the 3D form)
     int lanes_per_head;        // L: power of two >= head_dim / 8 (16-byte chunks per head)

@@ -120,11 +120,12 @@ __device__ __forceinline__ uint2 pack8_e4m3(const float yin[8])
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = yin[i];
-    const float m = __builtin_fmaxf(
-        __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1])),
-                        __builtin_fmaxf(__builtin_fabsf(y[2]), __builtin_fabsf(y[3]))),
-        __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[4]), __builtin_fabsf(y[5])),
-                        __builtin_fmaxf(__builtin_fabsf(y[6]), __builtin_fabsf(y[7]))));
+    // a chain of three-operand maxima with |.| operand modifiers: four v_max3_f32
+    float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1])),
+                              __builtin_fabsf(y[2]));
+    m = __builtin_fmaxf(__builtin_fmaxf(m, __builtin_fabsf(y[3])), __builtin_fabsf(y[4]));
+    m = __builtin_fmaxf(__builtin_fmaxf(m, __builtin_fabsf(y[5])), __builtin_fabsf(y[6]));
+    m = __builtin_fmaxf(m, __builtin_fabsf(y[7]));
     if (m > 448.0f) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = sat_e4m3(y[i]);
@@ -163,16 +164,18 @@ __device__ __forceinline__ uint4 ld16_stream(const void *base, uint32_t byte_off
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void st16_stream(uint8_t *p, uint4 v)
+// Streamed 16- and 8-byte stores at a (usually uniform) base plus a 32-bit byte offset, like
+// the loads: the saddr+voffset form, with no 64-bit address arithmetic per lane.
+__device__ __forceinline__ void st16_stream(void *base, uint32_t byte_off, uint4 v)
 {
     const u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(static_cast<uint8_t *>(base) + byte_off));
 }
 
-__device__ __forceinline__ void st8_stream(uint8_t *p, uint2 v)
+__device__ __forceinline__ void st8_stream(void *base, uint32_t byte_off, uint2 v)
 {
     const u32x2 w = {v.x, v.y};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(base) + byte_off));
 }
 
 // n / d for n < 2^31 with a host-computed magic pair (m, l): q = (mulhi(n, m) + n) >> l.
@@ -326,16 +329,16 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         partner = tid & 63;
     }
 
-    // Workgroups are dealt to the 8 XCDs round-robin (block b to XCD b % 8). With xcd_group G,
-    // XCD x takes runs of G consecutive blocks instead of every 8th block, so a page of the
-    // streams is touched by one XCD's translation caches, not all eight; blocks past the last
-    // whole run of 8G keep their own index.
+    // Workgroups are dealt to the 8 XCDs round-robin (block b to XCD b % 8). With xcd_group G
+    // (a power of two), XCD x takes runs of G consecutive blocks instead of every 8th block, so a
+    // page of the streams is touched by one XCD's translation caches, not all eight; blocks past
+    // the last whole run of 8G keep their own index. Uniform, so scalar shifts and masks.
     uint32_t blk = blockIdx.x;
     if (a.xcd_group) {
-        const uint32_t G = a.xcd_group, S = 8u * G, full = gridDim.x / S * S;
+        const uint32_t lg = __builtin_ctz(a.xcd_group), full = gridDim.x >> (lg + 3) << (lg + 3);
         if (blk < full) {
             const uint32_t j = blk >> 3, x = blk & 7u;
-            blk = (j / G) * S + x * G + j % G;
+            blk = ((j >> lg) << (lg + 3)) + (x << lg) + (j & (a.xcd_group - 1));
         }
     }
     // RS: this workgroup's region (uniform); blk becomes its token
@@ -731,10 +734,9 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             if (!ok[j] || !tok_ok) continue;
             const int r = reg[j] < 3 ? reg[j] : 0;
             const uint32_t tok = TPW == 2 ? (uint32_t)ts * (uint32_t)(a.out_stride[r] * ESIZE) : 0u;
-            uint8_t *orow = sel3(reg[j], out_q, out_k, out_v) + tok;
-            const uint32_t e0 = hoff[j] + off0;
-            if (FP8) st8_stream(orow + e0, make_uint2(pk[j].x, pk[j].y));
-            else st16_stream(orow + 2 * e0, pk[j]);
+            const uint32_t off = tok + (hoff[j] + off0) * ESIZE;
+            if (FP8) st8_stream(sel3(reg[j], out_q, out_k, out_v), off, make_uint2(pk[j].x, pk[j].y));
+            else st16_stream(sel3(reg[j], out_q, out_k, out_v), off, pk[j]);
         }
     }
 }
