@@ -208,6 +208,16 @@ def test_table_ex_contract():
                                1.0, 1e-6, 16, 2, 2, 64, 64, 1, 1, 128, 128, 64, 64,
                                g["q"].data_ptr(), ko.data_ptr(), 128, 128, None)
     assert rc == qr.QKROPE_ERR_INVALID
+    # token strides of 2^28 elements or more are refused (rows are addressed with 32-bit
+    # byte offsets inside a workgroup); one token keeps every span inside the buffers
+    for qs, qos in ((1 << 28, 128), (128, 1 << 28)):
+        rc = L.qkrope_run_table_ex(qr._handle_for(g["q"].device), g["q"].data_ptr(),
+                                   g["k"].data_ptr(), g["q_weight"].data_ptr(),
+                                   g["k_weight"].data_ptr(), c.data_ptr(), s.data_ptr(),
+                                   qr.QKROPE_DTYPE_F16, qr.QKROPE_DTYPE_F16, qr.QKROPE_DTYPE_F16,
+                                   1.0, 1e-6, 1, 2, 2, 64, 64, 1, 1, qs, 128, 64, 64,
+                                   qo.data_ptr(), ko.data_ptr(), qos, 128, None)
+        assert rc == qr.QKROPE_ERR_UNSUPPORTED
 
 
 # --- grouped-query head counts -----------------------------------------------------------------
