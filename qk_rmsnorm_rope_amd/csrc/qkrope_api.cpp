@@ -143,17 +143,6 @@ uint32_t xcd_group_for(int64_t blocks)
     return blocks >= 128 ? 16u : 0u;    // a power of two (the kernel shifts by its log)
 }
 
-// Magic pair for n / d, n < 2^31 (round-up method): with l = ceil(log2 d) and
-// m = floor(2^32 * (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l; the sum cannot
-// overflow 32 bits because mulhi(n, m) <= n < 2^31.
-FastDiv make_fast_div(uint32_t d)
-{
-    uint32_t l = 0;
-    while ((uint64_t(1) << l) < d) ++l;
-    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
-    return FastDiv{(uint32_t)m, l};
-}
-
 hipError_t launch(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if (k.src == kSrc3D) {

@@ -112,9 +112,14 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
     if (blocks >= (int64_t(1) << 31) || blocks * 64 * lanes >= (int64_t(1) << 32))
         return fail(QKROPE_ERR_UNSUPPORTED, "grid too large");
     a.xcd_group = a.tiles >= 8 ? (uint32_t)(a.tiles_padded / 8) : 0u;
+    a.div_tiles = make_fast_div((uint32_t)a.tiles_padded);
+    a.div_groups = make_fast_div((uint32_t)a.groups);
+    a.div_xcd = make_fast_div(a.xcd_group ? a.xcd_group : 1u);
+    // LDS rows of a power-of-two chunk count, so the per-token chunk rotation is a mask
+    a.row_chunks = next_pow2(C);
     a.vec_store = (N % 8 == 0) && aligned(q_out, 16) && aligned(k_out, 16) && aligned(v_out, 16);
     a.k_scale = k_scale;
-    const int lds_bytes = 2 * kCamTile * D * 2;
+    const int lds_bytes = 2 * kCamTile * a.row_chunks * 16;
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return fail(QKROPE_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(g.err));
     const hipError_t e = launch_cam(a, act_dtype == QKROPE_DTYPE_F16 ? kActF16 : kActBF16, cpl,

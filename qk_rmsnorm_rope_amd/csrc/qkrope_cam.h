@@ -31,12 +31,14 @@ struct CamArgs {
     int tiles;                      // token tiles per batch
     int tiles_padded;               // block-index stride of a (batch, group): tiles rounded up
     uint32_t xcd_group;             // as KernelArgs::xcd_group, over tile-fastest blocks
+    FastDiv div_tiles, div_groups, div_xcd;   // n / tiles_padded, n / groups, n / xcd_group
+    int row_chunks;                 // LDS tile row: 16-byte chunks, next power of two >= D/8
     int vec_store;                  // outputs take 16-byte stores (N % 8 == 0, aligned bases)
     float k_scale;
 };
 // cpl: 16-byte chunks per lane (1 for head_dim <= 64, else ceil(head_dim / 64), with 8 lanes per
 // token); threads = 64 * lanes_per_token;
-// lds_bytes = 2 * kCamTile * head_dim * 2.
+// lds_bytes = 2 * kCamTile * row_chunks * 16.
 hipError_t launch_cam(const CamArgs &args, int act, int cpl, int64_t blocks, int lds_bytes,
                       hipStream_t stream);
 

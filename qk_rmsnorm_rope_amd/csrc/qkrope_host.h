@@ -85,5 +85,16 @@ struct DeviceGuard {
     }
 };
 
+// Magic pair for n / d, 1 <= d, n < 2^31 (round-up method): with l = ceil(log2 d) and
+// m = floor(2^32 * (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l; the sum cannot
+// overflow 32 bits because mulhi(n, m) <= n < 2^31.
+inline FastDiv make_fast_div(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, l};
+}
+
 }  // namespace host
 }  // namespace qkrope

@@ -20,8 +20,9 @@
 //     the group's heads and tensors matters), then issues the 16-byte loads of all its chunks;
 //   * per head and tensor: ReLU (Q, K) on the packed 16-bit pairs (one integer max per two
 //     values), the K scale, the projection and the rotation in fp32, rounding to 16 bits, one
-//     16-byte LDS write of the chunk into the token's row of a [64 tokens][D] tile whose chunks
-//     are rotated by token/8 (so the column reads below hit distinct banks);
+//     16-byte LDS write of the chunk into the token's row of a [64 tokens][row_chunks] tile
+//     (D/8 chunks rounded up to a power of two) whose chunks are rotated by token/8 modulo
+//     row_chunks (so the column reads below hit distinct banks);
 //   * after a barrier, lane (row d, token segment s) gathers 8 consecutive tokens of dim d for
 //     one 16-byte store (issued after the last tensor): 8 lanes cover a row's 64-token run. The
 //     tile is double-buffered, one barrier per tensor;
@@ -68,22 +69,25 @@ __device__ __forceinline__ void project8(const float P[16], const float x[8], fl
 template <int ACT, int CPL, int LT>
 __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
 {
-    extern __shared__ __align__(16) uint8_t s_tile[];   // 2 x [64 tokens][D] 16-bit values
+    extern __shared__ __align__(16) uint8_t s_tile[];   // 2 x [64 tokens][row_chunks x 8] 16-bit
     const int tid = threadIdx.x;
     constexpr int NTH = 64 * LT;
 
+    // block -> (batch, head group, tile); uniform, with host-computed magic divisors
     uint32_t blk = blockIdx.x;
     if (a.xcd_group) {       // the grid is a whole number of 8*G runs: every block is remapped
         const uint32_t G = a.xcd_group, j = blk >> 3, x = blk & 7u;
-        blk = (j / G) * (8u * G) + x * G + j % G;
+        const uint32_t q = fast_div(j, a.div_xcd.m, a.div_xcd.l);
+        blk = q * (8u * G) + x * G + (j - q * G);
     }
-    const uint32_t tile = blk % (uint32_t)a.tiles_padded;
+    const uint32_t bg = fast_div(blk, a.div_tiles.m, a.div_tiles.l);
+    const uint32_t tile = blk - bg * (uint32_t)a.tiles_padded;
     if (tile >= (uint32_t)a.tiles) return;           // padding: no work (uniform)
-    const uint32_t bg = blk / (uint32_t)a.tiles_padded;
-    const uint32_t grp = bg % (uint32_t)a.groups;
-    const uint32_t b = bg / (uint32_t)a.groups;
+    const uint32_t b = fast_div(bg, a.div_groups.m, a.div_groups.l);
+    const uint32_t grp = bg - b * (uint32_t)a.groups;
 
     const int D = a.head_dim, C = D >> 3, H = a.heads;
+    const int CP = a.row_chunks, RS = CP * 8;    // LDS row: CP chunks, RS 16-bit elements
     const int64_t N = a.num_tokens;
     const int64_t n0 = (int64_t)tile * kCamTile;
     const int nvalid = (int)(N - n0 < kCamTile ? N - n0 : kCamTile);
@@ -141,7 +145,7 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
         const f32x4 sv = *reinterpret_cast<const f32x4 *>(a.sin_table + (n0 + nlc) * (D / 2) + 4 * chi[c]);
         tc[c][0] = cv.x; tc[c][1] = cv.y; tc[c][2] = cv.z; tc[c][3] = cv.w;
         ts[c][0] = sv.x; ts[c][1] = sv.y; ts[c][2] = sv.z; ts[c][3] = sv.w;
-        ldsw[c] = (uint32_t)(nl * D * 2 + ((chi[c] + (nl >> 3)) % C) * 16);
+        ldsw[c] = (uint32_t)(nl * RS * 2 + ((chi[c] + (nl >> 3)) & (CP - 1)) * 16);
     }
     // the lane's output units (row d, 8-token segment s), 8 * D of them, and their LDS reads
     int ud[CPL], us[CPL];
@@ -155,7 +159,7 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
         const int uu = uv[j] ? u : 0;
         us[j] = uu & 7;
         ud[j] = uu >> 3;
-        ldsr[j] = (uint32_t)((us[j] * 8 * D + (((ud[j] >> 3) + us[j]) % C) * 8 + (ud[j] & 7)) * 2);
+        ldsr[j] = (uint32_t)((us[j] * 8 * RS + (((ud[j] >> 3) + us[j]) & (CP - 1)) * 8 + (ud[j] & 7)) * 2);
         st_off[j] = (ud[j] * N + n0 + us[j] * 8) * 2;
     }
     // whole tiles of a row-aligned output: 16-byte stores, issued after the loop (measured
@@ -171,7 +175,7 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
     for (int i = 0; i < MI; ++i) {
         if (i >= iters) continue;          // uniform
         const int r = i % 3, h = h0 + i / 3;
-        uint8_t *buf = s_tile + (i & 1) * (kCamTile * D * 2);
+        uint8_t *buf = s_tile + (i & 1) * (kCamTile * RS * 2);
 
         float na = 0.0f, np = 0.0f;
 #pragma unroll
@@ -219,7 +223,7 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
             const uint16_t *src = reinterpret_cast<const uint16_t *>(buf + ldsr[j]);
             uint16_t e8[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) e8[k] = src[k * D];
+            for (int k = 0; k < 8; ++k) e8[k] = src[k * RS];
             if (fast) {
                 const uint4 w = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16,
                                            e8[4] | (uint32_t)e8[5] << 16, e8[6] | (uint32_t)e8[7] << 16);
