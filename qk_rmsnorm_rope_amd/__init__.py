@@ -165,6 +165,21 @@ def _same_device(device: torch.device, **tensors) -> None:
             raise ValueError(f"{name} must be a GPU tensor on {device}, got {t.device}")
 
 
+def _check_weight(w, need: int, dtype, name: str) -> None:
+    """A norm weight: contiguous, of `dtype`, holding at least the `need` elements the kernels
+    read (the C ABI takes a bare pointer, so its length is checked here)."""
+    if w is None or w.dtype != dtype or not w.is_contiguous() or w.numel() < need:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of at least {need} elements")
+
+
+def _weight_elems(norm_mode: str, heads: int, head_dim: int) -> int:
+    """Elements of one region's norm weight that a call reads: [head_dim] per head, [heads *
+    head_dim] across heads, none for a region without heads or without norm."""
+    if norm_mode == "none" or heads == 0:
+        return 0
+    return heads * head_dim if norm_mode == "across_heads" else head_dim
+
+
 def _rows(t: torch.Tensor, heads: int, head_dim: int, name: str) -> int:
     """Token stride (elements) of a [T, H, D] (or [T, H*D]) view with contiguous heads/dims."""
     if t.dim() == 3:
@@ -204,9 +219,11 @@ def qkrope_run_table(q, k, q_weight, k_weight, rope_table, eps, *, q_out, k_out,
         raise ValueError("rope_table must be a GPU [tokens, >= rotary_dim] tensor whose "
                          "columns are contiguous (unit stride along the last dim)")
     ts = rope_table.stride(0) if T > 1 else rope_table.shape[1]
-    for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
-        if norm_mode != "none" and (w is None or w.dtype != torch.bfloat16 or not w.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    if norm_mode not in NORM_MODES:
+        raise ValueError(f"norm_mode must be one of {sorted(NORM_MODES)}")
+    if norm_mode != "none":
+        for name, w, H in (("q_weight", q_weight, Hq), ("k_weight", k_weight, Hk)):
+            _check_weight(w, _weight_elems(norm_mode, H, D), torch.bfloat16, name)
     wq, wk = (q_weight, k_weight) if norm_mode != "none" else (None, None)
     _same_device(q.device, k=k, q_out=q_out, k_out=k_out, rope_table=rope_table, q_weight=wq,
                  k_weight=wk)
@@ -258,9 +275,11 @@ def qkrope_run_table_ex(q, k, q_weight, k_weight, cos_table, sin_table, eps, *, 
     R = rotary_dim if rotary_dim is not None else 2 * cos_table.shape[-1]
     cs = _table_cols(cos_table, T, R // 2, "cos_table")
     ss = _table_cols(sin_table, T, R // 2, "sin_table")
-    for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
-        if norm_mode != "none" and (w is None or w.dtype != q.dtype or not w.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous tensor of q's dtype")
+    if norm_mode not in NORM_MODES:
+        raise ValueError(f"norm_mode must be one of {sorted(NORM_MODES)}")
+    if norm_mode != "none":
+        for name, w, H in (("q_weight", q_weight, Hq), ("k_weight", k_weight, Hk)):
+            _check_weight(w, _weight_elems(norm_mode, H, D), q.dtype, name)
     wq, wk = (q_weight, k_weight) if norm_mode != "none" else (None, None)
     _same_device(q.device, k=k, q_out=q_out, k_out=k_out, cos_table=cos_table,
                  sin_table=sin_table, q_weight=wq, k_weight=wk)
@@ -319,9 +338,8 @@ def qkrope_run_3d_sharded(qkv, q_weight, k_weight, *, token_offset=0, sumsq=None
         raise ValueError("sumsq must be a contiguous float32 GPU tensor [tokens, 2]")
     _same_device(qkv.device, sumsq=sumsq)
     if is_qk_norm:
-        for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
-            if w is None or w.dtype != torch.bfloat16 or not w.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+        for name, w, H in (("q_weight", q_weight, num_heads_q), ("k_weight", k_weight, num_heads_k)):
+            _check_weight(w, _weight_elems("across_heads", H, head_dim), torch.bfloat16, name)
     _same_device(qkv.device, q_out=q_out, k_out=k_out, v_out=v_out,
                  q_weight=q_weight if is_qk_norm else None,
                  k_weight=k_weight if is_qk_norm else None)
@@ -356,9 +374,8 @@ def qkrope_run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
         if o.dtype != odt or not o.is_contiguous() or o.numel() != T * H * head_dim or not o.is_cuda:
             raise ValueError(f"{name} must be a contiguous {odt} GPU tensor of {T}x{H}x{head_dim}")
     if is_qk_norm:
-        for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
-            if w is None or w.dtype != torch.bfloat16 or not w.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+        for name, w, H in (("q_weight", q_weight, num_heads_q), ("k_weight", k_weight, num_heads_k)):
+            _check_weight(w, _weight_elems("across_heads", H, head_dim), torch.bfloat16, name)
     _same_device(qkv.device, q_out=q_out, k_out=k_out, v_out=v_out,
                  q_weight=q_weight if is_qk_norm else None,
                  k_weight=k_weight if is_qk_norm else None)

@@ -334,6 +334,21 @@ def test_contract_violations_raise_value_error():
     with pytest.raises(ValueError, match="unsupported"):
         qr.fused_qk_norm_rope(ti["q"], ti["k"], ti["q_weight"], ti["k_weight"], ti["rope_table"],
                               1e-6, rotary_dim=40, interleaved=False)
+    # norm weights shorter than what the kernels read are refused before any launch (the C ABI
+    # takes bare pointers): [heads * head_dim] across heads, [head_dim] per head
+    with pytest.raises(ValueError, match="q_weight"):
+        qr.fused_qk_rmsnorm_rope(qkv, wq[:-8], wk, **base)
+    with pytest.raises(ValueError, match="k_weight"):
+        qr.fused_qk_rmsnorm_rope(qkv, wq, wk[:128], **base)
+    t2 = t.with_(head_dim=64, rotary_dim=64, num_heads_q=2, num_heads_k=2)
+    t2i = {n: _gpu(v) for n, v in wl.table_inputs(t2).items()}
+    with pytest.raises(ValueError, match="k_weight"):
+        qr.fused_qk_norm_rope(t2i["q"], t2i["k"], t2i["q_weight"], t2i["k_weight"][:32],
+                              t2i["rope_table"], 1e-6)
+    with pytest.raises(ValueError, match="q_weight"):
+        qr.qkrope_run_table(t2i["q"], t2i["k"], t2i["q_weight"][:32], t2i["k_weight"],
+                            t2i["rope_table"].float(), 1e-6, q_out=torch.empty_like(t2i["q"]),
+                            k_out=torch.empty_like(t2i["k"]), norm_mode="across_heads")
 
 
 def test_single_hip_runtime_loaded():
