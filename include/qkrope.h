@@ -110,7 +110,9 @@ int qkrope_min_tokens(int64_t default_tokens, int64_t *out);
  *              overlap between an output and an input is QKROPE_ERR_INVALID.
  *
  * Limits (else QKROPE_ERR_UNSUPPORTED): head_dim a multiple of 8 and <= 256; num_tokens < 2^31;
- * q, k and output token strides multiples of 8 elements and < 2^28. Any even rotary_dim works with either pairing (half-split partners that straddle 16-byte
+ * q, k and output token strides multiples of 8 elements and < 2^28; heads * L <= 4096 for each
+ * of Q and K, L being head_dim / 8 rounded up to a power of two (e.g. 256 heads of 128). Any
+ * even rotary_dim works with either pairing (half-split partners that straddle 16-byte
  * chunks, i.e. rotary_dim % 16 != 0, are exchanged through LDS, a slower path).
  * num_tokens == 0 (or zero heads) is a valid no-op.
  */
@@ -181,8 +183,9 @@ int qkrope_run_table_ex(qkrope_handle h,
  *   q_out, k_out, v_out  [num_tokens, num_heads_x, head_dim], contiguous, and must not overlap
  *              qkv or each other.
  *
- * Limits (else QKROPE_ERR_UNSUPPORTED): num_tokens < 2^31; (Hq+Hk+Hv)*head_dim/8 <= 8192.
- * num_tokens == 0 is a valid no-op.
+ * Limits (else QKROPE_ERR_UNSUPPORTED): num_tokens < 2^31; one workgroup per token covers at
+ * most 2048 16-byte chunks (heads * head_dim / 8) in each of Q, K and V (e.g. 128 heads of 128
+ * in each), or 4096 in all three together. num_tokens == 0 is a valid no-op.
  */
 int qkrope_run_3d(qkrope_handle h,
                   const void *qkv, const void *q_weight, const void *k_weight, int64_t num_tokens,
