@@ -279,9 +279,16 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                   "a 16-bit table has the activation format");
     constexpr int ESIZE = FP8 ? 1 : 2;          // output bytes per element
 
-    // 3D angles of the token: per pair (cos, -sin, cos, sin), so a half-split lane reads its
-    // signed pair directly (first half: y = n cos - n' sin, second half: y = n cos + n' sin).
-    __shared__ f32x4 s_cs[IS3D ? TPW * kMaxPairs : 1];
+    // 3D angles of the token, in two planes: (cos, -sin) and (cos, sin) per pair, so a
+    // half-split lane reads its signed pair directly (first half: y = n cos - n' sin, second
+    // half: y = n cos + n' sin). A lane reads the NPAIR consecutive pairs from pair0 =
+    // NPAIR * g0; pair g * NPAIR + e sits at row e, column g of a plane (rows padded to an odd
+    // stride CSR), so for each e the lanes of a wave read consecutive 8-byte words (no bank
+    // conflicts; a pair-major table put the lanes 64-128 bytes apart, 8- to 16-way conflicts),
+    // and the writing lanes (pair tl) spread over the banks too.
+    constexpr int CSR = kMaxPairs / NPAIR + 1;  // row stride of a plane, f32x2
+    constexpr int CSP = NPAIR * CSR;            // one plane
+    __shared__ f32x2 s_cs[IS3D ? TPW * 2 * CSP : 1];
     __shared__ f32x2 s_red[32];
     // kPairHalfAny: one area of 64 lanes x 8 floats per wave (launched with threads * 32 bytes)
     extern __shared__ float s_xch[];
@@ -456,7 +463,10 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                     const float rev = __builtin_amdgcn_fractf((float)pos * omega_rev);
                     const float c = __builtin_amdgcn_cosf(rev) * a.attention_factor;
                     const float sn = __builtin_amdgcn_sinf(rev) * a.attention_factor;
-                    s_cs[ts * kMaxPairs + tl] = f32x4{c, -sn, c, sn};
+                    f32x2 *cs_tok = s_cs + ts * 2 * CSP;
+                    const int slot = (tl % NPAIR) * CSR + tl / NPAIR;
+                    cs_tok[CSP + slot] = f32x2{c, sn};
+                    if (HALF) cs_tok[slot] = f32x2{c, -sn};
                 }
             }
         } else if (XCH) {
@@ -628,12 +638,13 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             rk = __builtin_amdgcn_rsqf(sk * a.inv_count[1] + a.eps);
         }
         if (IS3D && unit_ok && !v_wg) {
-            // interleaved and second-half lanes read (cos, sin), first-half lanes (cos, -sin)
-            const f32x2 *tab = reinterpret_cast<const f32x2 *>(s_cs + ts * kMaxPairs) +
-                               (HALF && half_sign < 0.0f ? 0 : 1);
+            // interleaved and second-half lanes read (cos, sin), first-half lanes (cos, -sin);
+            // pair0 is a multiple of NPAIR here
+            const f32x2 *tab = s_cs + ts * 2 * CSP + (HALF && half_sign < 0.0f ? 0 : CSP) +
+                               pair0 / NPAIR;
 #pragma unroll
             for (int e = 0; e < NPAIR; ++e) {
-                const f32x2 cs = tab[2 * (pair0 + e)];
+                const f32x2 cs = tab[e * CSR];
                 cs_c[e] = cs.x;
                 cs_s[e] = cs.y;
             }
