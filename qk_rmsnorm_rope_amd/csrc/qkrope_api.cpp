@@ -120,15 +120,16 @@ bool choose_shape(const int64_t *n, int nreg, int min_lanes, LaunchShape *s)
 
 // One region (Q, K or V) of one token per workgroup instead of all of a token's regions in one
 // workgroup: lanes hold one 16-byte chunk each and a token's three workgroups run side by side.
-// Measured on MI355X (graph replay, 512-lane regions, conflict-free angle table), 3D form with
-// 16-bit outputs: 15360 tokens x 3x32 x 128 with the across-heads norm 77.2% -> 77.45% of
-// 8 TB/s, without norm 78.2% -> 81.1%; 122880 x 3x16 x 256 without norm 77.6% -> 78.6%, with
-// it 75.35% -> 75.8%, half-split pairs without norm 76.85% -> 78.65%. With E4M3 outputs
-// (79.3% -> 75.5%) and in the table form (80% -> 68%) one workgroup per token stays faster.
+// Measured on MI355X (graph replay, 512-lane regions), 3D form without norm and with 16-bit
+// outputs: 15360 tokens x 3x32 x 128 78.2% -> 81.1% of 8 TB/s, 122880 x 3x16 x 256 77.6% ->
+// 78.6%, the same with half-split pairs 76.85% -> 78.65%. With the across-heads norm the gain
+// was within noise from a graph (77.2% -> 77.45%) and a loss with per-launch dispatch (76.2% ->
+// 74.3%: three times the workgroups); with E4M3 outputs (79.3% -> 75.5%) and in the table form
+// (80% -> 68%) one workgroup per token is faster.
 bool split_regions(const LaunchShape &s, const KernelKey &k)
 {
-    return k.src == kSrc3D && (k.norm == kNormNone || k.norm == kNormAcross) && !k.fp8 &&
-           s.slot_uniform && s.tpw == 1 && s.slots == 1 && s.threads >= 512;
+    return k.src == kSrc3D && k.norm == kNormNone && !k.fp8 && s.slot_uniform && s.tpw == 1 &&
+           s.slots == 1 && s.threads >= 512;
 }
 
 // Token-block order across XCDs (KernelArgs::xcd_group). Workgroups are dealt to the 8 XCDs

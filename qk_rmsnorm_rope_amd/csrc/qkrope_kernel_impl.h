@@ -260,8 +260,8 @@ __device__ __forceinline__ float sumsq_packed(const uint4 v, float acc)
 // TPW: tokens per workgroup, 1, or 2 (region-major, one slot per region) when a token needs a
 // multiple of 32 but not of 64 lanes, so that two tokens fill whole waves.
 // RS: one region (Q, K or V) of one token per workgroup, NS slots; workgroup b takes region
-// b mod NREG of token b / NREG (in XCD order). Launched for the 3D form with 16-bit outputs
-// (no norm or the across-heads norm, either pairing).
+// b mod NREG of token b / NREG (in XCD order). Launched for the 3D form without norm and with
+// 16-bit outputs (either pairing), where every workgroup only streams.
 template <int DT, int PAIR, int NORM, int SRC, int ACT, bool FP8, int NS, bool SU, int TPW, bool RS>
 __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 {
@@ -597,11 +597,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                 sq += reg[j] == kQ ? ss[j] : 0.0f;
                 sk += reg[j] == kK ? ss[j] : 0.0f;
             }
-            if (RS) {
-                // one region: its sum alone (the other is zero)
-                const float sx = wave_sum(sq + sk);
-                if ((tid & 63) == 0) s_red[tid >> 6] = f32x2{sx, sx};
-            } else if (TPW == 1) {
+            if (TPW == 1) {
                 sq = wave_sum(sq);
                 sk = wave_sum(sk);
                 if ((tid & 63) == 0) s_red[tid >> 6] = f32x2{sq, sk};
@@ -627,11 +623,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             // every wave sums its token's partials: one token, lane w of each 16-lane row reads
             // wave w's; two tokens, lane w of each 32-lane group reads its token's group w
             float sq, sk;
-            if (RS) {
-                const int w = tid & 15;
-                const float p = w < (nth >> 6) ? s_red[w].x : 0.0f;
-                sq = sk = group_sum(p, 16);
-            } else if (TPW == 1) {
+            if (TPW == 1) {
                 const int w = tid & 15;
                 const f32x2 p = w < (nth >> 6) ? s_red[w] : f32x2{0.0f, 0.0f};
                 sq = group_sum(p.x, 16);
@@ -817,8 +809,7 @@ hipError_t go_if(const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if constexpr (slots_compiled(SRC == kSrc3D ? 3 : 2, SU, NS)) {
         if (s.split) {
-            if constexpr (SU && NS == 1 && SRC == kSrc3D &&
-                          (NORM == kNormNone || NORM == kNormAcross) && !FP8) {
+            if constexpr (SU && NS == 1 && SRC == kSrc3D && NORM == kNormNone && !FP8) {
                 if (s.tpw != 1) return hipErrorInvalidValue;
                 return go<DT, PAIR, NORM, SRC, ACT, FP8, NS, SU, 1, true>(s, a, st);
             } else {
