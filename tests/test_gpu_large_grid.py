@@ -94,3 +94,23 @@ def test_3d_form_past_one_grid():
                                num_heads_v=1, head_dim=64)
     got = sums[torch.as_tensor(tokens, device=DEV)].cpu().numpy()
     np.testing.assert_allclose(got, ref_sums, rtol=1e-5)
+    del outs
+    torch.cuda.empty_cache()
+    # the head-sharded apply over the same tokens, from global token 5 on, with the sums above:
+    # each launch reads its own range of the sums and continues the positions
+    off = 5
+    so = [torch.empty((T, 1, 64), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    print("sharded apply", flush=True)
+    qr.qkrope_run_3d_sharded(qkv.view(T, -1), wq, wk, token_offset=off, sumsq=sums,
+                             norm_elems_q=64, norm_elems_k=64, ppf=big.ppf, pph=big.pph,
+                             ppw=big.ppw, num_frame_channels=big.num_frame_channels,
+                             num_height_channels=big.num_height_channels,
+                             num_width_channels=big.num_width_channels, num_heads_q=1,
+                             num_heads_k=1, num_heads_v=1, head_dim=64, eps=big.eps,
+                             base=big.base, interleave=big.interleave, q_out=so[0], k_out=so[1],
+                             v_out=so[2])
+    torch.cuda.synchronize()
+    parts = [oracle.run_3d_workload(big, block[t % BLOCK:t % BLOCK + 1], inp["q_weight"],
+                                    inp["k_weight"], token_offset=int(t) + off) for t in tokens]
+    ref = tuple(np.concatenate([p[i] for p in parts]) for i in range(3))
+    check_3d_outputs(big, so, ref, tokens=tokens)
