@@ -159,6 +159,30 @@ def test_3d_fp8_saturation_and_non_power_of_two_v_scale():
     check_3d_outputs(w, run_3d(w, inputs), oracle_3d(w, inputs))
 
 
+@pytest.mark.parametrize("v_scale", [0.125, 0.25, 4.0])
+def test_3d_fp8_v_power_of_two_scale_edges(v_scale):
+    """E4M3 of V with a power-of-two scale is exact scaling then one rounding, so its codes must
+    equal the oracle's bit for bit, also where they saturate (sigma 300 puts many values past
+    448 / s at s = 4, few at s = 0.125) and at planted infinities, zeros, the limit 448 / s
+    itself, the next bf16 value above it, the smallest subnormal result and a rounding tie
+    between subnormal codes."""
+    w = wl.ROPE3D_NEOX_FP8_S18480.with_(ppf=1, pph=2, ppw=4, batch=2, sigma=300.0,
+                                       output_quant_scale=0.5, v_quant_scale=v_scale)
+    inputs = wl.rope3d_inputs(w)
+    x = inputs["qkv"].reshape(w.num_tokens, w.row_elems).clone()
+    lim = 448.0 / v_scale
+    above = torch.tensor([lim], dtype=torch.bfloat16).view(torch.int16) + 1
+    edge = torch.tensor([float("inf"), float("-inf"), 0.0, -0.0, lim, -lim,
+                         2.0 ** -9 / v_scale, 1.5 * 2.0 ** -9 / v_scale], dtype=torch.bfloat16)
+    voff = (w.num_heads_q + w.num_heads_k) * w.head_dim
+    x[0, voff:voff + 8] = edge                                   # one chunk over the limit (inf)
+    x[1, voff:voff + 8] = edge[2:].repeat(2)[:8]                 # within it: fast path, at lim
+    x[2, voff + 8:voff + 16] = above.view(torch.bfloat16).repeat(8)   # just above the limit
+    x[3, voff:voff + 8] = (edge[6:8] * 3).repeat(4)             # small codes only
+    inputs["qkv"] = x.reshape(inputs["qkv"].shape)
+    check_3d_outputs(w, run_3d(w, inputs), oracle_3d(w, inputs))
+
+
 # --- seeded sweep over the table contract -------------------------------------------------------
 
 SWEEP_TABLE = [
