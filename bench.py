@@ -48,13 +48,17 @@ CAM_SOURCES = [_CSRC + "qkrope_cam.h", _CSRC + "qkrope_api_cam.cpp",
                _CSRC + "qkrope_kernels_cam.hip"]
 
 
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_source_hash(w=None) -> str:
-    """Hash of the sources that decide a workload's kernel and launch shape."""
+    """Hash of the code of the sources that decide a workload's kernel and launch shape, with
+    comments and whitespace dropped (a record survives an edit of comments only)."""
     h = hashlib.sha256()
     cam = w is not None and is_cam(w)
     for rel in COMMON_SOURCES + (CAM_SOURCES if cam else PROLOGUE_SOURCES):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update("".join(_COMMENTS.sub(" ", f.read()).split()).encode())
     return h.hexdigest()[:16]
 
 

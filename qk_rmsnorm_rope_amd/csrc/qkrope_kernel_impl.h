@@ -13,11 +13,12 @@
 // Work decomposition (MI355X-first; the pages give no kernel design for this hardware):
 //   * The operation is HBM-bound (a few flops per byte), so the design goal is 16-byte coalesced
 //     loads and stores with many bytes in flight, and little ALU work per byte.
-//   * One workgroup per token (two when a token fills only half a wave's multiple, see TPW).
-//     On MI355X the hardware's own workgroup scheduling hides memory latency better than a
-//     software-pipelined walk over several tokens per workgroup, which measured slower at every
-//     depth tried. Large grids deal runs of 16 consecutive token blocks to each XCD
-//     (KernelArgs::xcd_group).
+//   * One workgroup per token (two when a token fills only half a wave's multiple, see TPW; one
+//     per region of a token in the 3D form without norm, see RS). On MI355X the hardware's own
+//     workgroup scheduling hides memory latency better than a software-pipelined walk over
+//     several tokens per workgroup, which measured slower at every depth tried. Large grids
+//     deal runs of 16 consecutive token blocks to each XCD (KernelArgs::xcd_group); a call
+//     whose grid would exceed one dispatch runs as several launches over token ranges (host).
 //   * A token's Q, K (and V) rows are cut into units of one 16-byte chunk (8 bf16), so every
 //     load and store instruction of a wave covers whole contiguous cache lines. Interleaved
 //     pairs never leave a chunk. Half-split/NeoX pairs (d, d + R/2) join chunk c with chunk
