@@ -138,7 +138,8 @@ int qkrope_run_table(qkrope_handle h,
  *     table_dtype is QKROPE_DTYPE_F32 or equal to act_dtype.
  *   - out_dtype equal to act_dtype (each output rounded once, to nearest even), or
  *     QKROPE_DTYPE_E4M3: outputs are OCP E4M3 bytes of y * out_scale (round to nearest even,
- *     finite overflow saturating to +-448, NaN kept), as the 3D form's output_fp8 does; then
+ *     finite overflow and infinities saturating to +-448, a NaN giving the NaN code 0xFF),
+ *     as the 3D form's output_fp8 does; then
  *     out_scale must be finite and > 0 (it is ignored otherwise), the output token strides count
  *     bytes, outputs must be 8-byte aligned, and no output may alias an input.
  * In-place use (q_out == q with equal strides) needs out_dtype == act_dtype. Other arguments,
@@ -179,7 +180,9 @@ int qkrope_run_table_ex(qkrope_handle h,
  *              attention_factor.
  *   output_fp8 0: q_out/k_out/v_out are bf16; V is a bit copy.
  *              1: they are OCP E4M3 bytes: Q/K = e4m3(y * output_quant_scale),
- *              V = e4m3(v * v_quant_scale); scales must be finite and > 0.
+ *              V = e4m3(v * v_quant_scale), round to nearest even, finite overflow and
+ *              infinities saturating to +-448, a NaN giving the NaN code 0xFF (the hardware
+ *              conversion's, whatever the NaN's sign); scales must be finite and > 0.
  *   q_out, k_out, v_out  [num_tokens, num_heads_x, head_dim], contiguous, and must not overlap
  *              qkv or each other.
  *

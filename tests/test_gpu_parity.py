@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle
-from parity import assert_bf16_close, check_3d_outputs, check_table_outputs
+from parity import (assert_bf16_close, assert_bits_equal, assert_e4m3_within_one,
+                    check_3d_outputs, check_table_outputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -181,6 +182,45 @@ def test_3d_fp8_v_power_of_two_scale_edges(v_scale):
     x[3, voff:voff + 8] = (edge[6:8] * 3).repeat(4)             # small codes only
     inputs["qkv"] = x.reshape(inputs["qkv"].shape)
     check_3d_outputs(w, run_3d(w, inputs), oracle_3d(w, inputs))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_3d_nan_inputs_propagate(fp8):
+    """A NaN in a token's K row makes its across-heads norm NaN, so every K output of that token
+    is NaN (E4M3: the NaN code); a NaN in V stays in its own element; every other token and
+    element matches the oracle as usual."""
+    w = wl.ROPE3D_NEOX_FP8_S18480.with_(ppf=1, pph=2, ppw=4, batch=2, output_fp8=fp8)
+    inputs = wl.rope3d_inputs(w)
+    x = inputs["qkv"].reshape(w.num_tokens, w.row_elems).clone()
+    D, Hq, Hk = w.head_dim, w.num_heads_q, w.num_heads_k
+    x[3, Hq * D + 5] = float("nan")                         # token 3, K
+    x[6, (Hq + Hk) * D + 17] = float("nan")                 # token 6, V element 17
+    inputs["qkv"] = x.reshape(inputs["qkv"].shape)
+    outs = [o.reshape(w.num_tokens, -1) for o in run_3d(w, inputs)]
+    ref = oracle_3d(w, inputs)
+
+    def is_nan(o):
+        if fp8:
+            return (o.view(torch.uint8).cpu() & 0x7F) == 0x7F
+        return torch.isnan(o.float().cpu())
+
+    assert bool(is_nan(outs[1][3]).all()), "every K output of the NaN token"
+    v_nan = is_nan(outs[2][6])
+    assert bool(v_nan[17]) and int(v_nan.sum()) == 1, "V: only the NaN element"
+    assert not bool(is_nan(outs[0]).any()), "Q has no NaN"
+    keep = [t for t in range(w.num_tokens) if t not in (3, 6)]
+    check = [o[keep] for o in outs]
+    refs = [r.reshape(w.num_tokens, -1)[keep] for r in ref]
+    names = ("q", "k", "v")
+    for i in range(3):
+        if fp8:
+            scale = w.v_quant_scale if i == 2 else w.output_quant_scale
+            codes = oracle.e4m3_encode(refs[i], scale)
+            (assert_bits_equal if i == 2 else assert_e4m3_within_one)(check[i], codes, names[i])
+        elif i == 2:
+            assert_bits_equal(check[i], oracle.bf16_encode(refs[i]), names[i])
+        else:
+            assert_bf16_close(check[i], refs[i], names[i])
 
 
 # --- seeded sweep over the table contract -------------------------------------------------------
