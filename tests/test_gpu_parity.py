@@ -223,6 +223,42 @@ def test_3d_nan_inputs_propagate(fp8):
             assert_bf16_close(check[i], refs[i], names[i])
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_3d_zero_rows(fp8):
+    """Rows of zeros are a degenerate case of the norm (mean of squares 0, scale eps^-1/2): their
+    outputs are zeros, exactly as the oracle's, in both output formats."""
+    w = wl.ROPE3D_ACROSS_S15360.with_(ppf=1, pph=2, ppw=4, batch=2, output_fp8=fp8,
+                                     output_quant_scale=0.5, v_quant_scale=0.25)
+    inputs = wl.rope3d_inputs(w)
+    x = inputs["qkv"].reshape(w.num_tokens, w.row_elems).clone()
+    qd, kd = w.num_heads_q * w.head_dim, w.num_heads_k * w.head_dim
+    x[2, :qd] = 0                         # token 2: Q row
+    x[5, qd:qd + kd] = 0                  # token 5: K row
+    x[7] = 0                              # token 7: everything
+    inputs["qkv"] = x.reshape(inputs["qkv"].shape)
+    outs = run_3d(w, inputs)
+    check_3d_outputs(w, outs, oracle_3d(w, inputs))
+    flat = [o.reshape(w.num_tokens, -1).view(torch.uint8 if fp8 else torch.int16) for o in outs]
+    zero = 0
+    assert bool((flat[0][2] & (0x7F if fp8 else 0x7FFF) == zero).all())
+    assert bool((flat[1][5] & (0x7F if fp8 else 0x7FFF) == zero).all())
+    assert all(bool((f[7] & (0x7F if fp8 else 0x7FFF) == zero).all()) for f in flat)
+
+
+def test_table_zero_heads():
+    """Per-head norm with a head of zeros, and a token of zeros: zeros out, like the oracle."""
+    w = wl.TABLE_INTERLEAVED_T4096.with_(num_tokens=40)
+    inputs = wl.table_inputs(w)
+    inputs["q"] = inputs["q"].clone()
+    inputs["k"] = inputs["k"].clone()
+    inputs["q"][3, 5] = 0
+    inputs["k"][9] = 0
+    qo, ko = run_table(w, inputs)
+    check_table_outputs(w.name, qo, ko, *oracle_table(w, inputs))
+    assert bool((qo[3, 5].view(torch.int16) & 0x7FFF == 0).all())
+    assert bool((ko[9].view(torch.int16) & 0x7FFF == 0).all())
+
+
 # --- seeded sweep over the table contract -------------------------------------------------------
 
 SWEEP_TABLE = [
