@@ -167,7 +167,10 @@ def _same_device(device: torch.device, **tensors) -> None:
 
 def _check_weight(w, need: int, dtype, name: str) -> None:
     """A norm weight: contiguous, of `dtype`, holding at least the `need` elements the kernels
-    read (the C ABI takes a bare pointer, so its length is checked here)."""
+    read (the C ABI takes a bare pointer, so its length is checked here). A region that reads
+    none (no heads) may pass None."""
+    if w is None and need == 0:
+        return
     if w is None or w.dtype != dtype or not w.is_contiguous() or w.numel() < need:
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of at least {need} elements")
 

@@ -114,3 +114,22 @@ def test_binding_refuses_host_tensors_before_any_call():
     o = [torch.zeros(1, 2, 64, 8, dtype=torch.bfloat16) for _ in range(3)]
     with pytest.raises(ValueError, match="GPU"):
         qr.qkrope_cam_prep(x, x, x, P, P, t, t, 1.0, q_out=o[0], k_out=o[1], v_out=o[2])
+
+
+def test_binding_weight_checks():
+    """The C ABI takes weights as bare pointers, so the binding checks their length and dtype;
+    a region without heads reads no weight and may pass None."""
+    import torch
+    import qk_rmsnorm_rope_amd as qr
+    qr._check_weight(None, 0, torch.bfloat16, "k_weight")
+    qr._check_weight(torch.ones(128, dtype=torch.bfloat16), 128, torch.bfloat16, "q_weight")
+    for w, need, dt in ((None, 1, torch.bfloat16),
+                        (torch.ones(127, dtype=torch.bfloat16), 128, torch.bfloat16),
+                        (torch.ones(128, dtype=torch.float32), 128, torch.bfloat16),
+                        (torch.ones(256, dtype=torch.bfloat16)[::2], 128, torch.bfloat16)):
+        with pytest.raises(ValueError, match="q_weight"):
+            qr._check_weight(w, need, dt, "q_weight")
+    assert qr._weight_elems("none", 8, 128) == 0
+    assert qr._weight_elems("per_head", 0, 128) == 0
+    assert qr._weight_elems("per_head", 8, 128) == 128
+    assert qr._weight_elems("across_heads", 8, 128) == 1024

@@ -364,14 +364,18 @@ def test_sharded_contract():
 
 # --- regions without heads (their tensors may be empty, with NULL data pointers) ----------------
 
+@pytest.mark.parametrize("none_weight", [False, True], ids=["empty_weight", "none_weight"])
 @pytest.mark.parametrize("hq,hk,inter,mode", [(0, 27, True, "across_heads"), (5, 0, False, "across_heads"),
                                               (0, 9, False, "per_head"), (12, 0, True, "none")])
-def test_table_empty_region_null_pointers(hq, hk, inter, mode):
+def test_table_empty_region_null_pointers(hq, hk, inter, mode, none_weight):
     w = table_workload(153, hq, hk, 200, 146 if inter else 96, inter, mode, "bf16", "bf16",
                        seed=4700 + hq + hk)
     inp = wl.table_inputs(w)
     g = {k: _gpu(v) for k, v in inp.items()}
     assert (g["q"].data_ptr() == 0) == (hq == 0) and (g["k"].data_ptr() == 0) == (hk == 0)
+    if none_weight:         # the weight of a region without heads may also be None
+        g["q_weight"] = g["q_weight"] if hq else None
+        g["k_weight"] = g["k_weight"] if hk else None
     qo, ko = torch.empty_like(g["q"]), torch.empty_like(g["k"])
     R = w.rotary_dim
     qr.qkrope_run_table_ex(g["q"], g["k"], g["q_weight"], g["k_weight"],
@@ -385,9 +389,10 @@ def test_table_empty_region_null_pointers(hq, hk, inter, mode):
         assert_bf16_close(ko, rk, "k")
 
 
+@pytest.mark.parametrize("none_weight", [False, True], ids=["empty_weight", "none_weight"])
 @pytest.mark.parametrize("H,norm", [((0, 0, 6), True), ((4, 0, 0), True), ((0, 3, 0), True),
                                     ((0, 5, 2), True)])
-def test_3d_empty_regions_null_weights(H, norm):
+def test_3d_empty_regions_null_weights(H, norm, none_weight):
     w = wl.Rope3DWorkload(name="empty3d", batch=2, ppf=2, pph=3, ppw=5, num_frame_channels=32,
                           num_height_channels=48, num_width_channels=48, num_heads_q=H[0],
                           num_heads_k=H[1], num_heads_v=H[2], head_dim=128, seed=4800 + sum(H),
@@ -395,6 +400,8 @@ def test_3d_empty_regions_null_weights(H, norm):
     inp = wl.rope3d_inputs(w)
     qkv, wq, wk = (_gpu(inp[k]) for k in ("qkv", "q_weight", "k_weight"))
     assert (wq.data_ptr() == 0) == (H[0] == 0) and (wk.data_ptr() == 0) == (H[1] == 0)
+    if none_weight:
+        wq, wk = (wq if H[0] else None), (wk if H[1] else None)
     outs = qr.run_workload_3d(w, qkv, wq, wk)
     torch.cuda.synchronize()
     ref = oracle.run_3d_workload(w, inp["qkv"].reshape(-1, w.row_elems), inp["q_weight"],
