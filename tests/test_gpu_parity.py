@@ -455,3 +455,33 @@ def test_single_hip_runtime_loaded():
     qr.lib()
     runtimes = qr._hip_runtimes_loaded()
     assert len(runtimes) == 1, runtimes
+
+
+@pytest.mark.parametrize("factor,base,inter,fp8", [
+    (0.5, 10000.0, True, False),     # YaRN compressing positions the other way (factor < 1)
+    (0.25, 3.0, False, True),        # and with a small base: angles of many turns
+    (1.0, 0.5, True, False),         # base < 1: frequencies above one radian per position
+    (3.0, 1.5, False, False),
+], ids=lambda v: str(v))
+def test_3d_yarn_factor_below_one_and_small_bases(factor, base, inter, fp8):
+    """The contract takes any factor > 0 and base > 0; a factor below one raises the blended
+    frequencies, and a small base gives angles of many turns (up to about 12 along the 40
+    width positions), whose reduction to the period must hold to the usual tolerance at every
+    position of a 6 x 7 x 40 grid."""
+    yarn = factor != 1.0
+    w = wl.Rope3DWorkload(name="yarn_edges", batch=2, ppf=6, pph=7, ppw=40,
+                          num_frame_channels=32, num_height_channels=48, num_width_channels=48,
+                          num_heads_q=6, num_heads_k=3, num_heads_v=2, head_dim=128,
+                          seed=wl.SEED_BASE + 520, interleave=inter, base=base, factor=factor,
+                          low=1.0 if yarn else 0.0, high=20.0 if yarn else 0.0,
+                          attention_factor=0.9 if yarn else 1.0, output_fp8=fp8,
+                          output_quant_scale=0.75 if fp8 else 1.0,
+                          v_quant_scale=1.5 if fp8 else 1.0)
+    inp = wl.rope3d_inputs(w)
+    qkv, wq, wk = (inp[k].to(DEV) for k in ("qkv", "q_weight", "k_weight"))
+    print(f"\nfactor {factor} base {base} interleave {inter} fp8 {fp8}", flush=True)
+    outs = qr.run_workload_3d(w, qkv, wq, wk)
+    torch.cuda.synchronize()
+    ref = oracle.run_3d_workload(w, inp["qkv"].reshape(-1, w.row_elems), inp["q_weight"],
+                                 inp["k_weight"])
+    check_3d_outputs(w, outs, ref)
