@@ -362,6 +362,31 @@ def test_sharded_contract():
     assert_bf16_close(o5[0], ref[0], "q of a 5-token shard at offset 3")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_sharded_largest_token_offset(fp8):
+    """Positions come from (token_offset + t) split by the grid with magic divisors that hold
+    for indices below 2^31: a shard ending at global index 2^31 - 1, on a 3 x 5 x 7 grid."""
+    w = wl.Rope3DWorkload(name="offset_top", batch=1, ppf=3, pph=5, ppw=7,
+                          num_frame_channels=16, num_height_channels=24, num_width_channels=24,
+                          num_heads_q=3, num_heads_k=2, num_heads_v=1, head_dim=64,
+                          seed=wl.SEED_BASE + 530, output_fp8=fp8,
+                          output_quant_scale=0.5 if fp8 else 1.0,
+                          v_quant_scale=2.0 if fp8 else 1.0)
+    inp = wl.rope3d_inputs(w)
+    qkv, wq, wk = (_gpu(inp[k]) for k in ("qkv", "q_weight", "k_weight"))
+    T = w.num_tokens
+    off = (1 << 31) - 1 - T
+    o = _outs(T, w, w.num_heads_q, w.num_heads_k, w.num_heads_v)
+    qr.qkrope_run_3d_sharded(qkv.reshape(T, -1), wq, wk, token_offset=off,
+                             num_heads_q=w.num_heads_q, num_heads_k=w.num_heads_k,
+                             num_heads_v=w.num_heads_v, q_out=o[0], k_out=o[1], v_out=o[2],
+                             **_kw(w))
+    torch.cuda.synchronize()
+    ref = oracle.run_3d_workload(w, inp["qkv"].reshape(T, -1), inp["q_weight"],
+                                 inp["k_weight"], token_offset=off)
+    check_3d_outputs(w, o, ref)
+
+
 # --- regions without heads (their tensors may be empty, with NULL data pointers) ----------------
 
 @pytest.mark.parametrize("none_weight", [False, True], ids=["empty_weight", "none_weight"])
