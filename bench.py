@@ -409,8 +409,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the prologue is token-local and this build runs on a "
-              "single MI355X (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the prologue is token-local and the library runs on "
+              "a single MI355X (no multi-GPU path); use --gpus 1", file=sys.stderr)
         return 2
 
     import torch
