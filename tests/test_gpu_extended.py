@@ -494,6 +494,60 @@ def test_graph_capture_and_replay():
             assert torch.equal(t, r), f"replay {rep}"
 
 
+def test_graph_replay_sharded_step_and_e4m3_outputs():
+    """The two-kernel sharded step (sums of squares, then the apply that reads them), the FP8
+    3D form and the split-table form with E4M3 outputs, captured in one HIP graph: every replay,
+    with the outputs and the sums cleared eagerly in between, matches the eager launch bit for
+    bit."""
+    ws = wl.ROPE3D_ACROSS_S15360_TP4.with_(ppf=1, pph=4)
+    w8 = wl.ROPE3D_NEOX_FP8_S18480.with_(ppf=1, pph=4)
+    wt = table_workload(333, 6, 2, 128, 128, False, "per_head", "bf16", "f32", seed=4900,
+                        out_dtype="e4m3", out_scale=0.8)
+    i_s = {k: _gpu(v) for k, v in wl.rope3d_inputs(ws).items()}
+    i8 = {k: _gpu(v) for k, v in wl.rope3d_inputs(w8).items()}
+    it = {k: _gpu(v) for k, v in wl.table_inputs(wt).items()}
+    Ts = ws.num_tokens
+    so = _outs(Ts, ws, ws.num_heads_q, ws.num_heads_k, ws.num_heads_v)
+    sums = torch.empty((Ts, 2), dtype=torch.float32, device=DEV)
+    o8 = qr.run_workload_3d(w8, i8["qkv"], i8["q_weight"], i8["k_weight"])
+    f8 = torch.float8_e4m3fn
+    qo = torch.empty(it["q"].shape, dtype=f8, device=DEV)
+    ko = torch.empty(it["k"].shape, dtype=f8, device=DEV)
+    R = wt.rotary_dim
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):      # the prepared step keeps the stream current at its creation
+        prep = qr.PreparedSharded3D(ws, i_s["qkv"], i_s["q_weight"], i_s["k_weight"], *so, sums,
+                                    sums)
+
+    def eager():
+        prep()
+        qr.run_workload_3d(w8, i8["qkv"], i8["q_weight"], i8["k_weight"], *o8)
+        qr.qkrope_run_table_ex(it["q"], it["k"], it["q_weight"], it["k_weight"],
+                               it["rope_table"][:, : R // 2], it["rope_table"][:, R // 2: R],
+                               wt.eps, q_out=qo, k_out=ko, rotary_dim=R, interleaved=False,
+                               out_scale=wt.out_scale)
+
+    outs = (*so, sums, *o8, qo, ko)
+    with torch.cuda.stream(s):
+        eager()
+    torch.cuda.synchronize()
+    ref = [t.view(torch.uint8).clone() if t.dtype == f8 else t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            eager()
+    for rep in range(4):
+        for t in outs:
+            (t.view(torch.uint8) if t.dtype == f8 else t).zero_()    # eager work between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, ref):
+            got = t.view(torch.uint8) if t.dtype == f8 else t
+            assert torch.equal(got, r), f"replay {rep}"
+
+
 def test_host_tensor_arguments_are_refused():
     """A host tensor among GPU ones (weights, tables, outputs, matrices) raises before launch."""
     wt = wl.TABLE_INTERLEAVED_T4096.with_(num_tokens=64)
