@@ -15,8 +15,13 @@
  *       optional FP8 E4M3 outputs.
  *
  * Conventions shared by every entry point:
- *   - All functions return a qkrope_status. On any status other than QKROPE_OK nothing has been
- *     launched, and qkrope_last_error() returns a message for the calling thread.
+ *   - All functions return a qkrope_status, and on any status other than QKROPE_OK
+ *     qkrope_last_error() returns a message for the calling thread. QKROPE_ERR_INVALID and
+ *     QKROPE_ERR_UNSUPPORTED are found before anything is launched. A call whose grid would
+ *     exceed one dispatch (2^32 - 1 lanes, e.g. past 2^26 tokens with 64-lane workgroups) runs
+ *     as several launches over consecutive token ranges, in order on `stream`. A
+ *     QKROPE_ERR_DEVICE from one of those launches leaves the earlier ranges enqueued and the
+ *     later ones not.
  *   - Tensor pointers are DEVICE pointers, owned by the caller. The library never allocates,
  *     frees, or synchronises on them; it only enqueues work on `stream` (a hipStream_t; NULL is
  *     the default stream) and returns. A kernel fault therefore surfaces at the caller's next
