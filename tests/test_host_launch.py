@@ -1,0 +1,209 @@
+"""The host side of the C ABI (qkrope_api.cpp) on the CPU: launch shapes and launch loops.
+
+A small C++ program compiles the library's own host source with the kernel launchers and the
+few HIP runtime calls it makes replaced by stubs that record each launch (its kernel key,
+launch shape, token range and input offset) instead of running it. The entry points then run
+unchanged on fake, never-dereferenced device addresses. This pins:
+  * the launch shape each named workload gets (the shapes the kernels were tuned for);
+  * the region split (three workgroups per token) where it applies, and only there;
+  * calls whose grid exceeds one dispatch: how many launches, their token ranges, grid sizes,
+    pointer offsets and position offsets, at sizes no GPU test allocates.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "qk_rmsnorm_rope_amd", "csrc")
+
+DRIVER = r"""
+#include "qkrope_api.cpp"
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+// ---- stubs: HIP runtime queries (no device here) and kernel launchers that record ----------
+hipError_t hipGetDevice(int *d) { *d = 0; return hipSuccess; }
+hipError_t hipSetDevice(int) { return hipSuccess; }
+hipError_t hipGetDeviceCount(int *n) { *n = 0; return hipSuccess; }
+hipError_t hipGetDeviceProperties(hipDeviceProp_t *, int) { return hipErrorNoDevice; }
+const char *hipGetErrorString(hipError_t) { return "stub"; }
+
+static uintptr_t g_base;     // the call's first input, to print offsets from
+
+static hipError_t rec(const char *kind, const qkrope::KernelKey &k, const qkrope::LaunchShape &s,
+                      const qkrope::KernelArgs &a)
+{
+    std::printf("launch %s threads=%d slots=%d su=%d tpw=%d split=%d blocks=%lld tpl=%d "
+                "pairing=%d norm=%d fp8=%d ntok=%lld toff=%u in0=%llu xcd=%u\n",
+                kind, s.threads, s.slots, (int)s.slot_uniform, s.tpw, (int)s.split,
+                (long long)s.blocks, k.head_dim_tpl, k.pairing, k.norm, (int)k.fp8,
+                (long long)a.num_tokens, a.token_offset,
+                (unsigned long long)(reinterpret_cast<uintptr_t>(a.in[0]) - g_base), a.xcd_group);
+    return hipSuccess;
+}
+#define STUB(name) \
+    hipError_t qkrope::name(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t) \
+    { return rec(#name, k, s, a); }
+STUB(launch_3d_d64) STUB(launch_3d_d128) STUB(launch_3d_d256)
+STUB(launch_table_interleaved_bf16) STUB(launch_table_halfsplit_bf16)
+STUB(launch_table_interleaved_f16) STUB(launch_table_halfsplit_f16)
+STUB(launch_table_halfsplit_any_bf16) STUB(launch_table_halfsplit_any_f16)
+hipError_t qkrope::launch_sumsq(const SumsqArgs &, int64_t tokens, int threads, hipStream_t)
+{
+    std::printf("launch sumsq threads=%d tokens=%lld\n", threads, (long long)tokens);
+    return hipSuccess;
+}
+
+static void *at(int k) { return reinterpret_cast<void *>((uintptr_t(1) << 40) + (uintptr_t(k) << 38)); }
+
+int main(int argc, char **argv)
+{
+    qkrope_ctx ctx{0, 256, "gfx950"};
+    qkrope_handle h = &ctx;
+    const char *form = argv[1];
+    long long v[20] = {0};
+    for (int i = 2; i < argc && i < 22; ++i) v[i - 2] = std::atoll(argv[i]);
+    g_base = reinterpret_cast<uintptr_t>(at(0));
+    int st;
+    if (!std::strcmp(form, "3d")) {
+        // T ppf pph ppw cf ch cw Hq Hk Hv D interleave is_qk_norm fp8 token_offset use_sumsq
+        const long long T = v[0];
+        const int D = (int)v[10];
+        const bool sums = v[15] != 0;
+        st = qkrope_run_3d_sharded(h, at(0), at(4), at(5), T, v[14], sums ? (const float *)at(6) : nullptr,
+                                   v[7] * D, v[8] * D, (int)v[1], (int)v[2], (int)v[3], (int)v[4],
+                                   (int)v[5], (int)v[6], (int)v[7], (int)v[8], (int)v[9], D, 1e-6,
+                                   1e4, (int)v[11], 1.0, 0.0, 0.0, 1.0, (int)v[12], (int)v[13],
+                                   1.0, 1.0, at(1), at(2), at(3), nullptr);
+    } else {
+        // T Hq Hk D R interleaved norm_mode act out tdt q_stride
+        const long long T = v[0];
+        const int Hq = (int)v[1], Hk = (int)v[2], D = (int)v[3], R = (int)v[4];
+        const long long qs = v[10] ? v[10] : (long long)Hq * D;
+        st = qkrope_run_table_ex(h, at(0), at(1), at(6), at(7), at(2), at(3), (int)v[9], (int)v[7],
+                                 (int)v[8], 1.0, 1e-6, T, Hq, Hk, D, R, (int)v[5], (int)v[6], qs,
+                                 (long long)Hk * D, R / 2, R / 2, at(4), at(5), qs,
+                                 (long long)Hk * D, nullptr);
+    }
+    std::printf("status %d %s\n", st, qkrope_last_error());
+    return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    if shutil.which("g++") is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("needs g++ and the ROCm headers")
+    d = tmp_path_factory.mktemp("launch")
+    src, exe = d / "launch_check.cpp", d / "launch_check"
+    src.write_text(DRIVER)
+    subprocess.run(["g++", "-std=c++17", "-O1", "-w", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-I", "/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True, capture_output=True, text=True)
+    return str(exe)
+
+
+def run(driver, *args):
+    """The recorded launches (dicts of their fields) and the call's status."""
+    out = subprocess.run([driver, *map(str, args)], capture_output=True, text=True, timeout=60,
+                         check=True).stdout.splitlines()
+    launches = []
+    for line in out:
+        if line.startswith("launch "):
+            parts = line.split()
+            rec = {"kind": parts[1]}
+            rec.update({k: v for k, v in (p.split("=") for p in parts[2:])})
+            launches.append({k: (v if k == "kind" else int(v)) for k, v in rec.items()})
+    status = int(out[-1].split()[1])
+    return launches, status
+
+
+def run_3d(driver, T, grid, ch, heads, D, interleave=1, norm=1, fp8=0, offset=0, sums=0):
+    return run(driver, "3d", T, *grid, *ch, *heads, D, interleave, norm, fp8, offset, sums)
+
+
+def test_named_3d_workloads_get_their_tuned_shapes(driver):
+    # 15360 x 3x32 x 128, across heads: one token per 512-lane workgroup, one chunk per region
+    (l,), st = run_3d(driver, 15360, (16, 24, 40), (16, 56, 56), (32, 32, 32), 128)
+    assert st == 0 and l["kind"] == "launch_3d_d128"
+    assert (l["threads"], l["slots"], l["su"], l["tpw"], l["split"]) == (512, 1, 1, 1, 0)
+    assert l["blocks"] == 15360 and l["xcd"] == 16
+    # 2 x 18480 x 3x20 x 64, NeoX, FP8: two tokens of 160 lanes per 320-lane workgroup
+    (l,), st = run_3d(driver, 36960, (20, 33, 28), (16, 24, 24), (20, 20, 20), 64, interleave=0,
+                      fp8=1)
+    assert st == 0 and (l["threads"], l["tpw"], l["split"], l["fp8"]) == (320, 2, 0, 1)
+    assert l["blocks"] == 36960 // 2
+    # 122880 x 3x16 x 256, no norm: one region of one token per workgroup (three per token)
+    (l,), st = run_3d(driver, 122880, (32, 48, 80), (64, 96, 96), (16, 16, 16), 256, norm=0)
+    assert st == 0 and (l["threads"], l["split"], l["norm"]) == (512, 1, 0)
+    assert l["blocks"] == 3 * 122880
+
+
+@pytest.mark.parametrize("norm,fp8,heads", [(1, 0, (16, 16, 16)), (0, 1, (16, 16, 16)),
+                                            (0, 0, (4, 4, 4))])
+def test_region_split_only_without_norm_for_16_bit_outputs_and_wide_rows(driver, norm, fp8,
+                                                                         heads):
+    (l,), st = run_3d(driver, 1536, (4, 4, 96), (64, 96, 96), heads, 256, norm=norm, fp8=fp8)
+    assert st == 0 and l["split"] == 0 and l["blocks"] == 1536 // l["tpw"]
+
+
+def test_named_table_workloads_get_their_tuned_shapes(driver):
+    # 4096 x 2x24 x 128, interleaved, bf16 table: 384 lanes (16 per head), one token each
+    (l,), st = run(driver, "table", 4096, 24, 24, 128, 128, 1, 1, 0, 0, 0, 0)
+    assert st == 0 and l["kind"] == "launch_table_interleaved_bf16"
+    assert (l["threads"], l["slots"], l["tpw"], l["split"], l["tpl"]) == (384, 1, 1, 0, 0)
+    # E4M3 outputs at head_dim == rotary_dim == 128 take the compile-time head geometry
+    (l,), st = run(driver, "table", 32768, 24, 24, 128, 128, 1, 1, 0, 3, 1, 0)
+    assert st == 0 and l["tpl"] == 128 and l["fp8"] == 1
+    # half-split with rotary_dim % 16 != 0 exchanges partners through LDS
+    (l,), st = run(driver, "table", 64, 2, 2, 128, 72, 0, 1, 0, 0, 1, 0)
+    assert st == 0 and l["kind"] == "launch_table_halfsplit_any_bf16"
+
+
+def test_region_split_past_one_grid_runs_as_two_launches(driver):
+    # 512-lane workgroups, three per token: one launch takes floor((2^32 - 1) / 512 / 3) tokens
+    per = ((1 << 32) - 1) // 512 // 3
+    T = per + 3001
+    heads, D = (32, 32, 16), 128
+    row = sum(heads) * D
+    ls, st = run_3d(driver, T, (1, 1, 7), (32, 48, 48), heads, D, norm=0, offset=11)
+    assert st == 0 and len(ls) == 2
+    a, b = ls
+    assert a["split"] == b["split"] == 1
+    assert (a["ntok"], b["ntok"]) == (per, 3001)
+    assert (a["blocks"], b["blocks"]) == (3 * per, 3 * 3001)
+    assert (a["toff"], b["toff"]) == (11, 11 + per)
+    assert (a["in0"], b["in0"]) == (0, per * row * 2)
+    assert a["blocks"] * a["threads"] <= (1 << 32) - 1
+
+
+@pytest.mark.parametrize("with_table", [False, True])
+def test_one_token_per_workgroup_past_one_grid(driver, with_table):
+    # 64-lane workgroups (one head of 64 per region), with the across-heads sums passed in
+    heads = (1, 1, 1)
+    per = ((1 << 32) - 1) // 64
+    T = 2 * per + 5
+    ls, st = run_3d(driver, T, (1, 1, 5), (16, 24, 24), heads, 64, offset=3, sums=1)
+    assert st == 0 and [l["ntok"] for l in ls] == [per, per, 5]
+    assert [l["toff"] for l in ls] == [3, 3 + per, 3 + 2 * per]
+    assert [l["in0"] for l in ls] == [0, per * 3 * 64 * 2, 2 * per * 3 * 64 * 2]
+    assert all(l["blocks"] * l["threads"] <= (1 << 32) - 1 for l in ls)
+    if with_table:   # the table form's rows, past one grid at 64-lane workgroups
+        T2 = per + 9
+        ls, st = run(driver, "table", T2, 1, 1, 8, 8, 1, 1, 0, 0, 1, 0)
+        assert st == 0 and [l["ntok"] for l in ls] == [per, 9]
+        assert [l["in0"] for l in ls] == [0, per * 8 * 2]
+
+
+def test_shapes_past_the_largest_rows_are_refused_before_any_launch(driver):
+    ls, st = run_3d(driver, 8, (1, 2, 4), (32, 48, 48), (129, 128, 128), 128)
+    assert ls == [] and st == 2
+    ls, st = run(driver, "table", 4, 257, 1, 128, 128, 1, 1, 0, 0, 1, 0)
+    assert ls == [] and st == 2
