@@ -22,6 +22,7 @@ CSRC = os.path.join(ROOT, "qk_rmsnorm_rope_amd", "csrc")
 
 DRIVER = r"""
 #include "qkrope_api.cpp"
+#include "qkrope_api_cam.cpp"
 
 #include <cstdio>
 #include <cstdlib>
@@ -60,6 +61,16 @@ hipError_t qkrope::launch_sumsq(const SumsqArgs &, int64_t tokens, int threads, 
     return hipSuccess;
 }
 
+hipError_t qkrope::launch_cam(const CamArgs &a, int act, int cpl, int64_t blocks, int lds_bytes,
+                              hipStream_t)
+{
+    std::printf("launch cam act=%d cpl=%d lanes=%d hpg=%d groups=%d tiles=%d tiles_padded=%d "
+                "xcd=%u blocks=%lld lds=%d row_chunks=%d vec=%d\n",
+                act, cpl, a.lanes_per_token, a.heads_per_group, a.groups, a.tiles, a.tiles_padded,
+                a.xcd_group, (long long)blocks, lds_bytes, a.row_chunks, a.vec_store);
+    return hipSuccess;
+}
+
 static void *at(int k) { return reinterpret_cast<void *>((uintptr_t(1) << 40) + (uintptr_t(k) << 38)); }
 
 int main(int argc, char **argv)
@@ -81,6 +92,15 @@ int main(int argc, char **argv)
                                    (int)v[5], (int)v[6], (int)v[7], (int)v[8], (int)v[9], D, 1e-6,
                                    1e4, (int)v[11], 1.0, 0.0, 0.0, 1.0, (int)v[12], (int)v[13],
                                    1.0, 1.0, at(1), at(2), at(3), nullptr);
+    } else if (!std::strcmp(form, "cam")) {
+        // B N H D act
+        const long long B = v[0], N = v[1];
+        const int H = (int)v[2], D = (int)v[3];
+        const long long s = (long long)H * D;
+        st = qkrope_cam_prep(h, at(0), at(1), at(2), (int)v[4], (const float *)at(3),
+                             (const float *)at(4), (const float *)at(5), (const float *)at(6),
+                             0.5f, B, N, H, D, s, s, s, at(7), at(8), at(9), (float *)at(10),
+                             nullptr);
     } else {
         // T Hq Hk D R interleaved norm_mode act out tdt q_stride
         const long long T = v[0];
@@ -207,3 +227,34 @@ def test_shapes_past_the_largest_rows_are_refused_before_any_launch(driver):
     assert ls == [] and st == 2
     ls, st = run(driver, "table", 4, 257, 1, 128, 128, 1, 1, 0, 0, 1, 0)
     assert ls == [] and st == 2
+
+
+def test_camera_prologue_launch(driver):
+    # 2 x 18480 x 20 heads x 64: groups of 2 heads, 64-token tiles padded to a multiple of 8 so
+    # each XCD takes a contiguous eighth, 16-byte stores (N % 8 == 0)
+    (l,), st = run(driver, "cam", 2, 18480, 20, 64, 0)
+    assert st == 0
+    assert (l["cpl"], l["lanes"], l["hpg"], l["groups"]) == (1, 8, 2, 10)
+    assert (l["tiles"], l["tiles_padded"], l["xcd"]) == (289, 296, 37)
+    assert (l["blocks"], l["lds"], l["row_chunks"], l["vec"]) == (2 * 296 * 10, 16384, 8, 1)
+    # head_dim 128: two chunks per lane, one head per group; odd heads split as evenly as can be
+    (l,), st = run(driver, "cam", 1, 1000, 3, 128, 2)
+    assert st == 0 and (l["cpl"], l["hpg"], l["groups"], l["row_chunks"]) == (2, 1, 3, 16)
+    (l,), st = run(driver, "cam", 1, 1000, 3, 64, 0)
+    assert st == 0 and (l["hpg"], l["groups"]) == (2, 2)
+    # head_dim 40: five chunks in a power-of-two LDS row; N % 8 != 0 stores elements
+    (l,), st = run(driver, "cam", 1, 301, 2, 40, 0)
+    assert st == 0 and (l["lanes"], l["row_chunks"], l["vec"]) == (8, 8, 0)
+    # fewer than 8 tiles: plain block order
+    (l,), st = run(driver, "cam", 3, 200, 4, 64, 0)
+    assert st == 0 and (l["tiles"], l["tiles_padded"], l["xcd"]) == (4, 4, 0)
+
+
+def test_camera_prologue_grid_limit(driver):
+    # one head of 64 (512-lane workgroups): 2^23 tiles fill 2^32 lanes; tiles are padded to a
+    # multiple of 8, so one tile fewer is still refused and eight fewer fit
+    for n in ((1 << 29), (1 << 29) - 64):
+        ls, st = run(driver, "cam", 1, n, 1, 64, 0)
+        assert ls == [] and st == 2
+    (l,), st = run(driver, "cam", 1, (1 << 29) - 8 * 64, 1, 64, 0)
+    assert st == 0 and l["blocks"] * 64 * l["lanes"] < (1 << 32)
