@@ -78,37 +78,46 @@ int main(int argc, char **argv)
     qkrope_ctx ctx{0, 256, "gfx950"};
     qkrope_handle h = &ctx;
     const char *form = argv[1];
-    long long v[20] = {0};
-    for (int i = 2; i < argc && i < 22; ++i) v[i - 2] = std::atoll(argv[i]);
+    double v[40] = {0};
+    for (int i = 2; i < argc && i < 42; ++i) v[i - 2] = std::atof(argv[i]);
+    auto I = [&](int i) { return (long long)v[i]; };
     g_base = reinterpret_cast<uintptr_t>(at(0));
     int st;
     if (!std::strcmp(form, "3d")) {
         // T ppf pph ppw cf ch cw Hq Hk Hv D interleave is_qk_norm fp8 token_offset use_sumsq
-        const long long T = v[0];
-        const int D = (int)v[10];
-        const bool sums = v[15] != 0;
-        st = qkrope_run_3d_sharded(h, at(0), at(4), at(5), T, v[14], sums ? (const float *)at(6) : nullptr,
-                                   v[7] * D, v[8] * D, (int)v[1], (int)v[2], (int)v[3], (int)v[4],
-                                   (int)v[5], (int)v[6], (int)v[7], (int)v[8], (int)v[9], D, 1e-6,
-                                   1e4, (int)v[11], 1.0, 0.0, 0.0, 1.0, (int)v[12], (int)v[13],
-                                   1.0, 1.0, at(1), at(2), at(3), nullptr);
+        // eps base factor low high attention_factor out_scale v_scale qkv_shift_bytes
+        // q_out_mode (0: own buffer, 1: inside qkv)
+        const long long T = I(0);
+        const int D = (int)I(10);
+        const bool sums = I(15) != 0;
+        const void *qkv = static_cast<const char *>(at(0)) + I(24);
+        void *qo = I(25) == 1 ? static_cast<char *>(at(0)) + 4096 : at(1);
+        st = qkrope_run_3d_sharded(h, qkv, at(4), at(5), T, I(14), sums ? (const float *)at(6) : nullptr,
+                                   I(7) * D, I(8) * D, (int)I(1), (int)I(2), (int)I(3), (int)I(4),
+                                   (int)I(5), (int)I(6), (int)I(7), (int)I(8), (int)I(9), D, v[16],
+                                   v[17], (int)I(11), v[18], v[19], v[20], v[21], (int)I(12),
+                                   (int)I(13), v[22], v[23], qo, at(2), at(3), nullptr);
     } else if (!std::strcmp(form, "cam")) {
         // B N H D act
-        const long long B = v[0], N = v[1];
-        const int H = (int)v[2], D = (int)v[3];
+        const long long B = I(0), N = I(1);
+        const int H = (int)I(2), D = (int)I(3);
         const long long s = (long long)H * D;
-        st = qkrope_cam_prep(h, at(0), at(1), at(2), (int)v[4], (const float *)at(3),
+        st = qkrope_cam_prep(h, at(0), at(1), at(2), (int)I(4), (const float *)at(3),
                              (const float *)at(4), (const float *)at(5), (const float *)at(6),
                              0.5f, B, N, H, D, s, s, s, at(7), at(8), at(9), (float *)at(10),
                              nullptr);
     } else {
-        // T Hq Hk D R interleaved norm_mode act out tdt q_stride
-        const long long T = v[0];
-        const int Hq = (int)v[1], Hk = (int)v[2], D = (int)v[3], R = (int)v[4];
-        const long long qs = v[10] ? v[10] : (long long)Hq * D;
-        st = qkrope_run_table_ex(h, at(0), at(1), at(6), at(7), at(2), at(3), (int)v[9], (int)v[7],
-                                 (int)v[8], 1.0, 1e-6, T, Hq, Hk, D, R, (int)v[5], (int)v[6], qs,
-                                 (long long)Hk * D, R / 2, R / 2, at(4), at(5), qs,
+        // T Hq Hk D R interleaved norm_mode act out tdt q_stride eps out_scale q_shift_bytes
+        // q_out_mode (0: own buffer, 1: q itself, 2: q shifted by 16 bytes)
+        const long long T = I(0);
+        const int Hq = (int)I(1), Hk = (int)I(2), D = (int)I(3), R = (int)I(4);
+        const long long qs = I(10) ? I(10) : (long long)Hq * D;
+        const void *q = static_cast<const char *>(at(0)) + I(13);
+        void *qo = I(14) == 1 ? const_cast<void *>(q)
+                 : I(14) == 2 ? static_cast<char *>(const_cast<void *>(q)) + 16 : at(4);
+        st = qkrope_run_table_ex(h, q, at(1), at(6), at(7), at(2), at(3), (int)I(9), (int)I(7),
+                                 (int)I(8), v[12], v[11], T, Hq, Hk, D, R, (int)I(5), (int)I(6), qs,
+                                 (long long)Hk * D, R / 2, R / 2, qo, at(5), qs,
                                  (long long)Hk * D, nullptr);
     }
     std::printf("status %d %s\n", st, qkrope_last_error());
@@ -145,8 +154,17 @@ def run(driver, *args):
     return launches, status
 
 
-def run_3d(driver, T, grid, ch, heads, D, interleave=1, norm=1, fp8=0, offset=0, sums=0):
-    return run(driver, "3d", T, *grid, *ch, *heads, D, interleave, norm, fp8, offset, sums)
+def run_3d(driver, T, grid, ch, heads, D, interleave=1, norm=1, fp8=0, offset=0, sums=0,
+           eps=1e-6, base=1e4, factor=1.0, low=0.0, high=0.0, af=1.0, oqs=1.0, vqs=1.0,
+           shift=0, q_out_mode=0):
+    return run(driver, "3d", T, *grid, *ch, *heads, D, interleave, norm, fp8, offset, sums, eps,
+               base, factor, low, high, af, oqs, vqs, shift, q_out_mode)
+
+
+def run_table(driver, T, Hq, Hk, D, R, inter=1, norm=1, act=0, out=0, tdt=1, q_stride=0,
+              eps=1e-6, out_scale=1.0, shift=0, q_out_mode=0):
+    return run(driver, "table", T, Hq, Hk, D, R, inter, norm, act, out, tdt, q_stride, eps,
+               out_scale, shift, q_out_mode)
 
 
 def test_named_3d_workloads_get_their_tuned_shapes(driver):
@@ -176,14 +194,14 @@ def test_region_split_only_without_norm_for_16_bit_outputs_and_wide_rows(driver,
 
 def test_named_table_workloads_get_their_tuned_shapes(driver):
     # 4096 x 2x24 x 128, interleaved, bf16 table: 384 lanes (16 per head), one token each
-    (l,), st = run(driver, "table", 4096, 24, 24, 128, 128, 1, 1, 0, 0, 0, 0)
+    (l,), st = run_table(driver, 4096, 24, 24, 128, 128, tdt=0)
     assert st == 0 and l["kind"] == "launch_table_interleaved_bf16"
     assert (l["threads"], l["slots"], l["tpw"], l["split"], l["tpl"]) == (384, 1, 1, 0, 0)
     # E4M3 outputs at head_dim == rotary_dim == 128 take the compile-time head geometry
-    (l,), st = run(driver, "table", 32768, 24, 24, 128, 128, 1, 1, 0, 3, 1, 0)
+    (l,), st = run_table(driver, 32768, 24, 24, 128, 128, out=3)
     assert st == 0 and l["tpl"] == 128 and l["fp8"] == 1
     # half-split with rotary_dim % 16 != 0 exchanges partners through LDS
-    (l,), st = run(driver, "table", 64, 2, 2, 128, 72, 0, 1, 0, 0, 1, 0)
+    (l,), st = run_table(driver, 64, 2, 2, 128, 72, inter=0)
     assert st == 0 and l["kind"] == "launch_table_halfsplit_any_bf16"
 
 
@@ -217,7 +235,7 @@ def test_one_token_per_workgroup_past_one_grid(driver, with_table):
     assert all(l["blocks"] * l["threads"] <= (1 << 32) - 1 for l in ls)
     if with_table:   # the table form's rows, past one grid at 64-lane workgroups
         T2 = per + 9
-        ls, st = run(driver, "table", T2, 1, 1, 8, 8, 1, 1, 0, 0, 1, 0)
+        ls, st = run_table(driver, T2, 1, 1, 8, 8)
         assert st == 0 and [l["ntok"] for l in ls] == [per, 9]
         assert [l["in0"] for l in ls] == [0, per * 8 * 2]
 
@@ -225,7 +243,7 @@ def test_one_token_per_workgroup_past_one_grid(driver, with_table):
 def test_shapes_past_the_largest_rows_are_refused_before_any_launch(driver):
     ls, st = run_3d(driver, 8, (1, 2, 4), (32, 48, 48), (129, 128, 128), 128)
     assert ls == [] and st == 2
-    ls, st = run(driver, "table", 4, 257, 1, 128, 128, 1, 1, 0, 0, 1, 0)
+    ls, st = run_table(driver, 4, 257, 1, 128, 128)
     assert ls == [] and st == 2
 
 
@@ -258,3 +276,44 @@ def test_camera_prologue_grid_limit(driver):
         assert ls == [] and st == 2
     (l,), st = run(driver, "cam", 1, (1 << 29) - 8 * 64, 1, 64, 0)
     assert st == 0 and l["blocks"] * 64 * l["lanes"] < (1 << 32)
+
+
+# --- argument validation: each contract rule, on the CPU (status 1 invalid, 2 unsupported) ------
+
+G3 = dict(T=120, grid=(2, 3, 4), ch=(32, 48, 48), heads=(4, 2, 2), D=128)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1), (dict(base=0.0), 1),
+    (dict(base=float("inf")), 1), (dict(factor=0.0), 1), (dict(factor=2.0, low=3.0, high=3.0), 1),
+    (dict(factor=2.0, low=0.0, high=float("inf")), 1), (dict(af=1.1), 1),
+    (dict(factor=2.0, high=8.0, af=float("nan")), 1), (dict(factor=2.0, high=8.0, af=1.1), 0),
+    (dict(fp8=1, oqs=0.0), 1), (dict(fp8=1, vqs=-1.0), 1), (dict(fp8=1, oqs=0.5, vqs=2.0), 0),
+    (dict(D=96, ch=(32, 32, 32)), 1), (dict(ch=(31, 49, 48)), 1), (dict(ch=(32, 48, 40)), 1),
+    (dict(grid=(0, 3, 4)), 1), (dict(offset=-1), 1), (dict(offset=(1 << 31) - 100), 2),
+    (dict(shift=8), 2), (dict(q_out_mode=1), 1),
+], ids=lambda v: str(v))
+def test_3d_argument_rules(driver, kw, status):
+    args = {**G3, **kw}
+    ls, st = run_3d(driver, args.pop("T"), args.pop("grid"), args.pop("ch"), args.pop("heads"),
+                    args.pop("D"), **args)
+    assert st == status
+    assert (ls != []) == (status == 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0), (dict(R=7), 1), (dict(R=136), 1), (dict(D=12, R=12), 2), (dict(D=264, R=264), 2),
+    (dict(norm=3), 1), (dict(out=3, out_scale=0.0), 1), (dict(out=3, out_scale=0.5), 0),
+    (dict(act=1), 1), (dict(tdt=2), 1), (dict(out=2), 1), (dict(q_stride=4 * 128 - 8), 1),
+    (dict(q_stride=4 * 128 + 4), 2), (dict(q_stride=1 << 28), 2), (dict(eps=-1e-6), 1),
+    (dict(shift=8), 2), (dict(q_out_mode=1), 0), (dict(q_out_mode=1, out=3), 1),
+    (dict(q_out_mode=2), 1), (dict(T=1 << 31), 2),
+], ids=lambda v: str(v))
+def test_table_argument_rules(driver, kw, status):
+    args = dict(T=33, Hq=4, Hk=2, D=128, R=128, inter=0)
+    args.update(kw)
+    ls, st = run_table(driver, args.pop("T"), args.pop("Hq"), args.pop("Hk"), args.pop("D"),
+                       args.pop("R"), **args)
+    assert st == status
+    assert (ls != []) == (status == 0)
