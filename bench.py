@@ -104,7 +104,8 @@ def algorithmic_bytes(w) -> int:
     T, D = w.num_tokens, w.head_dim
     qk = T * (w.num_heads_q + w.num_heads_k) * D * 2
     tab = T * w.rotary_dim * (4 if w.table_dtype == "f32" else 2)
-    wts = 0 if w.norm_mode == "none" else 2 * D * 2
+    wts = {"none": 0, "per_head": 2 * D * 2,
+           "across_heads": (w.num_heads_q + w.num_heads_k) * D * 2}[w.norm_mode]
     out = qk // 2 if w.out_dtype == "e4m3" else qk
     return qk + tab + wts + out
 
