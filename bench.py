@@ -41,14 +41,18 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 COLD_BYTES = 512 << 20         # --cold: rotating buffer sets total at least twice the MALL
 DEFAULT_WORKLOAD = "rope3d_across_interleaved_s15360_h32_d128"
 _CSRC = "qk_rmsnorm_rope_amd/csrc/"
+# build.py holds the compile flags; the per-variant .hip files choose the instantiations
 COMMON_SOURCES = [_CSRC + "qkrope_kernel_impl.h", _CSRC + "qkrope_internal.h",
-                  _CSRC + "qkrope_host.h"]
-PROLOGUE_SOURCES = [_CSRC + "qkrope_api.cpp"]
+                  _CSRC + "qkrope_host.h", "qk_rmsnorm_rope_amd/build.py"]
+PROLOGUE_SOURCES = [_CSRC + "qkrope_api.cpp"] + sorted(
+    _CSRC + f for f in os.listdir(os.path.join(ROOT, _CSRC))
+    if f.startswith("qkrope_kernels_") and f.endswith(".hip") and "cam" not in f)
 CAM_SOURCES = [_CSRC + "qkrope_cam.h", _CSRC + "qkrope_api_cam.cpp",
                _CSRC + "qkrope_kernels_cam.hip"]
 
 
 _COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+_PY_COMMENTS = re.compile(r"#[^\n]*")
 
 
 def kernel_source_hash(w=None) -> str:
@@ -58,7 +62,9 @@ def kernel_source_hash(w=None) -> str:
     cam = w is not None and is_cam(w)
     for rel in COMMON_SOURCES + (CAM_SOURCES if cam else PROLOGUE_SOURCES):
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
-            h.update("".join(_COMMENTS.sub(" ", f.read()).split()).encode())
+            text = f.read()
+        text = (_PY_COMMENTS if rel.endswith(".py") else _COMMENTS).sub(" ", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
