@@ -46,16 +46,18 @@
  *       names these but leaves open how they compose; the readings taken here:
  *   - Q: ReLU, projection by proj_q, RoPE. K: ReLU, times k_scale, projection by proj_kv, RoPE.
  *     V: projection by proj_kv, RoPE (the K/V matrices are one transform shared by K and V).
- *     ReLU(x) = 0 if the sign bit of x is set, else x: max(x, 0) for every non-NaN x (also
- *     -0 -> +0); the page does not say what a NaN becomes, and this reading keeps one whose
- *     sign bit is clear and zeroes one whose sign bit is set.
+ *     ReLU(x) = x for x > 0, 0 for every other number (negatives and both zeros give +0), and
+ *     a NaN of either sign stays NaN. The page does not say what a NaN becomes; it presents
+ *     cam_prep_func as the native equivalent of a PyTorch module, and PyTorch's ReLU passes
+ *     every NaN through, so this reading does too.
  *   - A 4x4 matrix P acts on a head vector as D/4 independent groups of four consecutive
  *     channels: y[4g + i] = sum_j P[i][j] * x[4g + j], P stored row-major.
  *   - RoPE rotates the adjacent pairs (2i, 2i+1) of the projected vector by the angle whose
  *     cosine and sine are row n, column i of the tables (rotation by +theta as above).
  *   - inflation_sq(b, h, n) = |P_kv applied to k'|^2 / |k'|^2 for the key head vector
  *     k' = k_scale * ReLU(k) that enters the projection (how much the projection grows its
- *     squared norm), and 1 where |k'| = 0.
+ *     squared norm), and 1 where |k'| = 0; a NaN in k' makes it NaN (the quotient's own
+ *     value).
  *
  * Everything is computed in double from the exact decoded inputs and rounded once at the output.
  */
@@ -502,7 +504,7 @@ static double cam_head(const uint16_t *x, int act, int relu, double scale, const
     double na = 0.0, np_ = 0.0;
     for (int d = 0; d < D; ++d) {
         double v = act_decode(act, x[d]);
-        if (relu) v = signbit(v) ? 0.0 : v;
+        if (relu) v = (v > 0.0 || isnan(v)) ? v : 0.0;
         a[d] = scale * v;
         na += a[d] * a[d];
     }
@@ -513,7 +515,7 @@ static double cam_head(const uint16_t *x, int act, int relu, double scale, const
         y[2 * i] = p[2 * i] * c - p[2 * i + 1] * s;
         y[2 * i + 1] = p[2 * i + 1] * c + p[2 * i] * s;
     }
-    return na > 0.0 ? np_ / na : 1.0;
+    return na == 0.0 ? 1.0 : np_ / na;
 }
 
 int oracle_cam_prep(const uint16_t *q, const uint16_t *k, const uint16_t *v, int act_dtype,

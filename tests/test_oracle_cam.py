@@ -15,6 +15,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 
@@ -52,12 +53,15 @@ def random_proj(rng, B, N, scale=0.5):
     return (np.eye(4) + scale * rng.standard_normal((B, N, 4, 4))).astype(np.float32)
 
 
-def reference_by_primitives(x, P, cos, sin, relu, scale):
-    """The stated composition written with library primitives, per (b, n, h): a block-diagonal
-    kron(I, P) matmul, then RoPE as multiplication of complex pairs by cos + i sin. x: fp64
-    [B, N, H, D]. Returns fp64 [B, H, D, N] and |p|^2 / |a|^2 [B, H, N]."""
+def reference_by_primitives(x, P, cos, sin, relu, scale, grouped=False):
+    """The stated composition written with library primitives, per (b, n, h): PyTorch's ReLU
+    (the page presents cam_prep_func as the native equivalent of a PyTorch module), a
+    block-diagonal kron(I, P) matmul (grouped: the [D/4, 4] groups times P^T, which keeps a NaN
+    inside its group where the zeros of kron(I, P) would spread it), then RoPE as
+    multiplication of complex pairs by cos + i sin. x: fp64 [B, N, H, D]. Returns fp64
+    [B, H, D, N] and |p|^2 / |a|^2 [B, H, N] (1 where |a| = 0)."""
     B, N, H, D = x.shape
-    a = scale * (np.maximum(x, 0.0) if relu else x)
+    a = scale * (torch.relu(torch.from_numpy(x)).numpy() if relu else x)
     out = np.empty((B, H, D, N))
     infl = np.empty((B, H, N))
     for b in range(B):
@@ -65,12 +69,13 @@ def reference_by_primitives(x, P, cos, sin, relu, scale):
             M = np.kron(np.eye(D // 4), P[b, n].astype(np.float64))
             rot = cos[n].astype(np.float64) + 1j * sin[n].astype(np.float64)
             for h in range(H):
-                p = M @ a[b, n, h]
+                p = ((a[b, n, h].reshape(D // 4, 4) @ P[b, n].astype(np.float64).T).ravel()
+                     if grouped else M @ a[b, n, h])
                 z = (p[0::2] + 1j * p[1::2]) * rot
                 out[b, h, 0::2, n] = z.real
                 out[b, h, 1::2, n] = z.imag
                 na = a[b, n, h] @ a[b, n, h]
-                infl[b, h, n] = (p @ p) / na if na > 0 else 1.0
+                infl[b, h, n] = 1.0 if na == 0 else (p @ p) / na
     return out, infl
 
 
@@ -172,6 +177,73 @@ def test_cam_all_negative_head():
     assert np.all(qo[0, 0] == 0) and np.all(ko[0, 0] == 0)
     assert infl[0, 0, 0] == 1.0 and infl[0, 1, 0] == pytest.approx(4.0, rel=1e-15)
     np.testing.assert_array_equal(vo[0, 0, :, 0], 2.0 * decode(x)[0, 0, 0])
+
+
+@pytest.mark.filterwarnings("ignore:invalid value encountered")
+def test_cam_nan_propagates_like_library_relu():
+    """A NaN of either sign, planted into q, k and v, passes through ReLU as PyTorch's does:
+    the four channels of its projection group come out NaN (in every rotation pair of the
+    group), inflation_sq of a key head holding one is NaN, and every other output equals the
+    NaN-free run. The bf16 patterns include the NaNs next to the infinities (0x7F81, 0xFF81)
+    and the quiet ones (0x7FC0, 0xFFC0)."""
+    rng = np.random.default_rng(19)
+    B, N, H, D = 2, 5, 3, 16
+    q, k, v = (rand_bits(rng, (B, N, H, D)) for _ in range(3))
+    pq, pkv = random_proj(rng, B, N), random_proj(rng, B, N)
+    c, s = angle_tables(rng, N, D)
+    ks = 0.125
+    clean = oracle.cam_prep(q, k, v, pq, pkv, c, s, ks)
+    plant = {  # tensor -> [(b, n, h, d, bits)]
+        "q": [(0, 1, 0, 3, 0xFFC0), (1, 4, 2, 12, 0x7FC0), (1, 0, 1, 5, 0xFF81)],
+        "k": [(0, 2, 1, 0, 0xFF81), (1, 3, 0, 9, 0x7F81), (0, 0, 2, 15, 0xFFC0)],
+        "v": [(1, 1, 1, 6, 0xFFC0), (0, 4, 0, 1, 0x7FC0)],
+    }
+    x = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+    for name, sites in plant.items():
+        for b, n, h, d, bits in sites:
+            x[name][b, n, h, d] = bits
+    qo, ko, vo, infl = oracle.cam_prep(x["q"], x["k"], x["v"], pq, pkv, c, s, ks)
+    rq, _ = reference_by_primitives(decode(x["q"]), pq, c, s, True, 1.0, grouped=True)
+    rk, rinfl = reference_by_primitives(decode(x["k"]), pkv, c, s, True, ks, grouped=True)
+    rv, _ = reference_by_primitives(decode(x["v"]), pkv, c, s, False, 1.0, grouped=True)
+    for got, ref, cl, name in ((qo, rq, clean[0], "q"), (ko, rk, clean[1], "k"),
+                               (vo, rv, clean[2], "v")):
+        want_nan = np.zeros(got.shape, bool)
+        for b, n, h, d, _ in plant[name]:
+            g = d // 4 * 4
+            want_nan[b, h, g:g + 4, n] = True
+        np.testing.assert_array_equal(np.isnan(got), want_nan, err_msg=name)
+        np.testing.assert_array_equal(np.isnan(ref), want_nan, err_msg=name)
+        np.testing.assert_allclose(got[~want_nan], ref[~want_nan], rtol=1e-13, atol=1e-14)
+        np.testing.assert_array_equal(got[~want_nan], cl[~want_nan])
+    want_nan = np.zeros(infl.shape, bool)
+    for b, n, h, _, _ in plant["k"]:
+        want_nan[b, h, n] = True
+    np.testing.assert_array_equal(np.isnan(infl), want_nan)
+    np.testing.assert_array_equal(np.isnan(rinfl), want_nan)
+    np.testing.assert_array_equal(infl[~want_nan], clean[3][~want_nan])
+
+
+def test_cam_relu_of_signed_zeros_and_infinities():
+    """ReLU gives 0 for -0, +0, -inf and a negative subnormal and keeps a positive subnormal
+    (P = I, zero angles: each value reaches the output unchanged). A +inf survives ReLU, and
+    the projection then makes its whole group NaN (0 * inf in IEEE arithmetic), as the grouped
+    library reference does."""
+    B, N, H, D = 1, 1, 1, 12
+    bits = np.array([0x8000, 0x0000, 0xFF80, 0xBF80, 0x3F80, 0x8001, 0x0001, 0x4000,
+                     0x7F80, 0x3F80, 0xBF80, 0x0000], np.uint16).reshape(B, N, H, D)
+    c, s = zero_angle_tables(N, D)
+    P = eye_proj(B, N)
+    qo, _, vo, _ = oracle.cam_prep(bits, bits, bits, P, P, c, s, 1.0)
+    with np.errstate(invalid="ignore"):
+        ref, _ = reference_by_primitives(decode(bits), P, c, s, True, 1.0, grouped=True)
+    got = qo[0, 0, :, 0]
+    np.testing.assert_array_equal(got[:8], [0, 0, 0, 0, 1.0, 0, decode(bits)[0, 0, 0, 6], 2.0])
+    assert np.all(np.isnan(got[8:]))
+    np.testing.assert_array_equal(got, ref[0, 0, :, 0])      # NaNs at the same places
+    # V is not rectified: its -inf makes group 0 NaN, group 1 passes unchanged
+    assert np.all(np.isnan(vo[0, 0, :4, 0]))
+    np.testing.assert_array_equal(vo[0, 0, 4:8, 0], decode(bits)[0, 0, 0, 4:8])
 
 
 def test_cam_identity_projection_equals_table_form():
