@@ -263,8 +263,10 @@ int qkrope_run_3d_sharded(qkrope_handle h,
  * per batch b, token n and head h, where P . x applies the token's 4x4 matrix to each group of
  * four consecutive channels, y[4g+i] = sum_j P[i][j] * x[4g+j], and RoPE rotates the pairs
  * (2i, 2i+1) by +theta: (a, b) -> (a cos - b sin, b cos + a sin) with cos = rope_cos[n][i],
- * sin = rope_sin[n][i]. ReLU(x) = 0 when the sign bit of x is set, else x (max(x, 0) for every
- * non-NaN x; the page does not say what a NaN becomes). The RMSNorm of q and k is the caller's.
+ * sin = rope_sin[n][i]. ReLU(x) = x for x > 0 and for a NaN of either sign (the page does not
+ * say what a NaN becomes; PyTorch's ReLU, whose native equivalent the page presents, keeps it),
+ * +0 otherwise; a NaN in a key head makes its inflation_sq NaN. The RMSNorm of q and k is the
+ * caller's.
  *
  *   q, k, v        device, [batch, num_tokens, num_heads, head_dim] activations (act_dtype bf16
  *                  or binary16); token (b, n) starts at (b*num_tokens + n) * x_stride elements;

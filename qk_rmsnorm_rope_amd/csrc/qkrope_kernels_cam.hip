@@ -8,7 +8,8 @@
 // where P . x applies the token's 4x4 matrix to each group of four consecutive channels
 // (y[4g+i] = sum_j P[i][j] x[4g+j]) and RoPE rotates the adjacent pairs (2i, 2i+1) by +theta;
 // inflation_sq = |P_kv . k'|^2 / |k'|^2 for k' = k_scale * ReLU(k), 1 where k' = 0. ReLU keeps
-// x when its sign bit is clear and gives 0 otherwise (max(x, 0) for every non-NaN x).
+// x when it is positive or a NaN (of either sign, as PyTorch's ReLU does: the page presents the
+// op as a PyTorch module's native equivalent) and gives +0 otherwise.
 //
 // Work decomposition. The op streams 4 bytes per element (16-bit in, 16-bit out) for ~12 flops,
 // and turns a token-major layout into a dim-major one: a token's heads arrive as contiguous
@@ -18,8 +19,8 @@
 //   * lane (token nl, chunk dl) loads its token's two 4x4 matrices and four (cos, sin) pairs
 //     per chunk once (the fp32 tables are twice the size of a bf16 head, so sharing them over
 //     the group's heads and tensors matters), then issues the 16-byte loads of all its chunks;
-//   * per head and tensor: ReLU (Q, K) on the packed 16-bit pairs (one integer max per two
-//     values), the K scale, the projection and the rotation in fp32, rounding to 16 bits, one
+//   * per head and tensor: ReLU (Q, K) on the packed 16-bit pairs (three packed integer
+//     operations per two values), the K scale, the projection and the rotation in fp32, rounding to 16 bits, one
 //     16-byte LDS write of the chunk into the token's row of a [64 tokens][row_chunks] tile
 //     (D/8 chunks rounded up to a power of two) whose chunks are rotated by token/8 modulo
 //     row_chunks (so the column reads below hit distinct banks);
@@ -41,12 +42,18 @@ namespace dev {
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-// ReLU of two packed 16-bit floats (bf16 or binary16): a value whose sign bit is set is a
-// negative integer when read as int16, so an integer max with 0 zeroes exactly those.
+// ReLU of two packed 16-bit floats (bf16 or binary16), NaNs kept. Read as int16, a negative
+// number (-0 to -inf) is at most -C, C = 0x80 (bf16: -inf is 0xFF80) or 0x400 (binary16: 0xFC00),
+// and the negative NaNs lie between -C and 0. Adding C - 1 with saturation leaves exactly the
+// negative numbers below zero (positive patterns saturate at 0x7FFF instead of wrapping); the
+// arithmetic shift turns that sign into a mask of the halves to clear. Three packed operations.
+template <int ACT>
 __device__ __forceinline__ uint32_t relu2(uint32_t u)
 {
-    const s16x2 v = __builtin_bit_cast(s16x2, u);
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, s16x2{0, 0}));
+    constexpr short C1 = ACT == kActBF16 ? 0x7F : 0x3FF;
+    const s16x2 t = __builtin_elementwise_add_sat(__builtin_bit_cast(s16x2, u), s16x2{C1, C1});
+    const uint32_t clear = __builtin_bit_cast(uint32_t, t >> 15);
+    return u & ~clear;
 }
 
 // y = P . x on each group of four channels of an 8-element chunk.
@@ -181,7 +188,8 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             uint4 raw = v[i][c];
-            if (r < 2) raw = make_uint4(relu2(raw.x), relu2(raw.y), relu2(raw.z), relu2(raw.w));
+            if (r < 2)
+                raw = make_uint4(relu2<ACT>(raw.x), relu2<ACT>(raw.y), relu2<ACT>(raw.z), relu2<ACT>(raw.w));
             float x[8], p[8], y[8];
             unpack8<ACT>(raw, x);
             if (r == 0) {
@@ -211,7 +219,8 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
             na = group_sum(na, LT) * (a.k_scale * a.k_scale);
             np = group_sum(np, LT);
             if (dl == 0 && nl < nvalid)
-                a.inflation[((int64_t)b * H + h) * N + n0 + nl] = na > 0.0f ? np * __builtin_amdgcn_rcpf(na) : 1.0f;
+                // 1 for a zero key; a NaN key keeps the quotient's NaN
+                a.inflation[((int64_t)b * H + h) * N + n0 + nl] = na != 0.0f ? np * __builtin_amdgcn_rcpf(na) : 1.0f;
         }
         __syncthreads();
 

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from parity import assert_cam_close, assert_inflation_close
+from parity import assert_cam_close, assert_inflation_close, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +77,49 @@ def test_cam_matches_oracle(B, N, H, D, act):
     ref = oracle.cam_prep(inp["q"], inp["k"], inp["v"], inp["proj_q"], inp["proj_kv"],
                           inp["rope_cos"], inp["rope_sin"], w.k_scale)
     check(w.name, outs, infl, ref)
+
+
+# (tensor, b, n, h, d, 16-bit pattern) planted per activation format: NaNs of both signs (quiet,
+# and the ones next to the infinities), -inf and -0 where ReLU applies
+SPECIAL_SITES = {
+    "bf16": [("q", 0, 5, 1, 3, 0xFFC0), ("q", 1, 70, 3, 40, 0x7FC0), ("q", 0, 135, 0, 63, 0xFF81),
+             ("k", 0, 9, 2, 0, 0xFF81), ("k", 1, 64, 1, 17, 0x7F81), ("k", 1, 0, 3, 62, 0xFFC0),
+             ("v", 0, 100, 0, 6, 0xFFC0), ("v", 1, 127, 2, 33, 0x7FC0),
+             ("q", 0, 7, 0, 4, 0xFF80), ("k", 1, 8, 1, 9, 0xFF80), ("q", 0, 10, 0, 0, 0x8000)],
+    "f16": [("q", 0, 5, 1, 3, 0xFE00), ("q", 1, 70, 3, 40, 0x7E00), ("q", 0, 135, 0, 63, 0xFC01),
+            ("k", 0, 9, 2, 0, 0xFC01), ("k", 1, 64, 1, 17, 0x7C01), ("k", 1, 0, 3, 62, 0xFE00),
+            ("v", 0, 100, 0, 6, 0xFE00), ("v", 1, 127, 2, 33, 0x7E00),
+            ("q", 0, 7, 0, 4, 0xFC00), ("k", 1, 8, 1, 9, 0xFC00), ("q", 0, 10, 0, 0, 0x8000)],
+}
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_cam_nan_and_special_inputs(act):
+    """NaNs of either sign pass ReLU as the oracle's (PyTorch's) ReLU passes them: each makes
+    the four output channels of its projection group NaN, and a NaN key head makes its
+    inflation_sq NaN; -inf and -0 rectify to 0. NaN positions must be the oracle's exactly and
+    every other value matches it to the usual tolerance."""
+    w = workload(2, 136, 4, 64, act, seed=77)
+    print(f"\ncam special values {w.name}", flush=True)
+    inp = wl.cam_inputs(w)
+    for name, b, n, h, d, bits in SPECIAL_SITES[act]:
+        inp[name].view(torch.int16)[b, n, h, d] = bits - 65536 if bits >= 32768 else bits
+    outs, infl = run_gpu(gpu_inputs(inp), w.k_scale)
+    torch.cuda.synchronize()
+    ref = oracle.cam_prep(inp["q"], inp["k"], inp["v"], inp["proj_q"], inp["proj_kv"],
+                          inp["rope_cos"], inp["rope_sin"], w.k_scale)
+    # three NaN groups of four channels in each tensor (Q's and K's -inf are rectified), and
+    # three NaN keys
+    assert [int(np.isnan(r).sum()) for r in ref] == [12, 12, 8, 3]
+    for o, r, n in zip(list(outs) + [infl], ref, ("q", "k", "v", "inflation_sq")):
+        g = to_f64(o).reshape(r.shape)
+        assert np.array_equal(np.isnan(g), np.isnan(r)), f"{n}: NaN positions differ"
+        keep_gpu = torch.where(torch.isnan(o), torch.zeros_like(o), o)
+        keep_ref = np.where(np.isnan(r), 0.0, r)
+        if n == "inflation_sq":
+            assert_inflation_close(keep_gpu, keep_ref, f"{w.name} {n}")
+        else:
+            assert_cam_close(keep_gpu, keep_ref, f"{w.name} {n}")
 
 
 def test_cam_hand_case_on_gpu():
