@@ -191,9 +191,10 @@ int qkrope_run_table_ex(qkrope_handle h,
  *   q_out, k_out, v_out  [num_tokens, num_heads_x, head_dim], contiguous, and must not overlap
  *              qkv or each other.
  *
- * Limits (else QKROPE_ERR_UNSUPPORTED): num_tokens < 2^31; one workgroup per token covers at
- * most 2048 16-byte chunks (heads * head_dim / 8) in each of Q, K and V (e.g. 128 heads of 128
- * in each), or 4096 in all three together. num_tokens == 0 is a valid no-op.
+ * Limits (else QKROPE_ERR_UNSUPPORTED): num_tokens < 2^31; seq_len = ppf*pph*ppw < 2^31; one
+ * workgroup per token covers at most 2048 16-byte chunks (heads * head_dim / 8) in each of Q, K
+ * and V (e.g. 128 heads of 128 in each), or 4096 in all three together. num_tokens == 0 is a
+ * valid no-op.
  */
 int qkrope_run_3d(qkrope_handle h,
                   const void *qkv, const void *q_weight, const void *k_weight, int64_t num_tokens,
@@ -229,7 +230,8 @@ int qkrope_sumsq_3d(qkrope_handle h, const void *qkv, int64_t num_tokens, int nu
 /* qkrope_run_3d on a shard:
  *   token_offset  global index of qkv's first token: token t sits at grid position
  *                 (token_offset + t) mod (ppf*pph*ppw). num_tokens need not be a multiple of
- *                 ppf*pph*ppw; token_offset >= 0 and token_offset + num_tokens < 2^31.
+ *                 ppf*pph*ppw; token_offset >= 0 and token_offset + num_tokens < 2^31
+ *                 (ppf*pph*ppw < 2^31 as for qkrope_run_3d).
  *   sumsq         NULL: the norm spans the shard's own heads (as qkrope_run_3d).
  *                 Otherwise (with is_qk_norm) a device array [num_tokens, 2] of fp32 sums of
  *                 squares of each token's Q and K rows over ALL heads of the unsharded problem

@@ -25,7 +25,6 @@ import threading
 
 import torch  # imported before the library so both share torch's HIP runtime
 
-from .workloads import WORKLOADS  # noqa: F401  (re-exported for convenience)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqkrope.so")
 
@@ -364,12 +363,17 @@ def qkrope_run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
                   interleave=True, factor=1.0, low=0.0, high=0.0, attention_factor=1.0,
                   is_qk_norm=True, output_fp8=False, output_quant_scale=1.0, v_quant_scale=1.0,
                   stream=None) -> None:
-    """3D form into caller-provided contiguous outputs."""
-    if qkv.dtype != torch.bfloat16 or not qkv.is_cuda or not qkv.is_contiguous():
-        raise ValueError("qkv must be a contiguous bfloat16 GPU tensor")
+    """3D form into caller-provided contiguous outputs. qkv is [tokens, row] with tokens a
+    multiple of ppf*pph*ppw, or [batch, seq_len, row] with seq_len == ppf*pph*ppw (FlashInfer's
+    parameter list: seq_len = ppf * pph * ppw)."""
     row = (num_heads_q + num_heads_k + num_heads_v) * head_dim
     if qkv.dim() not in (2, 3) or qkv.shape[-1] != row:
         raise ValueError(f"qkv must be [tokens, {row}] or [batch, seq_len, {row}]")
+    if qkv.dim() == 3 and qkv.shape[1] != ppf * pph * ppw:
+        raise ValueError(f"a [batch, seq_len, row] qkv needs seq_len == ppf*pph*ppw = "
+                         f"{ppf * pph * ppw}, got {qkv.shape[1]}")
+    if qkv.dtype != torch.bfloat16 or not qkv.is_cuda or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous bfloat16 GPU tensor")
     T = qkv.numel() // row
     odt = torch.float8_e4m3fn if output_fp8 else torch.bfloat16
     for name, o, H in (("q_out", q_out, num_heads_q), ("k_out", k_out, num_heads_k),

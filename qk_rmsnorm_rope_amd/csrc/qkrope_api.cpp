@@ -413,7 +413,13 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
         if (C[i] < 0 || C[i] % 2) return fail(QKROPE_ERR_INVALID, "channel counts must be even and >= 0");
     if (C[0] + C[1] + C[2] != D) return fail(QKROPE_ERR_INVALID, "channel counts must sum to head_dim");
     if (c.ppf <= 0 || c.pph <= 0 || c.ppw <= 0) return fail(QKROPE_ERR_INVALID, "ppf, pph, ppw must be positive");
-    const int64_t S = (int64_t)c.ppf * c.pph * c.ppw;
+    // positions are split with 32-bit magic divisors (divisors < 2^31): bound the grid, each
+    // partial product checked before the next multiplication so nothing overflows
+    const int64_t kMaxSeq = int64_t(1) << 31;
+    const int64_t fh = (int64_t)c.ppf * c.pph;       // < 2^62
+    if (fh >= kMaxSeq || fh * c.ppw >= kMaxSeq)
+        return fail(QKROPE_ERR_UNSUPPORTED, "ppf*pph*ppw must be < 2^31");
+    const int64_t S = fh * c.ppw;
     if (c.whole_sequences && T % S) return fail(QKROPE_ERR_INVALID, "num_tokens must be a multiple of ppf*pph*ppw");
     if (c.token_offset < 0) return fail(QKROPE_ERR_INVALID, "token_offset must be >= 0");
     if (!(c.base > 0.0) || !std::isfinite(c.base)) return fail(QKROPE_ERR_INVALID, "base must be finite and > 0");

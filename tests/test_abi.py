@@ -133,3 +133,21 @@ def test_binding_weight_checks():
     assert qr._weight_elems("per_head", 0, 128) == 0
     assert qr._weight_elems("per_head", 8, 128) == 128
     assert qr._weight_elems("across_heads", 8, 128) == 1024
+
+
+# --- the binding's shape rules, checked before any device is touched ----------------------------
+
+def test_3d_binding_requires_seq_len_of_the_grid():
+    """A [batch, seq_len, row] qkv must have seq_len == ppf*pph*ppw (FlashInfer's parameter
+    list: seq_len = ppf * pph * ppw); a 2D [tokens, row] qkv only needs whole sequences, which
+    the library checks."""
+    import torch
+    import qk_rmsnorm_rope_amd as qr
+    H, D = 2, 64
+    kw = dict(ppf=2, pph=3, ppw=4, num_frame_channels=16, num_height_channels=24,
+              num_width_channels=24, num_heads_q=H, num_heads_k=H, num_heads_v=H, head_dim=D)
+    qkv = torch.zeros((1, 48, 3 * H * D), dtype=torch.bfloat16)    # two sequences in one row
+    with pytest.raises(ValueError, match="seq_len == ppf\\*pph\\*ppw = 24"):
+        qr.fused_qk_rmsnorm_rope(qkv, None, None, **kw)
+    with pytest.raises(ValueError, match="seq_len"):
+        qr.qkrope_run_3d(qkv, None, None, q_out=None, k_out=None, v_out=None, **kw)

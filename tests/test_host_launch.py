@@ -293,6 +293,12 @@ G3 = dict(T=120, grid=(2, 3, 4), ch=(32, 48, 48), heads=(4, 2, 2), D=128)
     (dict(D=96, ch=(32, 32, 32)), 1), (dict(ch=(31, 49, 48)), 1), (dict(ch=(32, 48, 40)), 1),
     (dict(grid=(0, 3, 4)), 1), (dict(offset=-1), 1), (dict(offset=(1 << 31) - 100), 2),
     (dict(shift=8), 2), (dict(q_out_mode=1), 1),
+    # seq_len = ppf*pph*ppw must be < 2^31 (32-bit position division): pph*ppw = 2^32 once
+    # truncated to 0 (a division by zero on the host), 46341^2 = 2^31 + 4281 gave a shift of 32
+    # in the kernel; products past int64 are refused as well
+    (dict(grid=(1, 65536, 65536)), 2), (dict(grid=(1, 46341, 46341)), 2),
+    (dict(grid=(46341, 46341, 1)), 2), (dict(grid=(2147483647, 2147483647, 2147483647)), 2),
+    (dict(grid=(1, 46340, 46340)), 0), (dict(grid=(2, 1 << 15, (1 << 15) - 1)), 0),
 ], ids=lambda v: str(v))
 def test_3d_argument_rules(driver, kw, status):
     args = {**G3, **kw}
