@@ -7,11 +7,15 @@ One step is one launch of the whole prologue (norm, rotation, V copy, output rou
 batch of the workload. The timed steps are captured once into a HIP graph and replayed (the way
 a fixed-shape prologue that runs in every layer and denoising step is launched in production);
 --stream launches them one by one from the host instead.
-The default workload is the 15360-token, 32-head, head_dim-128 3D problem
-with across-heads norm and interleaved pairs (LTX-2's video self-attention shape). Inputs are
-seeded synthetic bf16 drawn by qk_rmsnorm_rope_amd.workloads, resident in HBM before timing.
+The default workload is the largest one that fits one GPU: 122880 tokens of packed bf16 QKV,
+16 heads of 256 each, 3D RoPE with YaRN and no norm (6.04 GB moved per step). In the same run,
+and in the same JSON line under "also_timed", the two other workloads held to the bandwidth
+target are timed the same way: the 15360-token, 32-head, head_dim-128 3D problem with
+across-heads norm (LTX-2's video self-attention shape) and the 2 x 18480-token, 20-head,
+head_dim-64 NeoX problem with E4M3 outputs (SANA-WM's grid). Inputs are seeded synthetic bf16
+drawn by qk_rmsnorm_rope_amd.workloads, resident in HBM before timing.
 Prints one JSON line with tokens/s, the HBM roofline of the kernel and a CPU baseline (the fp64
-oracle on a bounded sample of the same workload).
+oracle on a bounded sample of the headline workload).
 
 Other modes (used to produce the committed profiles):
     --profile-run       only warmup + steps launches, no CPU baseline, no JSON line
@@ -39,7 +43,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 COLD_BYTES = 512 << 20         # --cold: rotating buffer sets total at least twice the MALL
-DEFAULT_WORKLOAD = "rope3d_across_interleaved_s15360_h32_d128"
+DEFAULT_WORKLOAD = "rope3d_yarn_nonorm_s122880_h16_d256"
+# timed after the default workload, in the same run, as sub-records of its JSON line
+ALSO_TIMED = ("rope3d_across_interleaved_s15360_h32_d128", "rope3d_neox_fp8_b2_s18480_h20_d64")
 _CSRC = "qk_rmsnorm_rope_amd/csrc/"
 # build.py holds the compile flags; the per-variant .hip files choose the instantiations
 COMMON_SOURCES = [_CSRC + "qkrope_kernel_impl.h", _CSRC + "qkrope_internal.h",
@@ -399,6 +405,43 @@ def crossover(dev, warmup) -> None:
                       "the fused call is never slower than the eager chain"}), flush=True)
 
 
+def measure(w, dev, args, use_graph):
+    """Prepare `args.sets` buffer sets of workload `w` on `dev` and time it as bench.py does.
+    Returns (cpu_inputs, wall_s_total, s_per_step, s_per_launch of the dominant kernel, extra)."""
+    import torch
+    sets = args.sets
+    if args.cold:
+        sets = max(sets, -(-COLD_BYTES // algorithmic_bytes(w)))
+    timer = time_graph if use_graph else time_launches
+    cpu_inputs, launch, calls = make_launcher(w, dev, sets)
+    torch.cuda.synchronize()
+    total, mean_step = timer(launch, args.steps, args.warmup)
+    mean_launch = mean_step
+    extra = {"buffer_sets": sets}
+    if is_sharded(w):
+        # the step is two kernels: time each on its own for the per-kernel rooflines
+        _, mean_launch = timer(lambda i: calls[i % sets].apply(), args.steps, args.warmup)
+        _, mean_sumsq = timer(lambda i: calls[i % sets].sumsq(), args.steps, args.warmup)
+        extra.update({"sumsq_kernel": {"achieved": sumsq_bytes(w) / mean_sumsq / 1e9,
+                                       "unit": "GB/s", "mean_launch_us": mean_sumsq * 1e6,
+                                       "algorithmic_bytes": sumsq_bytes(w)},
+                      "apply_kernel_us": mean_launch * 1e6, "step_us": mean_step * 1e6})
+    del launch, calls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return cpu_inputs, total, mean_step, mean_launch, extra
+
+
+def roofline(w, mean_launch) -> dict:
+    nbytes = algorithmic_bytes(w)
+    achieved = nbytes / mean_launch / 1e9
+    traffic = traffic_from_profile(w)
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic["bytes_per_launch"] if traffic else None,
+            "algorithmic_bytes": nbytes, "mean_launch_us": mean_launch * 1e6}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,6 +451,8 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=3,
                     help="input/output buffer sets rotated across launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true",
+                    help="time only the default workload (skip the also_timed sub-records)")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--crossover", action="store_true")
@@ -431,37 +476,29 @@ def main() -> int:
         crossover(dev, args.warmup)
         return 0
     w = wl.WORKLOADS[args.workload]
-    if args.cold:
-        per_set = algorithmic_bytes(w)
-        args.sets = max(args.sets, -(-COLD_BYTES // per_set))
     use_graph = not args.stream
     if use_graph:
         # launchers bind the stream they are prepared on: prepare them on the capture stream
         capture = torch.cuda.Stream()
         capture.wait_stream(torch.cuda.current_stream())
         torch.cuda.set_stream(capture)
-    timer = time_graph if use_graph else time_launches
-    cpu_inputs, launch, calls = make_launcher(w, dev, args.sets)
-    torch.cuda.synchronize()
-    total, mean_step = timer(launch, args.steps, args.warmup)
-    mean_launch = mean_step
-    extra = {}
-    if is_sharded(w):
-        # the step is two kernels: time each on its own for the per-kernel rooflines
-        _, mean_launch = timer(lambda i: calls[i % args.sets].apply(), args.steps, args.warmup)
-        _, mean_sumsq = timer(lambda i: calls[i % args.sets].sumsq(), args.steps, args.warmup)
-        extra = {"sumsq_kernel": {"achieved": sumsq_bytes(w) / mean_sumsq / 1e9,
-                                  "unit": "GB/s", "mean_launch_us": mean_sumsq * 1e6,
-                                  "algorithmic_bytes": sumsq_bytes(w)},
-                 "apply_kernel_us": mean_launch * 1e6, "step_us": mean_step * 1e6}
+    cpu_inputs, total, mean_step, mean_launch, extra = measure(w, dev, args, use_graph)
+    sets = extra.pop("buffer_sets")
     if args.profile_run:
         print(f"{w.name}: {args.steps} launches, mean {mean_step * 1e6:.1f} us", flush=True)
         return 0
 
-    nbytes = algorithmic_bytes(w)
+    also = []
+    if args.workload == DEFAULT_WORKLOAD and not args.no_also:
+        for name in ALSO_TIMED:
+            wa = wl.WORKLOADS[name]
+            _, t_a, step_a, launch_a, ex_a = measure(wa, dev, args, use_graph)
+            also.append({"workload": name, "tokens": total_tokens(wa),
+                         "value": total_tokens(wa) / (t_a / args.steps), "unit": "tokens/s",
+                         "ms_per_step": t_a / args.steps * 1e3,
+                         "buffer_sets": ex_a["buffer_sets"], "roofline": roofline(wa, launch_a)})
+
     ms_per_step = total / args.steps * 1e3
-    achieved = nbytes / mean_launch / 1e9
-    traffic = traffic_from_profile(w)
     result = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak) for fused QK-RMSNorm+RoPE+V",
         "value": total_tokens(w) / (total / args.steps),
@@ -482,14 +519,13 @@ def main() -> int:
                    "head_dim": w.head_dim,
                    "parallelism": (f"one rank of {w.head_shards} head shards"
                                    if is_sharded(w) else "single-gpu"),
-                   "buffer_sets": args.sets,
+                   "buffer_sets": sets,
                    "launch": "hip_graph" if use_graph else "stream"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic["bytes_per_launch"] if traffic else None,
-                     "algorithmic_bytes": nbytes, "mean_launch_us": mean_launch * 1e6},
+        "roofline": roofline(w, mean_launch),
         **extra,
     }
+    if also:
+        result["also_timed"] = also
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, cpu_inputs)
         result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
