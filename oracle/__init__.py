@@ -26,9 +26,10 @@ ACT_BF16, ACT_F16 = 0, 1
 
 
 def build(verbose: bool = False) -> str:
-    """Compile oracle.c into liboracle.so with gcc (portable x86-64, OpenMP)."""
+    """Compile oracle.c into liboracle.so with gcc (portable x86-64, OpenMP; ISO C, so no
+    floating-point contraction or reassociation)."""
     tmp = LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+    cmd = ["gcc", "-O3", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
            "-o", tmp, SOURCE, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -7,7 +7,14 @@ unchanged on fake, never-dereferenced device addresses. This pins:
   * the launch shape each named workload gets (the shapes the kernels were tuned for);
   * the region split (three workgroups per token) where it applies, and only there;
   * calls whose grid exceeds one dispatch: how many launches, their token ranges, grid sizes,
-    pointer offsets and position offsets, at sizes no GPU test allocates.
+    pointer offsets and position offsets, at sizes no GPU test allocates;
+  * that every address range a launch lets its kernel form lies inside one of the caller's
+    tensors: the stubs model each kernel's reads and writes (token rows of every region, idle
+    slots reading a row's first chunk, norm weights, table rows, the sums of a sharded call, the
+    camera prologue's matrices and tables) from the launch's arguments and check them against
+    the tensors the call was given. This covers regions without heads (which borrow another
+    region's row and weights), launches split over token ranges and two-token workgroups, with
+    no GPU. The same program also runs under AddressSanitizer and UndefinedBehaviorSanitizer.
 """
 from __future__ import annotations
 
@@ -27,6 +34,59 @@ DRIVER = r"""
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
+
+// ---- the caller's tensors, and the ranges a launch lets its kernel touch -------------------
+struct Span { uintptr_t lo, hi; };
+static std::vector<Span> g_spans;
+static void reg(const void *p, long long bytes)
+{
+    if (p && bytes > 0) g_spans.push_back({reinterpret_cast<uintptr_t>(p),
+                                           reinterpret_cast<uintptr_t>(p) + (uintptr_t)bytes});
+}
+// [p, p + bytes) must lie inside one caller tensor
+static void need(const void *p, long long bytes, const char *what)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p), hi = lo + (uintptr_t)bytes;
+    for (const Span &s : g_spans)
+        if (lo >= s.lo && hi <= s.hi) return;
+    std::printf("OOB %s at %#llx + %lld bytes\n", what, (unsigned long long)lo, bytes);
+}
+
+// The prologue kernel's accesses (qkrope_kernel_impl.h), per launch of T tokens: every slot
+// reads 16 bytes of its region's token row at its head's chunk (an idle slot, or a region
+// without heads, the row's first chunk); stores go to the region's output rows; per-head
+// weights are read at a chunk of [head_dim], across-heads weights at [heads * head_dim] (the
+// first chunk for a region without heads); table rows at columns below rotary_dim / 2; a
+// sharded call's sums at [T, 2].
+static void check_prologue(const qkrope::KernelKey &k, const qkrope::KernelArgs &a)
+{
+    const bool is3d = k.src == qkrope::kSrc3D;
+    const int nreg = is3d ? 3 : 2;
+    const long long T = a.num_tokens, D = a.head_dim;
+    const int esize = k.fp8 ? 1 : 2;
+    static const char *in_names[3] = {"load q", "load k", "load v"};
+    static const char *out_names[3] = {"store q", "store k", "store v"};
+    for (int r = 0; r < nreg; ++r) {
+        const long long width = a.heads[r] > 0 ? a.heads[r] * D : 8;
+        need(a.in[r], ((T - 1) * a.in_stride[r] + width) * 2, in_names[r]);
+        if (a.heads[r] > 0)
+            need(a.out[r], ((T - 1) * a.out_stride[r] + a.heads[r] * D) * esize, out_names[r]);
+    }
+    if (k.norm == qkrope::kNormPerHead) {
+        need(a.weight[0], D * 2, "q weight");
+        need(a.weight[1], D * 2, "k weight");
+    } else if (k.norm == qkrope::kNormAcross || k.norm == qkrope::kNormAcrossExt) {
+        need(a.weight[0], a.heads[0] > 0 ? a.heads[0] * D * 2 : 16, "q weight");
+        need(a.weight[1], a.heads[1] > 0 ? a.heads[1] * D * 2 : 16, "k weight");
+    }
+    if (!is3d && a.rotary_dim > 0) {
+        const long long ts = k.src == qkrope::kSrcTableF32 ? 4 : 2, half = a.rotary_dim / 2;
+        need(a.table_cos, ((T - 1) * a.cos_stride + half) * ts, "cos table");
+        need(a.table_sin, ((T - 1) * a.sin_stride + half) * ts, "sin table");
+    }
+    if (a.sumsq_in) need(a.sumsq_in, T * 8, "sums in");
+}
 
 // ---- stubs: HIP runtime queries (no device here) and kernel launchers that record ----------
 hipError_t hipGetDevice(int *d) { *d = 0; return hipSuccess; }
@@ -46,6 +106,7 @@ static hipError_t rec(const char *kind, const qkrope::KernelKey &k, const qkrope
                 (long long)s.blocks, k.head_dim_tpl, k.pairing, k.norm, (int)k.fp8,
                 (long long)a.num_tokens, a.token_offset,
                 (unsigned long long)(reinterpret_cast<uintptr_t>(a.in[0]) - g_base), a.xcd_group);
+    check_prologue(k, a);
     return hipSuccess;
 }
 #define STUB(name) \
@@ -55,9 +116,12 @@ STUB(launch_3d_d64) STUB(launch_3d_d128) STUB(launch_3d_d256)
 STUB(launch_table_interleaved_bf16) STUB(launch_table_halfsplit_bf16)
 STUB(launch_table_interleaved_f16) STUB(launch_table_halfsplit_f16)
 STUB(launch_table_halfsplit_any_bf16) STUB(launch_table_halfsplit_any_f16)
-hipError_t qkrope::launch_sumsq(const SumsqArgs &, int64_t tokens, int threads, hipStream_t)
+hipError_t qkrope::launch_sumsq(const SumsqArgs &a, int64_t tokens, int threads, hipStream_t)
 {
     std::printf("launch sumsq threads=%d tokens=%lld\n", threads, (long long)tokens);
+    const long long chunks = a.q_chunks + a.k_chunks;      // 16-byte chunks read per token
+    if (chunks > 0) need(a.qkv, ((tokens - 1) * a.row + chunks * 8) * 2, "sums load");
+    need(a.out, tokens * 8, "sums store");
     return hipSuccess;
 }
 
@@ -68,6 +132,18 @@ hipError_t qkrope::launch_cam(const CamArgs &a, int act, int cpl, int64_t blocks
                 "xcd=%u blocks=%lld lds=%d row_chunks=%d vec=%d\n",
                 act, cpl, a.lanes_per_token, a.heads_per_group, a.groups, a.tiles, a.tiles_padded,
                 a.xcd_group, (long long)blocks, lds_bytes, a.row_chunks, a.vec_store);
+    // qkrope_kernels_cam.hip: token rows of q, k, v; one 4x4 fp32 matrix per (b, n) each; table
+    // rows [N, D/2]; output planes [B, H, D, N]; inflation [B, H, N]
+    const long long BN = (long long)a.batch * a.num_tokens, D = a.head_dim, H = a.heads;
+    for (int r = 0; r < 3; ++r) {
+        need(a.in[r], ((BN - 1) * a.in_stride[r] + H * D) * 2, "cam load");
+        need(a.out[r], BN * H * D * 2, "cam store");
+    }
+    need(a.proj[0], BN * 64, "proj_q");
+    need(a.proj[1], BN * 64, "proj_kv");
+    need(a.cos_table, a.num_tokens * (D / 2) * 4, "cam cos");
+    need(a.sin_table, a.num_tokens * (D / 2) * 4, "cam sin");
+    if (a.inflation) need(a.inflation, BN * H * 4, "inflation");
     return hipSuccess;
 }
 
@@ -82,6 +158,8 @@ int main(int argc, char **argv)
     for (int i = 2; i < argc && i < 42; ++i) v[i - 2] = std::atof(argv[i]);
     auto I = [&](int i) { return (long long)v[i]; };
     g_base = reinterpret_cast<uintptr_t>(at(0));
+    // QKROPE_TEST_SHRINK=n: the first input is registered n bytes short (a check of the checker)
+    const long long shrink = std::getenv("QKROPE_TEST_SHRINK") ? std::atoll(std::getenv("QKROPE_TEST_SHRINK")) : 0;
     int st;
     if (!std::strcmp(form, "3d")) {
         // T ppf pph ppw cf ch cw Hq Hk Hv D interleave is_qk_norm fp8 token_offset use_sumsq
@@ -92,16 +170,39 @@ int main(int argc, char **argv)
         const bool sums = I(15) != 0;
         const void *qkv = static_cast<const char *>(at(0)) + I(24);
         void *qo = I(25) == 1 ? static_cast<char *>(at(0)) + 4096 : at(1);
+        const long long es = I(13) ? 1 : 2;
+        reg(qkv, T * (I(7) + I(8) + I(9)) * D * 2 - shrink);
+        reg(qo, T * I(7) * D * es);
+        reg(at(2), T * I(8) * D * es);
+        reg(at(3), T * I(9) * D * es);
+        reg(at(4), I(7) * D * 2);
+        reg(at(5), I(8) * D * 2);
+        if (sums) reg(at(6), T * 8);
         st = qkrope_run_3d_sharded(h, qkv, at(4), at(5), T, I(14), sums ? (const float *)at(6) : nullptr,
-                                   I(7) * D, I(8) * D, (int)I(1), (int)I(2), (int)I(3), (int)I(4),
+                                   (I(7) ? I(7) : 1) * D, (I(8) ? I(8) : 1) * D, (int)I(1), (int)I(2), (int)I(3), (int)I(4),
                                    (int)I(5), (int)I(6), (int)I(7), (int)I(8), (int)I(9), D, v[16],
                                    v[17], (int)I(11), v[18], v[19], v[20], v[21], (int)I(12),
                                    (int)I(13), v[22], v[23], qo, at(2), at(3), nullptr);
+    } else if (!std::strcmp(form, "sumsq")) {
+        // T Hq Hk Hv D
+        const long long T = I(0);
+        const int D = (int)I(4);
+        reg(at(0), T * (I(1) + I(2) + I(3)) * D * 2 - shrink);
+        reg(at(6), T * 8);
+        st = qkrope_sumsq_3d(h, at(0), T, (int)I(1), (int)I(2), (int)I(3), D, (float *)at(6),
+                             nullptr);
     } else if (!std::strcmp(form, "cam")) {
         // B N H D act
         const long long B = I(0), N = I(1);
         const int H = (int)I(2), D = (int)I(3);
         const long long s = (long long)H * D;
+        for (int i = 0; i < 3; ++i) reg(at(i), B * N * s * 2 - (i == 0 ? shrink : 0));
+        reg(at(3), B * N * 64);
+        reg(at(4), B * N * 64);
+        reg(at(5), N * (D / 2) * 4);
+        reg(at(6), N * (D / 2) * 4);
+        for (int i = 7; i < 10; ++i) reg(at(i), B * N * s * 2);
+        reg(at(10), B * H * N * 4);
         st = qkrope_cam_prep(h, at(0), at(1), at(2), (int)I(4), (const float *)at(3),
                              (const float *)at(4), (const float *)at(5), (const float *)at(6),
                              0.5f, B, N, H, D, s, s, s, at(7), at(8), at(9), (float *)at(10),
@@ -115,6 +216,16 @@ int main(int argc, char **argv)
         const void *q = static_cast<const char *>(at(0)) + I(13);
         void *qo = I(14) == 1 ? const_cast<void *>(q)
                  : I(14) == 2 ? static_cast<char *>(const_cast<void *>(q)) + 16 : at(4);
+        const long long os = I(8) == 3 ? 1 : 2, ts = I(9) == 1 ? 4 : 2;
+        const long long wl = I(6) == 2 ? 0 : D;            // per-head weights [D]
+        reg(q, ((T - 1) * qs + (long long)Hq * D) * 2 - shrink);
+        reg(at(1), T * Hk * D * 2);
+        reg(at(2), T * (R / 2) * ts);
+        reg(at(3), T * (R / 2) * ts);
+        if (I(14) == 0) reg(qo, ((T - 1) * qs + (long long)Hq * D) * os);
+        reg(at(5), T * Hk * D * os);
+        reg(at(6), (wl ? wl : (long long)Hq * D) * 2);
+        reg(at(7), (wl ? wl : (long long)Hk * D) * 2);
         st = qkrope_run_table_ex(h, q, at(1), at(6), at(7), at(2), at(3), (int)I(9), (int)I(7),
                                  (int)I(8), v[12], v[11], T, Hq, Hk, D, R, (int)I(5), (int)I(6), qs,
                                  (long long)Hk * D, R / 2, R / 2, qo, at(5), qs,
@@ -139,10 +250,17 @@ def driver(tmp_path_factory):
     return str(exe)
 
 
-def run(driver, *args):
-    """The recorded launches (dicts of their fields) and the call's status."""
+def run(driver, *args, shrink=0, allow_oob=False):
+    """The recorded launches (dicts of their fields) and the call's status. Fails if any launch
+    lets its kernel touch memory outside the caller's tensors (unless allow_oob)."""
+    env = dict(os.environ, QKROPE_TEST_SHRINK=str(shrink)) if shrink else None
     out = subprocess.run([driver, *map(str, args)], capture_output=True, text=True, timeout=60,
-                         check=True).stdout.splitlines()
+                         check=True, env=env).stdout.splitlines()
+    oob = [l for l in out if l.startswith("OOB ")]
+    if oob and not allow_oob:
+        raise AssertionError(f"{args}: out-of-tensor ranges: {oob[:4]}")
+    if allow_oob:
+        return oob
     launches = []
     for line in out:
         if line.startswith("launch "):
@@ -323,3 +441,54 @@ def test_table_argument_rules(driver, kw, status):
                        args.pop("R"), **args)
     assert st == status
     assert (ls != []) == (status == 0)
+
+
+# --- every address a launch lets its kernel form lies in a caller's tensor ----------------------
+# (run() checks this for every launch of every test above; these cases aim at the edges)
+
+def test_range_check_catches_a_tensor_one_chunk_short(driver):
+    """The checker is not vacuous: registering the input 16 bytes short is caught."""
+    oob = run(driver, "3d", 120, 2, 3, 4, 32, 48, 48, 4, 2, 2, 128, 1, 1, 0, 0, 0, 1e-6, 1e4,
+              1.0, 0.0, 0.0, 1.0, 1.0, 1.0, 0, 0, shrink=16, allow_oob=True)
+    assert oob and oob[0].startswith("OOB load v")
+    oob = run(driver, "table", 33, 4, 2, 128, 128, 0, 1, 0, 0, 1, 0, 1e-6, 1.0, 0, 0,
+              shrink=16, allow_oob=True)
+    assert oob and oob[0].startswith("OOB load q")
+    assert run(driver, "cam", 2, 130, 3, 64, 0, shrink=16, allow_oob=True)[0].startswith("OOB cam")
+    assert run(driver, "sumsq", 50, 4, 4, 0, 64, shrink=16, allow_oob=True)
+
+
+@pytest.mark.parametrize("Hq,Hk,norm", [(0, 3, 1), (0, 3, 2), (3, 0, 1), (3, 0, 2), (0, 2, 0),
+                                        (5, 0, 0)])
+def test_table_regions_without_heads_stay_in_bounds(driver, Hq, Hk, norm):
+    """A region without heads (NULL-able pointers) borrows the other region's row and weights."""
+    for inter in (0, 1):
+        (l,), st = run_table(driver, 37, Hq, Hk, 128, 96, inter=inter, norm=norm)
+        assert st == 0
+
+
+@pytest.mark.parametrize("heads,norm,fp8,sums", [
+    ((4, 0, 2), 1, 0, 0), ((4, 2, 0), 1, 1, 0), ((0, 3, 3), 1, 0, 0), ((0, 0, 5), 0, 0, 0),
+    ((2, 2, 0), 1, 0, 1), ((0, 4, 1), 1, 1, 1), ((6, 0, 0), 0, 1, 0),
+])
+def test_3d_regions_without_heads_stay_in_bounds(driver, heads, norm, fp8, sums):
+    (l,), st = run_3d(driver, 24, (2, 3, 4), (32, 48, 48), heads, 128, norm=norm, fp8=fp8,
+                      sums=sums)
+    assert st == 0
+
+
+def test_two_token_workgroups_with_an_odd_token_count(driver):
+    # 160 lanes a token, two tokens per workgroup: the last workgroup's missing second token
+    # re-reads the first one's row and stores nothing
+    (l,), st = run_3d(driver, 15, (1, 3, 5), (16, 24, 24), (20, 20, 20), 64, interleave=0, fp8=1)
+    assert st == 0 and l["tpw"] == 2 and l["blocks"] == 8
+
+
+def test_sums_kernel_ranges_and_launch_loop(driver):
+    per = ((1 << 32) - 1) // 64          # one head of 64 in Q and K: 64-lane workgroups
+    ls, st = run(driver, "sumsq", per + 7, 1, 1, 1, 64)
+    assert st == 0 and [l["tokens"] for l in ls] == [per, 7]
+    ls, st = run(driver, "sumsq", 300, 0, 0, 3, 64)             # no Q or K heads: zeros written
+    assert st == 0 and len(ls) == 1
+    ls, st = run(driver, "sumsq", 64, 48, 48, 48, 128)          # rows wider than one workgroup
+    assert st == 0 and ls[0]["threads"] == 768
