@@ -17,7 +17,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# QKROPE_ORACLE_LIB: load another build of oracle.c instead (the mutation test runs the pins
+# against copies with planted mistakes)
+LIB_PATH = os.environ.get("QKROPE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 SOURCE = os.path.join(_HERE, "oracle.c")
 
 NORM_MODES = {"none": 0, "per_head": 1, "across_heads": 2}
