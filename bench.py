@@ -363,9 +363,10 @@ def eager_table_chain(q, k, q_weight, k_weight, table, eps, rotary_dim, interlea
 
 def crossover(dev, warmup) -> None:
     """Per-call wall time of the fused table-form call (through the page's signature, outputs
-    allocated per call as a consumer does) and of the eager chain, for 64..65536 tokens of the
-    24-head, head_dim-128 interleaved workload with a bf16 table; one JSON line per size, then
-    the smallest size from which on the fused call is never slower."""
+    allocated per call as a consumer does), of the eager chain, and of the fused call marshalled
+    once beforehand (PreparedTable: one C call, the floor of the host cost), for 64..65536 tokens
+    of the 24-head, head_dim-128 interleaved workload with a bf16 table; one JSON line per size,
+    then the smallest size from which on the fused call is never slower than the eager chain."""
     import torch
     import qk_rmsnorm_rope_amd as qr
     from qk_rmsnorm_rope_amd import workloads as wl
@@ -379,13 +380,16 @@ def crossover(dev, warmup) -> None:
         args = (q, k, g["q_weight"], g["k_weight"], tab, w.eps)
         fused = lambda: qr.fused_qk_norm_rope(*args, rotary_dim=w.rotary_dim, interleaved=True)
         eager = lambda: eager_table_chain(*args, w.rotary_dim, True)
+        # reference: the same call marshalled once, outputs allocated once (one C call)
+        prepared = qr.PreparedTable(*args, q_out=torch.empty_like(q), k_out=torch.empty_like(k),
+                                    rotary_dim=w.rotary_dim, interleaved=True)
         if T == sizes[0]:
             a, b = fused(), eager()
             torch.cuda.synchronize()
             assert all((x.float() - y.float()).abs().max().item() < 0.05 for x, y in zip(a, b))
         n = max(20, min(2000, (1 << 22) // T))
         res = {"tokens": T, "calls": n}
-        for name, fn in (("fused_us", fused), ("eager_us", eager)):
+        for name, fn in (("fused_us", fused), ("eager_us", eager), ("prepared_us", prepared)):
             for _ in range(warmup):
                 fn()
             torch.cuda.synchronize()

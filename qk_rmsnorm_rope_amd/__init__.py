@@ -399,6 +399,31 @@ def qkrope_run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
 
 # --- the pages' Python signatures --------------------------------------------------------------
 
+# The page signatures are called once per attention site and step, so their host cost matters:
+# they are marshalled in C++ (_qkrope_native, built next to libqkrope.so) with the same checks
+# and messages as the functions above, then make one call into the same C ABI.
+_native_mod = None
+
+
+def native():
+    """The C++ marshaller of the page signatures (loaded once, after libqkrope.so)."""
+    global _native_mod
+    if _native_mod is None:
+        lib()
+        try:
+            from . import _qkrope_native
+        except ImportError as e:
+            raise RuntimeError("qk_rmsnorm_rope_amd/_qkrope_native is missing or fails to load "
+                               f"({e}): build it with `python qk_rmsnorm_rope_amd/build.py`") from e
+        _native_mod = _qkrope_native
+    return _native_mod
+
+
+def _device_error(e: RuntimeError) -> RuntimeError:
+    """A library status from the marshaller becomes QkropeError; other errors pass unchanged."""
+    return QkropeError(str(e)) if str(e).startswith("qkrope_") else e
+
+
 def fused_qk_norm_rope(q, k, q_weight, k_weight, rope_table, eps, *, head_dim=None,
                        rotary_dim=None, interleaved=False):
     """Q/K RMSNorm (per head, [head_dim] weights) then RoPE from a [tokens, rotary_dim] table.
@@ -406,14 +431,13 @@ def fused_qk_norm_rope(q, k, q_weight, k_weight, rope_table, eps, *, head_dim=No
     Signature of vLLM-Omni's fused_qk_norm_rope. q/k are bfloat16 or float16; the table is
     float32 or q's dtype. Returns new (q, k) with the inputs' shapes.
     """
-    q_out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    k_out = torch.empty(k.shape, dtype=k.dtype, device=k.device)
-    R = rotary_dim if rotary_dim is not None else rope_table.shape[-1]
-    # the packed [cos | sin] row as two column views
-    qkrope_run_table_ex(q, k, q_weight, k_weight, rope_table[:, : R // 2],
-                        rope_table[:, R // 2: R], eps, q_out=q_out, k_out=k_out,
-                        head_dim=head_dim, rotary_dim=R, interleaved=interleaved)
-    return q_out, k_out
+    try:
+        return (_native_mod or native()).table(
+            q, k, q_weight, k_weight, rope_table, float(eps),
+            -1 if head_dim is None else int(head_dim), -1 if rotary_dim is None else int(rotary_dim),
+            bool(interleaved))
+    except RuntimeError as e:
+        raise _device_error(e) from None
 
 
 def fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
@@ -425,24 +449,20 @@ def fused_qk_rmsnorm_rope(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_c
     """Across-heads QK RMSNorm + 3D RoPE + V copy (+ FP8), FlashInfer's signature.
 
     Returns (q_out, k_out, v_out), each [B, S, H, D] for a 3D qkv or [T, H, D] for a 2D one;
-    pre-allocated outputs are used when given (destination-passing style).
+    pre-allocated outputs are used when given (destination-passing style). qkv is
+    [tokens, row] with tokens a multiple of ppf*pph*ppw, or [batch, seq_len, row] with
+    seq_len == ppf*pph*ppw.
     """
-    lead = tuple(qkv.shape[:-1])
-    odt = torch.float8_e4m3fn if output_fp8 else torch.bfloat16
-    outs = []
-    for o, H in ((q_out, num_heads_q), (k_out, num_heads_k), (v_out, num_heads_v)):
-        outs.append(o if o is not None else
-                    torch.empty(lead + (H, head_dim), dtype=odt, device=qkv.device))
-    qkrope_run_3d(qkv, q_weight, k_weight, ppf=ppf, pph=pph, ppw=ppw,
-                  num_frame_channels=num_frame_channels, num_height_channels=num_height_channels,
-                  num_width_channels=num_width_channels, num_heads_q=num_heads_q,
-                  num_heads_k=num_heads_k, num_heads_v=num_heads_v, head_dim=head_dim,
-                  q_out=outs[0], k_out=outs[1], v_out=outs[2], eps=eps, base=base,
-                  interleave=interleave, factor=factor, low=low, high=high,
-                  attention_factor=attention_factor, is_qk_norm=is_qk_norm,
-                  output_fp8=output_fp8, output_quant_scale=output_quant_scale,
-                  v_quant_scale=v_quant_scale)
-    return tuple(outs)
+    try:
+        return (_native_mod or native()).rope3d(
+            qkv, q_weight, k_weight, int(ppf), int(pph), int(ppw), int(num_frame_channels),
+            int(num_height_channels), int(num_width_channels), int(num_heads_q), int(num_heads_k),
+            int(num_heads_v), int(head_dim), float(eps), float(base), bool(interleave),
+            float(factor), float(low), float(high), float(attention_factor), bool(is_qk_norm),
+            bool(output_fp8), float(output_quant_scale), float(v_quant_scale), q_out, k_out,
+            v_out)
+    except RuntimeError as e:
+        raise _device_error(e) from None
 
 
 class Prepared3D:

@@ -26,12 +26,15 @@ def pytest_terminal_summary(terminalreporter):
     if rows:
         tr = terminalreporter
         tr.section("observed parity against the oracle's rounded result")
-        tr.write_line(f"{'output':64s} {'elements':>10s} {'bit-equal':>9s} {'<=1 ulp':>8s} "
-                      f"{'max ulp':>7s}")
+        tr.write_line(f"{'output':56s} {'elements':>10s} {'bit-equal':>9s} {'<=1 ulp':>8s} "
+                      f"{'max ulp*':>8s} {'tol used':>8s}")
         for k in sorted(rows):
             v = rows[k]
-            tr.write_line(f"{k:64s} {v['n']:10d} {v['bit_equal'] / v['n']:9.4%} "
-                          f"{v['within_1ulp'] / v['n']:8.4%} {v['max_ulp']:7d}")
+            tr.write_line(f"{k:56s} {v['n']:10d} {v['bit_equal'] / v['n']:9.4%} "
+                          f"{v['within_1ulp'] / v['n']:8.4%} {v['max_ulp']:8d} "
+                          f"{v['max_tol_used']:8.3f}")
+        tr.write_line("* among outputs where the relative part of the tolerance governs; "
+                      "tol used: the largest err / bound (E4M3: codes)")
     out = os.environ.get("QKROPE_PARITY_REPORT")
     if out:
         with open(out, "w") as f:

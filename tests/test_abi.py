@@ -151,3 +151,25 @@ def test_3d_binding_requires_seq_len_of_the_grid():
         qr.fused_qk_rmsnorm_rope(qkv, None, None, **kw)
     with pytest.raises(ValueError, match="seq_len"):
         qr.qkrope_run_3d(qkv, None, None, q_out=None, k_out=None, v_out=None, **kw)
+
+
+def test_native_marshaller_loads_and_checks_arguments_on_the_host():
+    """The page signatures go through the C++ marshaller (_qkrope_native), linked to the same
+    libqkrope.so; its argument checks raise ValueError before any device is touched."""
+    import torch
+    import qk_rmsnorm_rope_amd as qr
+    n = qr.native()
+    assert hasattr(n, "table") and hasattr(n, "rope3d")
+    maps = open("/proc/self/maps").read()
+    assert qr.LIB_PATH in maps and "_qkrope_native" in maps
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    tab = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        qr.fused_qk_norm_rope(q, q, None, None, tab, 1e-6)
+    with pytest.raises(ValueError, match="bfloat16 or both float16"):
+        qr.fused_qk_norm_rope(q.float(), q.float(), None, None, tab, 1e-6)
+    with pytest.raises(ValueError, match="qkv must be"):
+        qr.fused_qk_rmsnorm_rope(torch.zeros((4, 100), dtype=torch.bfloat16), None, None, ppf=1,
+                                 pph=1, ppw=4, num_frame_channels=0, num_height_channels=0,
+                                 num_width_channels=64, num_heads_q=1, num_heads_k=1,
+                                 num_heads_v=1, head_dim=64)
