@@ -446,6 +446,302 @@ def roofline(w, mean_launch) -> dict:
             "algorithmic_bytes": nbytes, "mean_launch_us": mean_launch * 1e6}
 
 
+# --- profiles: rocprofv3 passes over bench.py's own sequences, and their summaries -------------
+#
+# `bench.py --profile-workload NAME [--profile-dir DIR]` runs, each as a child process under
+# rocprofv3 (from /tmp, TMPDIR=/tmp), a kernel trace of bench.py's timed sequence and four
+# counter passes of a short stream-launched sequence, then writes profiles/counters_NAME.md
+# (kernel durations, HBM bytes per dispatch against the algorithmic bytes, and the traffic
+# record bench.py reports) and profiles/sq_NAME.md (instruction mix, VALU busy, LDS bank
+# conflicts). `--profile-workload copy` profiles the plain copy that calibrates the byte
+# counters (profiles/copy_calibration.md); it is read by every other summary, so profile it
+# first. Raw rocprofv3 output stays in DIR.
+
+PMC_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    # read requests by size: FETCH_SIZE's expression weighs each 128-byte request as 64 bytes
+    # unless TCC_BUBBLE counts it, so its calibration is cross-checked from the request sizes
+    "rdreq": ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+              "TCC_EA0_RDREQ_128B_sum"],
+    "sq": ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVES", "SQ_ACTIVE_INST_VALU",
+           "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"],
+}
+COPY_KERNEL = "vectorized_elementwise_kernel<8"   # torch's copy in --copy-calibration
+
+
+def _rel(path: str) -> str:
+    return os.path.relpath(path, ROOT)
+
+
+def profile_commands(name: str, out_dir: str) -> dict:
+    """The rocprofv3 command of each pass (argv lists, paths absolute)."""
+    bench = os.path.join(ROOT, "bench.py")
+    if name == "copy":
+        prog, prog_pmc = None, ["python3", bench, "--copy-calibration", "--steps", "5",
+                                "--warmup", "2"]
+    else:
+        prog = ["python3", bench, "--workload", name, "--profile-run", "--steps", "100",
+                "--warmup", "20"]
+        prog_pmc = ["python3", bench, "--workload", name, "--profile-run", "--stream",
+                    "--steps", "5", "--warmup", "2"]
+    cmds = {}
+    if prog:
+        cmds["trace"] = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv",
+                         "-d", os.path.join(out_dir, f"trace_{name}"), "-o", "trace", "--", *prog]
+    for p, counters in PMC_PASSES.items():
+        if name == "copy" and p == "sq":
+            continue
+        cmds[p] = ["rocprofv3", "--pmc", *counters, "--output-format", "csv",
+                   "-d", os.path.join(out_dir, f"{p}_{name}"), "-o", p, "--", *prog_pmc]
+    return cmds
+
+
+def _show(cmd: list) -> str:
+    """A command as it reads from the repository root (the profile summaries quote it)."""
+    out = []
+    for a in cmd:
+        out.append(_rel(a) if os.path.isabs(a) and a.startswith(ROOT) else a)
+    return " ".join(out)
+
+
+def _csv_rows(path: str) -> list:
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(out_dir: str, pass_name: str, name: str, suffix: str) -> str:
+    d = os.path.join(out_dir, f"{pass_name}_{name}")
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _counters(out_dir: str, pass_name: str, name: str, kernel: str) -> tuple:
+    """Per-dispatch values of each counter for kernels whose name contains `kernel`:
+    ({counter: [values]}, kernel name)."""
+    import collections
+    vals, kname = collections.defaultdict(list), None
+    for r in _csv_rows(_find(out_dir, pass_name, name, "counter_collection.csv")):
+        if kernel in r["Kernel_Name"]:
+            vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+            kname = r["Kernel_Name"]
+    if not vals:
+        raise ValueError(f"{pass_name}_{name}: no dispatch of {kernel}")
+    return vals, kname
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+
+def _record(path: str, tag: str) -> dict | None:
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!--\s*" + tag + r"\s+(\{.*?\})\s*-->", open(path).read(), re.S)
+    return json.loads(m.group(1)) if m else None
+
+
+def summarize_copy(out_dir: str, cmds: dict) -> str:
+    """profiles/copy_calibration.md from the copy's fetch, write and read-request passes."""
+    n = 1 << 29                                   # bf16 elements: 1 GiB read, 1 GiB written
+    true_kib = 2 * n / 1024
+    f, kname = _counters(out_dir, "fetch", "copy", COPY_KERNEL)
+    w, _ = _counters(out_dir, "write", "copy", COPY_KERNEL)
+    rq, _ = _counters(out_dir, "rdreq", "copy", COPY_KERNEL)
+    fetch, write = _median(f["FETCH_SIZE"]), _median(w["WRITE_SIZE"])
+    r128, r64 = _median(rq["TCC_EA0_RDREQ_128B_sum"]), _median(rq["TCC_EA0_RDREQ_64B_sum"])
+    r32, rall = _median(rq["TCC_EA0_RDREQ_32B_sum"]), _median(rq["TCC_EA0_RDREQ_sum"])
+    req_bytes = 128 * r128 + 64 * r64 + 32 * r32
+    rec = {"fetch_factor": round(true_kib / fetch, 4), "write_factor": round(true_kib / write, 4)}
+    text = f"""# HBM counter calibration with a plain copy kernel (MI355X)
+
+Commands (repository root; `python3 bench.py --profile-workload copy` runs them and writes this
+file):
+
+""" + "".join(f"    {_show(c)}\n" for c in cmds.values()) + f"""
+The copy is torch's elementwise kernel (`{kname[:60]}...`) negating a 2^29-element bf16 tensor
+into another: 1 GiB read and 1 GiB written per launch.
+
+| counter | per launch (median of {len(f['FETCH_SIZE'])}) | true | scale applied to kernel counters |
+|---|---|---|---|
+| FETCH_SIZE (KiB) | {fetch:.0f} | {true_kib:.0f} | {rec['fetch_factor']:.4f} |
+| WRITE_SIZE (KiB) | {write:.0f} | {true_kib:.0f} | {rec['write_factor']:.4f} |
+
+Why FETCH_SIZE reads half: its expression on this part is
+`(TCC_BUBBLE*128 + (TCC_EA0_RDREQ - TCC_BUBBLE - TCC_EA0_RDREQ_32B)*64 + TCC_EA0_RDREQ_32B*32) / 1024`,
+so a read request counts 64 bytes unless TCC_BUBBLE marks it as 128. The request-size counters of
+the same copy:
+
+| TCC_EA0_RDREQ | _128B | _64B | _32B | bytes from the sizes | true bytes | ratio |
+|---|---|---|---|---|---|---|
+| {rall:.0f} | {r128:.0f} | {r64:.0f} | {r32:.0f} | {req_bytes:,.0f} | {2 * n:,} | {req_bytes / (2 * n):.5f} |
+
+Every read is a 128-byte request, which FETCH_SIZE counts as 64: the scale of 2 is the request
+size, confirmed independently of the copy's known size. Each counter record of a prologue kernel
+also gives its read bytes from the request sizes.
+
+<!-- calibration {json.dumps(rec)} -->
+"""
+    path = os.path.join(ROOT, "profiles", "copy_calibration.md")
+    open(path, "w").write(text)
+    return path
+
+
+def summarize_workload(name: str, out_dir: str, cmds: dict) -> list:
+    """profiles/counters_NAME.md and profiles/sq_NAME.md from the passes' CSV files."""
+    from qk_rmsnorm_rope_amd import workloads as wl
+    w = wl.WORKLOADS[name]
+    kern = kernel_name(w) + "<"
+    cal = _record(os.path.join(ROOT, "profiles", "copy_calibration.md"), "calibration")
+    if cal is None:
+        raise RuntimeError("profile the copy first: bench.py --profile-workload copy")
+    nbytes = algorithmic_bytes(w)
+    # kernel trace: every dispatch, and the last 100 (bench.py's timed graph replay)
+    tr = [r for r in _csv_rows(_find(out_dir, "trace", name, "kernel_trace.csv"))
+          if kern in r["Kernel_Name"]]
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr]
+    last = dur[-100:]
+    gaps = [(int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) / 1e3
+            for a, b in zip(tr[-100:], tr[-99:])]
+    srt = sorted(last)
+    pct = lambda p: srt[min(len(srt) - 1, int(p * len(srt)))]
+    avg, avg_last = sum(dur) / len(dur), sum(last) / len(last)
+    k0 = tr[0]
+    # bytes per dispatch
+    f, _ = _counters(out_dir, "fetch", name, kern)
+    wr, _ = _counters(out_dir, "write", name, kern)
+    rq, _ = _counters(out_dir, "rdreq", name, kern)
+    fetch_kib, write_kib = _median(f["FETCH_SIZE"]), _median(wr["WRITE_SIZE"])
+    fetch_b = round(fetch_kib * 1024 * cal["fetch_factor"])
+    write_b = round(write_kib * 1024 * cal["write_factor"])
+    req_b = (128 * _median(rq["TCC_EA0_RDREQ_128B_sum"]) + 64 * _median(rq["TCC_EA0_RDREQ_64B_sum"])
+             + 32 * _median(rq["TCC_EA0_RDREQ_32B_sum"]))
+    read_alg, write_alg = nbytes - output_bytes(w), output_bytes(w)
+    rec = {"bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
+           "read_request_bytes": round(req_b), "algorithmic_bytes": nbytes,
+           "avg_kernel_us": round(avg, 2), "avg_kernel_us_last100": round(avg_last, 2),
+           "kernel_source_hash": kernel_source_hash(w)}
+    gb = lambda us: nbytes / (us * 1e-6) / 1e9
+    pc = lambda us: gb(us) / PEAK_HBM_GBS
+    shown = {p: _show(c) for p, c in cmds.items()}
+    counters_md = f"""# {name}: rocprofv3 kernel trace and HBM counters (MI355X)
+
+Commands (repository root; `python3 bench.py --profile-workload {name}` runs them and writes this
+file and sq_{name}.md):
+
+    {shown['trace']}
+    {shown['fetch']}
+    {shown['write']}
+    {shown['rdreq']}
+
+The kernel trace runs bench.py's own sequence (warm-up launches on the stream, then the 100 timed
+steps captured in a HIP graph, replayed once to warm up and once timed); the counter passes
+launch on the stream (per-dispatch counters do not depend on how the launch was submitted).
+
+Kernel: `{k0['Kernel_Name']}`
+(workgroup {k0['Workgroup_Size_X']}, grid {k0['Grid_Size_X']} work-items, LDS {k0['LDS_Block_Size']} B, scratch {k0['Scratch_Size']} B, {k0['VGPR_Count']} VGPRs)
+
+| kernel trace | value |
+|---|---|
+| dispatches | {len(dur)} |
+| average duration | {avg:.2f} us |
+| min / max | {min(dur):.2f} / {max(dur):.2f} us |
+| algorithmic bytes per launch | {nbytes:,} |
+| algorithmic GB/s at the average | {gb(avg):.0f} ({pc(avg):.1%} of 8 TB/s) |
+| average of the last 100 (bench.py's timed graph replay) | {avg_last:.2f} us, {gb(avg_last):.0f} GB/s ({pc(avg_last):.1%} of 8 TB/s) |
+| last 100: p10 / median / p90 | {pct(0.1):.2f} / {pct(0.5):.2f} / {pct(0.9):.2f} us (median: {pc(pct(0.5)):.1%} of 8 TB/s) |
+| median idle gap between consecutive launches (last 100) | {_median(gaps) if gaps else 0.0:.2f} us |
+
+| HBM bytes per dispatch (median of {len(f['FETCH_SIZE'])}) | raw | bytes | algorithmic bytes | ratio |
+|---|---|---|---|---|
+| FETCH_SIZE x {cal['fetch_factor']} | {fetch_kib:.0f} KiB | {fetch_b:,} | {read_alg:,} | {fetch_b / read_alg:.4f} |
+| read requests x their size (128/64/32 B) | {_median(rq['TCC_EA0_RDREQ_sum']):.0f} requests | {req_b:,.0f} | {read_alg:,} | {req_b / read_alg:.4f} |
+| WRITE_SIZE x {cal['write_factor']} | {write_kib:.0f} KiB | {write_b:,} | {write_alg:,} | {write_b / max(write_alg, 1):.4f} |
+
+Calibration: profiles/copy_calibration.md. The record below is what bench.py reports as
+`roofline.traffic` (FETCH_SIZE and WRITE_SIZE, calibrated); it is ignored once the kernel
+sources hash differently.
+
+<!-- traffic {json.dumps(rec)} -->
+"""
+    sq, _ = _counters(out_dir, "sq", name, kern)
+    m = {c: _median(v) for c, v in sq.items()}
+    cus = 256
+    try:
+        info = _csv_rows(_find(out_dir, "sq", name, "agent_info.csv"))
+        cus = int(next(r["Cu_Count"] for r in info if int(r.get("Cu_Count") or 0) > 0))
+    except (FileNotFoundError, StopIteration, KeyError, ValueError):
+        pass
+    waves = m["SQ_WAVES"]
+    valu_busy = 100 * m["SQ_ACTIVE_INST_VALU"] / cus / m["GRBM_GUI_ACTIVE"]
+    lds_conf = 100 * m["SQ_LDS_BANK_CONFLICT"] / cus / m["GRBM_GUI_ACTIVE"]
+    sq_md = f"""# {name}: instruction mix and VALU / LDS use (rocprofv3 SQ counters, MI355X)
+
+Command (repository root; written by `python3 bench.py --profile-workload {name}`):
+
+    {shown['sq']}
+
+Kernel `{k0['Kernel_Name']}`, medians over {len(sq['SQ_WAVES'])} dispatches of the stream-launched
+sequence. VALU busy and LDS bank conflicts are rocprofv3's derived metrics VALUBusy =
+100 * SQ_ACTIVE_INST_VALU / CU_NUM / GRBM_GUI_ACTIVE and LDSBankConflict =
+100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CU_NUM, with CU_NUM = {cus}.
+
+| counter (per dispatch) | value | per wave |
+|---|---|---|
+| SQ_WAVES | {waves:,.0f} | |
+| SQ_INSTS_VALU | {m['SQ_INSTS_VALU']:,.0f} | {m['SQ_INSTS_VALU'] / waves:.1f} |
+| SQ_INSTS_SALU | {m['SQ_INSTS_SALU']:,.0f} | {m['SQ_INSTS_SALU'] / waves:.1f} |
+| SQ_INSTS_LDS | {m['SQ_INSTS_LDS']:,.0f} | {m['SQ_INSTS_LDS'] / waves:.1f} |
+| SQ_LDS_BANK_CONFLICT (cycles) | {m['SQ_LDS_BANK_CONFLICT']:,.0f} | {m['SQ_LDS_BANK_CONFLICT'] / waves:.2f} |
+| SQ_ACTIVE_INST_VALU | {m['SQ_ACTIVE_INST_VALU']:,.0f} | |
+| GRBM_GUI_ACTIVE (cycles) | {m['GRBM_GUI_ACTIVE']:,.0f} | |
+| **VALU busy** | **{valu_busy:.1f}%** | |
+| LDS bank conflict | {lds_conf:.2f}% of cycles | |
+
+<!-- sq {json.dumps({"valu_per_wave": round(m['SQ_INSTS_VALU'] / waves, 1), "valu_busy_pct": round(valu_busy, 1), "lds_bank_conflict_per_wave": round(m['SQ_LDS_BANK_CONFLICT'] / waves, 2), "kernel_source_hash": kernel_source_hash(w)})} -->
+"""
+    paths = []
+    for fname, text in ((f"counters_{name}.md", counters_md), (f"sq_{name}.md", sq_md)):
+        path = os.path.join(ROOT, "profiles", fname)
+        open(path, "w").write(text)
+        paths.append(path)
+    return paths
+
+
+def profile_workload(name: str, out_dir: str, only_summarize: bool = False) -> int:
+    """Run the rocprofv3 passes of `name` (a workload, or "copy") as child processes, then
+    write the summaries. Each pass prints one line; a pass that fails stops the run."""
+    import subprocess
+    out_dir = os.path.abspath(out_dir)
+    os.makedirs(out_dir, exist_ok=True)
+    cmds = profile_commands(name, out_dir)
+    env = dict(os.environ, TMPDIR="/tmp")
+    if not only_summarize:
+        for p, cmd in cmds.items():
+            t0 = time.time()
+            log = os.path.join(out_dir, f"{p}_{name}.log")
+            with open(log, "w") as lf:
+                r = subprocess.run(cmd, cwd="/tmp", env=env, stdout=lf, stderr=subprocess.STDOUT,
+                                   timeout=300)
+            print(f"profile {name} {p}: rc {r.returncode} in {time.time() - t0:.1f}s", flush=True)
+            # rocprofv3 itself may end with a segmentation fault after the program is done and
+            # its output written; the summary below checks that the files are there
+            if r.returncode not in (0, -11, 139):
+                print(open(log).read()[-3000:], flush=True)
+                return r.returncode
+    paths = summarize_copy(out_dir, cmds) if name == "copy" else \
+        summarize_workload(name, out_dir, cmds)
+    for p in ([paths] if isinstance(paths, str) else paths):
+        print(f"wrote {_rel(p)}", flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -462,7 +758,16 @@ def main() -> int:
     ap.add_argument("--crossover", action="store_true")
     ap.add_argument("--stream", action="store_true")
     ap.add_argument("--cold", action="store_true")
+    ap.add_argument("--profile-workload", metavar="NAME",
+                    help="run the rocprofv3 passes of NAME (a workload, or 'copy') and write "
+                         "its summaries under profiles/")
+    ap.add_argument("--profile-dir", default=os.path.join(ROOT, "gpurun_out", "prof"),
+                    help="where --profile-workload keeps rocprofv3's raw output")
+    ap.add_argument("--summarize-only", action="store_true",
+                    help="with --profile-workload: rewrite the summaries from existing output")
     args = ap.parse_args()
+    if args.profile_workload:
+        return profile_workload(args.profile_workload, args.profile_dir, args.summarize_only)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the prologue is token-local and the library runs on "
