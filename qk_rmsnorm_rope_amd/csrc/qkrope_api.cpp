@@ -65,7 +65,9 @@ using namespace qkrope::host;
 // region) leaves half a wave idle; two such tokens share a workgroup instead, filling whole
 // waves (36960 x 3x20 x 64: 160 lanes per token, 83% -> 100% of lanes busy).
 // `min_lanes`: lanes a token needs besides its chunks (3D: one per angle pair, head_dim / 2).
-bool choose_shape(const int64_t *n, int nreg, int min_lanes, LaunchShape *s)
+// `allow_two`: two tokens per workgroup are allowed only when every token stride, in bytes, is
+// below 2^24: the kernel forms the second token's row offsets with 24-bit multiplies.
+bool choose_shape(const int64_t *n, int nreg, int min_lanes, LaunchShape *s, bool allow_two = true)
 {
     int64_t total = 0, maxn = 0;
     for (int r = 0; r < nreg; ++r) {
@@ -79,8 +81,8 @@ bool choose_shape(const int64_t *n, int nreg, int min_lanes, LaunchShape *s)
         if (ns == 1) {
             const int64_t t32 = (maxn + 31) / 32 * 32;
             const double util2 = (double)total / ((double)nreg * t32);
-            if (t32 % 64 != 0 && 2 * t32 <= 1024 && t32 >= min_lanes && util2 >= 0.75 &&
-                util2 > util + 0.05) {
+            if (allow_two && t32 % 64 != 0 && 2 * t32 <= 1024 && t32 >= min_lanes &&
+                util2 >= 0.75 && util2 > util + 0.05) {
                 *s = LaunchShape{(int)(2 * t32), 1, true, 0, 0, 2};
                 return true;
             }
@@ -307,8 +309,11 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
 
     const int L = next_pow2(D / 8);           // lanes per head: one 16-byte chunk each
     const int64_t n_units[2] = {(int64_t)Hq * L, (int64_t)Hk * L};
+    const int64_t k24 = int64_t(1) << 24;
+    const bool small_strides = 2 * std::max(c.q_stride, c.k_stride) < k24 &&
+                               osize * std::max(c.q_out_stride, c.k_out_stride) < k24;
     LaunchShape shape;
-    if (!choose_shape(n_units, 2, 1, &shape))
+    if (!choose_shape(n_units, 2, 1, &shape, small_strides))
         return fail(QKROPE_ERR_UNSUPPORTED, "too many heads for one workgroup per token");
 
     KernelArgs a;

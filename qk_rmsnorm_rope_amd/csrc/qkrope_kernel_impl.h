@@ -112,7 +112,8 @@ __device__ __forceinline__ float sat_e4m3(float y)
 }
 
 // Each conversion writes one 16-bit half of its destination and keeps the other; the first of
-// each pair starts from a register that is live anyway (its bits are overwritten by the second).
+// each pair starts from the register of its own first input, which dies there (the other half is
+// written by the second conversion), so no copy is needed.
 // The conversion itself maps NaN to the NaN code, so saturation is only needed where some
 // |y| > 448; that is rare, so lanes test the chunk's largest magnitude (v_max3 ignores NaN)
 // and only those above 448 take the saturating path.
@@ -133,9 +134,9 @@ __device__ __forceinline__ uint2 pack8_e4m3(const float yin[8])
     }
     const float a0 = y[0], a1 = y[1], a2 = y[2], a3 = y[3];
     const float b0 = y[4], b1 = y[5], b2 = y[6], b3 = y[7];
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, __float_as_int(a2), false);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, __float_as_int(a0), false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(b0, b1, __float_as_int(b2), false);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(b0, b1, __float_as_int(b0), false);
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(b2, b3, hi, true);
     return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
@@ -407,6 +408,15 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     const bool tok_ok = TPW == 1 || t0 + ts < a.num_tokens;
     const int ts_eff = tok_ok ? ts : 0;
     const int64_t t = t0 + ts_eff;
+    // The second token's rows are one stride further: offset = ts * stride_bytes + in-row
+    // offset, one 24-bit multiply-add per access (the host picks two tokens per workgroup only
+    // for strides below 2^24 bytes). The empty asm hides that ts is 0 or 1, which would
+    // otherwise turn the multiply into a select, a copy and an add.
+    uint32_t ts_ld = (uint32_t)ts_eff, ts_st = (uint32_t)ts;
+    if (TPW == 2) {
+        asm("" : "+v"(ts_ld));
+        asm("" : "+v"(ts_st));
+    }
     {
         // -- loads: every chunk of every slot, and the across-heads weights. Issued
         // unconditionally from one basic block so all are in flight together; an idle slot
@@ -423,8 +433,8 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             for (int j = 0; j < NSLOT; ++j) {
                 const int r = reg[j] < 3 ? reg[j] : 0;
                 const uint32_t oh = ok[j] ? 2 * (hoff[j] + off0) : 0u;
-                const uint32_t tok = TPW == 2 ? (uint32_t)ts_eff * (uint32_t)(2 * a.in_stride[r]) : 0u;
-                x[j] = ld16_stream<true>(sel3(r, in_q, in_k, in_v), oh + tok);
+                const uint32_t off = TPW == 2 ? __umul24(ts_ld, (uint32_t)(2 * a.in_stride[r])) + oh : oh;
+                x[j] = ld16_stream<true>(sel3(r, in_q, in_k, in_v), off);
                 if (ACROSS && (SU ? r < 2 : true)) {
                     const uint16_t *w = r == 1 ? a.weight[1] : a.weight[0];
                     wa[j] = ld16(w, (ok[j] && r < 2) ? oh : 0u);
@@ -592,7 +602,7 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) ss[j] = group_sum(ss[j], L);
         } else if (NORM == kNormAcross && !v_wg) {
-            float sq = 0.0f, sk = 0.0f;
+            float sq = -0.0f, sk = -0.0f;           // x + -0 == x for every x: folds away
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 sq += reg[j] == kQ ? ss[j] : 0.0f;
@@ -745,8 +755,8 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         for (int j = 0; j < NSLOT; ++j) {
             if (!ok[j] || !tok_ok) continue;
             const int r = reg[j] < 3 ? reg[j] : 0;
-            const uint32_t tok = TPW == 2 ? (uint32_t)ts * (uint32_t)(a.out_stride[r] * ESIZE) : 0u;
-            const uint32_t off = tok + (hoff[j] + off0) * ESIZE;
+            const uint32_t in_row = (hoff[j] + off0) * ESIZE;
+            const uint32_t off = TPW == 2 ? __umul24(ts_st, (uint32_t)(a.out_stride[r] * ESIZE)) + in_row : in_row;
             if (FP8) st8_stream(sel3(reg[j], out_q, out_k, out_v), off, make_uint2(pk[j].x, pk[j].y));
             else st16_stream(sel3(reg[j], out_q, out_k, out_v), off, pk[j]);
         }

@@ -492,3 +492,14 @@ def test_sums_kernel_ranges_and_launch_loop(driver):
     assert st == 0 and len(ls) == 1
     ls, st = run(driver, "sumsq", 64, 48, 48, 48, 128)          # rows wider than one workgroup
     assert st == 0 and ls[0]["threads"] == 768
+
+
+def test_two_tokens_per_workgroup_only_for_strides_below_2_24_bytes(driver):
+    # 20 heads of 64 in each of Q and K: 160 lanes a token, two tokens per workgroup; the kernel
+    # forms the second token's offsets with 24-bit multiplies, so wide strides take one token
+    (l,), st = run_table(driver, 33, 20, 20, 64, 64)
+    assert st == 0 and l["tpw"] == 2
+    (l,), st = run_table(driver, 33, 20, 20, 64, 64, q_stride=(1 << 23) - 8)
+    assert st == 0 and l["tpw"] == 2
+    (l,), st = run_table(driver, 33, 20, 20, 64, 64, q_stride=1 << 23)
+    assert st == 0 and l["tpw"] == 1 and l["blocks"] == 33
