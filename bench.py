@@ -459,7 +459,8 @@ def roofline(w, mean_launch) -> dict:
 
 PMC_PASSES = {
     "fetch": ["FETCH_SIZE"],
-    "write": ["WRITE_SIZE"],
+    # WRITE_SIZE is built from these two: 64-byte and 32-byte write requests
+    "write": ["WRITE_SIZE", "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"],
     # read requests by size: FETCH_SIZE's expression weighs each 128-byte request as 64 bytes
     # unless TCC_BUBBLE counts it, so its calibration is cross-checked from the request sizes
     "rdreq": ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
@@ -623,6 +624,9 @@ def summarize_workload(name: str, out_dir: str, cmds: dict) -> list:
     req_b = (128 * _median(rq["TCC_EA0_RDREQ_128B_sum"]) + 64 * _median(rq["TCC_EA0_RDREQ_64B_sum"])
              + 32 * _median(rq["TCC_EA0_RDREQ_32B_sum"]))
     read_alg, write_alg = nbytes - output_bytes(w), output_bytes(w)
+    wr64 = _median(wr["TCC_EA0_WRREQ_64B_sum"]) if "TCC_EA0_WRREQ_64B_sum" in wr else 0.0
+    wr32 = (_median(wr["TCC_EA0_WRREQ_sum"]) - wr64) if "TCC_EA0_WRREQ_sum" in wr else 0.0
+    wr32_share = 32 * wr32 / max(32 * wr32 + 64 * wr64, 1)
     rec = {"bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
            "read_request_bytes": round(req_b), "algorithmic_bytes": nbytes,
            "avg_kernel_us": round(avg, 2), "avg_kernel_us_last100": round(avg_last, 2),
@@ -664,6 +668,9 @@ Kernel: `{k0['Kernel_Name']}`
 | read requests x their size (128/64/32 B) | {_median(rq['TCC_EA0_RDREQ_sum']):.0f} requests | {req_b:,.0f} | {read_alg:,} | {req_b / read_alg:.4f} |
 | WRITE_SIZE x {cal['write_factor']} | {write_kib:.0f} KiB | {write_b:,} | {write_alg:,} | {write_b / max(write_alg, 1):.4f} |
 
+Write requests: {wr64:,.0f} of 64 bytes and {wr32:,.0f} of 32 bytes per dispatch ({wr32_share:.1%} of the written bytes
+in 32-byte requests).
+
 Calibration: profiles/copy_calibration.md. The record below is what bench.py reports as
 `roofline.traffic` (FETCH_SIZE and WRITE_SIZE, calibrated); it is ignored once the kernel
 sources hash differently.
@@ -672,15 +679,23 @@ sources hash differently.
 """
     sq, _ = _counters(out_dir, "sq", name, kern)
     m = {c: _median(v) for c, v in sq.items()}
-    cus = 256
+    sq_rows = [r for r in _csv_rows(_find(out_dir, "sq", name, "counter_collection.csv"))
+               if kern in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE"]
+    dur_us = _median([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                      for r in sq_rows]) if sq_rows else 0.0
+    cus, xcds = 256, 8
     try:
         info = _csv_rows(_find(out_dir, "sq", name, "agent_info.csv"))
-        cus = int(next(r["Cu_Count"] for r in info if int(r.get("Cu_Count") or 0) > 0))
+        gpu = next(r for r in info if str(r.get("Name", "")).startswith("gfx"))
+        cus, xcds = int(gpu["Cu_Count"]), int(gpu.get("Num_Xcc") or 1)
     except (FileNotFoundError, StopIteration, KeyError, ValueError):
         pass
     waves = m["SQ_WAVES"]
-    valu_busy = 100 * m["SQ_ACTIVE_INST_VALU"] / cus / m["GRBM_GUI_ACTIVE"]
-    lds_conf = 100 * m["SQ_LDS_BANK_CONFLICT"] / cus / m["GRBM_GUI_ACTIVE"]
+    # the per-dispatch GRBM_GUI_ACTIVE is summed over the XCDs, each counting its own busy
+    # cycles; the derived metrics divide by one XCD's (rocprofv3 takes the maximum over them)
+    active = m["GRBM_GUI_ACTIVE"] / xcds
+    valu_busy = 100 * m["SQ_ACTIVE_INST_VALU"] / cus / active
+    lds_conf = 100 * m["SQ_LDS_BANK_CONFLICT"] / cus / active
     sq_md = f"""# {name}: instruction mix and VALU / LDS use (rocprofv3 SQ counters, MI355X)
 
 Command (repository root; written by `python3 bench.py --profile-workload {name}`):
@@ -690,7 +705,9 @@ Command (repository root; written by `python3 bench.py --profile-workload {name}
 Kernel `{k0['Kernel_Name']}`, medians over {len(sq['SQ_WAVES'])} dispatches of the stream-launched
 sequence. VALU busy and LDS bank conflicts are rocprofv3's derived metrics VALUBusy =
 100 * SQ_ACTIVE_INST_VALU / CU_NUM / GRBM_GUI_ACTIVE and LDSBankConflict =
-100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CU_NUM, with CU_NUM = {cus}.
+100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CU_NUM, with CU_NUM = {cus} and GRBM_GUI_ACTIVE
+one XCD's busy cycles (the recorded value is the sum over the {xcds} XCDs: {active:,.0f} cycles
+each, {active / max(1e-9, dur_us):,.0f} MHz over the dispatch's {dur_us:.1f} us).
 
 | counter (per dispatch) | value | per wave |
 |---|---|---|

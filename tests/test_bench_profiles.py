@@ -85,7 +85,9 @@ def test_workload_summary_and_traffic_record(root):
     write_csv(os.path.join(out, f"trace_{name}", "y", "trace_kernel_trace.csv"), TRACE_COLS, rows)
     read_alg = bench.algorithmic_bytes(w) - bench.output_bytes(w)
     pmc(out, "fetch", name, kern, {"FETCH_SIZE": read_alg / 2048})
-    pmc(out, "write", name, kern, {"WRITE_SIZE": bench.output_bytes(w) / 1024})
+    pmc(out, "write", name, kern, {"WRITE_SIZE": bench.output_bytes(w) / 1024,
+                                   "TCC_EA0_WRREQ_sum": bench.output_bytes(w) / 64 + 10,
+                                   "TCC_EA0_WRREQ_64B_sum": bench.output_bytes(w) / 64})
     pmc(out, "rdreq", name, kern, {"TCC_EA0_RDREQ_sum": read_alg / 128,
                                    "TCC_EA0_RDREQ_128B_sum": read_alg / 128,
                                    "TCC_EA0_RDREQ_64B_sum": 0, "TCC_EA0_RDREQ_32B_sum": 0})
@@ -93,9 +95,11 @@ def test_workload_summary_and_traffic_record(root):
                                 "SQ_INSTS_LDS": 92400 * 20.0, "SQ_WAVES": 92400.0,
                                 "SQ_ACTIVE_INST_VALU": 0.5 * 256 * 170000,
                                 "SQ_LDS_BANK_CONFLICT": 256 * 1700.0,
-                                "GRBM_GUI_ACTIVE": 170000.0})
-    write_csv(os.path.join(out, f"sq_{name}", "x", "sq_agent_info.csv"), ["Cu_Count"],
-              [{"Cu_Count": 0}, {"Cu_Count": 256}])
+                                "GRBM_GUI_ACTIVE": 8 * 170000.0})   # summed over 8 XCDs
+    write_csv(os.path.join(out, f"sq_{name}", "x", "sq_agent_info.csv"),
+              ["Name", "Cu_Count", "Num_Xcc"],
+              [{"Name": "AMD EPYC", "Cu_Count": 16, "Num_Xcc": 1},
+               {"Name": "gfx950", "Cu_Count": 256, "Num_Xcc": 8}])
     cp, sp = bench.summarize_workload(name, out, bench.profile_commands(name, out))
     rec = bench._record(cp, "traffic")
     avg = sum(durs) / len(durs)
@@ -109,6 +113,7 @@ def test_workload_summary_and_traffic_record(root):
     assert "p10 / median / p90 | 71.00 / 75.00 / 79.00 us" in text
     assert "median idle gap between consecutive launches (last 100) | 1.00 us" in text
     assert "| FETCH_SIZE x 2.0 |" in text and "| 1.0000 |" in text
+    assert f"{bench.output_bytes(w) // 64:,} of 64 bytes and 10 of 32 bytes" in text
     sq = bench._record(sp, "sq")
     assert sq["valu_per_wave"] == 250.0 and sq["valu_busy_pct"] == 50.0
     assert sq["lds_bank_conflict_per_wave"] == pytest.approx(256 * 1700 / 92400, abs=0.01)
