@@ -368,6 +368,8 @@ int run_table(qkrope_handle h, const TableCall &c, void *stream)
     a.inv_count[1] = (float)(1.0 / (double)(across ? (int64_t)Hk * D : D));
     a.qk_scale = fp8 ? (float)c.out_scale : 1.0f;
     a.v_scale = 1.0f;
+    a.v_inv_pow2 = 0.0f;
+    a.v_limit_bits = 0;
     shape.lds_bytes = pairing == kPairHalfAny ? shape.threads * 32 : 0;
 
     KernelKey key;
@@ -521,6 +523,20 @@ int run_3d(qkrope_handle h, const Rope3DCall &c, void *stream)
     a.inv_count[1] = nk > 0 ? (float)(1.0 / nk) : 0.0f;
     a.qk_scale = c.output_fp8 ? (float)c.output_quant_scale : 1.0f;
     a.v_scale = c.output_fp8 ? (float)c.v_quant_scale : 1.0f;
+    a.v_inv_pow2 = 0.0f;
+    a.v_limit_bits = 0;
+    if (c.output_fp8) {
+        int e = 0;
+        const double m = std::frexp(c.v_quant_scale, &e);     // v_quant_scale = m * 2^e
+        if (m == 0.5 && e - 1 >= -20 && e - 1 <= 20) {
+            a.v_inv_pow2 = (float)std::ldexp(1.0, 1 - e);
+            // 448 / v_scale = 1.75 * 2^(9 - e): bf16 pattern of its exact value
+            const float lim = (float)std::ldexp(1.75, 9 - e);
+            uint32_t bits;
+            std::memcpy(&bits, &lim, 4);
+            a.v_limit_bits = bits >> 16;
+        }
+    }
     a.token_offset = (uint32_t)c.token_offset;
     a.seq_len = (uint32_t)S;
     a.hw = (uint32_t)((int64_t)c.pph * c.ppw);

@@ -52,6 +52,11 @@ struct KernelArgs {
     float inv_count[2];        // 1 / (elements the Q, K norm averages over)
     float qk_scale;            // FP8 scale for Q/K outputs (1 for bf16)
     float v_scale;             // FP8 scale for V (1 for bf16)
+    // E4M3 V with v_scale = 2^k, |k| <= 20 (bf16 activations): 1 / v_scale for the scaled packed
+    // conversion, and the bf16 pattern of 448 / v_scale, the largest magnitude it takes without
+    // saturating; 0 and 0 send V through the general path
+    float v_inv_pow2;
+    uint32_t v_limit_bits;
 
     // 3D positions of token t: s = (token_offset + t) mod seq_len; f = s / hw;
     // h = (s / ppw) mod pph; w = s mod ppw.

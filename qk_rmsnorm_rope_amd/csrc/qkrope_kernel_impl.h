@@ -141,6 +141,24 @@ __device__ __forceinline__ uint2 pack8_e4m3(const float yin[8])
     return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2v __attribute__((ext_vector_type(2)));
+
+// Magnitudes of two packed 16-bit floats as unsigned integers (order-preserving for non-NaN).
+__device__ __forceinline__ u16x2 mag16(uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7fff7fffu); }
+
+// E4M3 codes of four bf16 values (two packed pairs) divided by a power of two `inv` (the
+// conversion uses the scale's exponent only): v_cvt_scalef32_pk_fp8_bf16, round to nearest even,
+// no saturation. Each conversion writes one 16-bit half of its destination; the first starts from
+// its own input's register, whose other half the second conversion overwrites.
+__device__ __forceinline__ uint32_t pack4_e4m3_pow2(uint32_t lo, uint32_t hi, float inv)
+{
+    s16x2v r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(s16x2v, lo),
+                                                         __builtin_bit_cast(bf16x2, lo), inv, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, hi), inv, true);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // ---- memory -----------------------------------------------------------------------------------
 
 // Cache policy of the streamed activations: every input byte is read once and every output
@@ -672,6 +690,22 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             if (RS && !FP8 && v_wg) {
                 pk[j] = x[j];                           // V: bit copy (uniform branch)
                 continue;
+            }
+            if (FP8 && ACT == kActBF16 && isv && a.v_inv_pow2 != 0.0f) {   // uniform
+                // V with a power-of-two scale: v * v_scale is exact, so its code is the scaled
+                // packed conversion of the bf16 pairs as they are (it divides by the scale's power
+                // of two and rounds to nearest even, but does not saturate). A chunk with a
+                // magnitude past 448 / v_scale (an infinity or a NaN included) takes the general
+                // path below, which saturates; NaN gets the same code 0xFF on either path.
+                const uint4 xv = x[j];
+                const u16x2 m = __builtin_elementwise_max(
+                    __builtin_elementwise_max(mag16(xv.x), mag16(xv.y)),
+                    __builtin_elementwise_max(mag16(xv.z), mag16(xv.w)));
+                if ((uint32_t)__builtin_elementwise_max(m.x, m.y) <= a.v_limit_bits) {
+                    pk[j] = make_uint4(pack4_e4m3_pow2(xv.x, xv.y, a.v_inv_pow2),
+                                       pack4_e4m3_pow2(xv.z, xv.w, a.v_inv_pow2), 0, 0);
+                    continue;
+                }
             }
             float n[8];
             unpack8<ACT>(x[j], n);

@@ -207,11 +207,19 @@ CAM_PREP_S18480 = CamWorkload(
     name="cam_prep_b2_s18480_h20_d64", batch=2, ppf=20, pph=33, ppw=28, num_heads=20,
     head_dim=64, seed=SEED_BASE + 100)
 
+# The same camera prologue on a 16 x 32 x 36 grid (2 x 18432 tokens): N a multiple of 64, so
+# every output row of [B, H, D, N] starts on a 128-byte line (at 18480 the row pitch, 36960
+# bytes, is 96 mod 128 and the rows start at four phases). A comparison point for the layout's
+# cost, not a target shape.
+CAM_PREP_S18432 = CAM_PREP_S18480.with_(
+    name="cam_prep_b2_s18432_h20_d64", ppf=16, pph=32, ppw=36, seed=SEED_BASE + 110)
+
 WORKLOADS = {w.name: w for w in (TABLE_HALFSPLIT_T256, TABLE_INTERLEAVED_T4096,
                                  ROPE3D_ACROSS_S15360, ROPE3D_NEOX_FP8_S18480,
                                  ROPE3D_YARN_S122880, TABLE_INTERLEAVED_T32768,
                                  TABLE_INTERLEAVED_T32768_F16, TABLE_INTERLEAVED_T32768_E4M3,
-                                 ROPE3D_ACROSS_S15360_TP4, CAM_PREP_S18480)}
+                                 ROPE3D_ACROSS_S15360_TP4, CAM_PREP_S18480,
+                                 CAM_PREP_S18432)}
 
 
 # --- drawing -----------------------------------------------------------------------------------

@@ -34,6 +34,8 @@ EXPECTED = {
     # inflation_sq [B, H, N] fp32 out
     "cam_prep_b2_s18480_h20_d64":
         36960 * (12 * 20 * 64 + 2 * 64) + 18480 * 2 * 32 * 4 + 36960 * 20 * 4,
+    "cam_prep_b2_s18432_h20_d64":
+        36864 * (12 * 20 * 64 + 2 * 64) + 18432 * 2 * 32 * 4 + 36864 * 20 * 4,
 }
 
 
