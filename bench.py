@@ -469,6 +469,7 @@ PMC_PASSES = {
            "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"],
 }
 COPY_KERNEL = "vectorized_elementwise_kernel<8"   # torch's copy in --copy-calibration
+COPY_TRACE_STEPS = 20                              # timed copies in its kernel trace
 
 
 def _rel(path: str) -> str:
@@ -479,8 +480,9 @@ def profile_commands(name: str, out_dir: str) -> dict:
     """The rocprofv3 command of each pass (argv lists, paths absolute)."""
     bench = os.path.join(ROOT, "bench.py")
     if name == "copy":
-        prog, prog_pmc = None, ["python3", bench, "--copy-calibration", "--steps", "5",
-                                "--warmup", "2"]
+        prog = ["python3", bench, "--copy-calibration", "--steps", str(COPY_TRACE_STEPS),
+                "--warmup", "5"]
+        prog_pmc = ["python3", bench, "--copy-calibration", "--steps", "5", "--warmup", "2"]
     else:
         prog = ["python3", bench, "--workload", name, "--profile-run", "--steps", "100",
                 "--warmup", "20"]
@@ -559,6 +561,13 @@ def summarize_copy(out_dir: str, cmds: dict) -> str:
     r32, rall = _median(rq["TCC_EA0_RDREQ_32B_sum"]), _median(rq["TCC_EA0_RDREQ_sum"])
     req_bytes = 128 * r128 + 64 * r64 + 32 * r32
     rec = {"fetch_factor": round(true_kib / fetch, 4), "write_factor": round(true_kib / write, 4)}
+    # the copy's own bandwidth: the timed launches of its kernel trace (after the warm-up)
+    tr = [r for r in _csv_rows(_find(out_dir, "trace", "copy", "kernel_trace.csv"))
+          if COPY_KERNEL in r["Kernel_Name"]]
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr][-COPY_TRACE_STEPS:]
+    avg_us = sum(dur) / len(dur)
+    gbs = 4 * n / avg_us / 1e3
     text = f"""# HBM counter calibration with a plain copy kernel (MI355X)
 
 Commands (repository root; `python3 bench.py --profile-workload copy` runs them and writes this
@@ -567,6 +576,16 @@ file):
 """ + "".join(f"    {_show(c)}\n" for c in cmds.values()) + f"""
 The copy is torch's elementwise kernel (`{kname[:60]}...`) negating a 2^29-element bf16 tensor
 into another: 1 GiB read and 1 GiB written per launch.
+
+| kernel trace (last {len(dur)} launches, after 5 warm-up ones) | value |
+|---|---|
+| average duration | {avg_us:.2f} us |
+| achieved | {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s) |
+| min / max | {min(dur):.2f} / {max(dur):.2f} us |
+
+A plain streaming kernel (torch's vectorized elementwise kernel, 8-element vectors, normal loads
+and stores) on this box: a reference point for the prologue kernels, which stream with
+non-temporal loads and stores.
 
 | counter | per launch (median of {len(f['FETCH_SIZE'])}) | true | scale applied to kernel counters |
 |---|---|---|---|

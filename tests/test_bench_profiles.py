@@ -59,10 +59,24 @@ def test_copy_calibration_summary(root):
     pmc(out, "rdreq", "copy", k, {"TCC_EA0_RDREQ_sum": 8388608 + 100, "TCC_EA0_RDREQ_128B_sum":
                                   8388608, "TCC_EA0_RDREQ_64B_sum": 100,
                                   "TCC_EA0_RDREQ_32B_sum": 0})
+    # kernel trace: 5 warm-up copies of 500 us, then 20 timed ones of 400 and 420 us alternating
+    rows, t = [], 0
+    for d in [500.0] * 5 + [400.0, 420.0] * 10:
+        rows.append({"Kernel_Name": k + "(x)", "Start_Timestamp": t, "End_Timestamp": t + int(d * 1000)})
+        rows.append({"Kernel_Name": "__amd_rocclr_fillBuffer", "Start_Timestamp": t + 1,
+                     "End_Timestamp": t + 2})
+        t += int(d * 1000) + 500
+    write_csv(os.path.join(out, "trace_copy", "y", "trace_kernel_trace.csv"), TRACE_COLS, rows)
     path = bench.summarize_copy(out, bench.profile_commands("copy", out))
     text = open(path).read()
     assert bench._record(path, "calibration") == {"fetch_factor": 2.0, "write_factor": 1.0}
     assert "| 8388708 | 8388608 | 100 | 0 | 1,073,748,224 | 1,073,741,824 | 1.00001 |" in text
+    # 2 GiB per copy at the timed launches' 410 us average
+    gbs = 2 * 2 ** 30 / 410e-6 / 1e9
+    assert f"| average duration | 410.00 us |" in text
+    assert f"| achieved | {gbs:.0f} GB/s ({100 * gbs / 8000:.1f}% of 8 TB/s) |" in text
+    assert "| min / max | 400.00 / 420.00 us |" in text
+    assert "--kernel-trace" in text and "--copy-calibration --steps 20 --warmup 5" in text
     assert "bench.py --copy-calibration" in text and str(root) not in text
 
 
