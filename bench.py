@@ -170,7 +170,9 @@ def make_launcher(w, dev, sets):
         B, N, H, D = w.batch, w.num_tokens, w.num_heads, w.head_dim
         for _ in range(sets):
             g = {k: v.to(dev) for k, v in cpu.items()}
-            outs = [torch.empty((B, H, D, N), dtype=g["q"].dtype, device=dev) for _ in range(3)]
+            # rows of w.out_pitch elements, of which the op writes the first N
+            outs = [torch.empty((B, H, D, w.out_pitch), dtype=g["q"].dtype, device=dev)[..., :N]
+                    for _ in range(3)]
             infl = torch.empty((B, H, N), dtype=torch.float32, device=dev)
             calls.append(qr.PreparedCam(g["q"], g["k"], g["v"], g["proj_q"], g["proj_kv"],
                                         g["rope_cos"], g["rope_sin"], w.k_scale, *outs, infl))

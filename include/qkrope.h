@@ -278,12 +278,19 @@ int qkrope_run_3d_sharded(qkrope_handle h,
  *                  aligned.
  *   rope_cos, rope_sin  device float32 [num_tokens, head_dim/2], 16-byte aligned.
  *   k_scale        multiplies K (the page's head_dim^-1/2 * spatial_tokens^-1/2).
- *   q_out, k_out, v_out  device, [batch, num_heads, head_dim, num_tokens] in act_dtype,
- *                  contiguous, 2-byte aligned (16-byte aligned with num_tokens % 8 == 0 takes
- *                  the fast store path).
+ *   q_out, k_out, v_out  device, [batch, num_heads, head_dim, num_tokens] in act_dtype, 2-byte
+ *                  aligned; row (b, h, d) of each starts at ((b*num_heads + h)*head_dim + d) *
+ *                  out_row_stride elements and holds the num_tokens values; elements between
+ *                  num_tokens and out_row_stride are not written.
+ *   out_row_stride elements between consecutive output rows, >= num_tokens and < 2^31
+ *                  (num_tokens: contiguous outputs). With 16-byte aligned outputs and a stride
+ *                  that is a multiple of 8, whole 64-token tiles take 16-byte stores; a stride
+ *                  that is a multiple of 64 (with 128-byte aligned outputs) starts every row on
+ *                  a 128-byte line, which these stores write fastest.
  *   inflation_sq   device float32 [batch, num_heads, num_tokens], contiguous, or NULL to skip.
- * No output may overlap an input or another output. head_dim must be a multiple of 4
- * (QKROPE_ERR_INVALID otherwise); this library handles multiples of 8 up to 256,
+ * No output may overlap an input or another output (their whole row spans, padding included).
+ * head_dim must be a multiple of 4 and out_row_stride >= num_tokens (QKROPE_ERR_INVALID
+ * otherwise); this library handles multiples of 8 up to 256,
  * batch * num_tokens < 2^31, and grids of at most 2^32 - 1 lanes (one launch; first exceeded
  * with a single head of 64 past 2^29 (b, n) tokens) (QKROPE_ERR_UNSUPPORTED). An empty problem
  * (batch, num_tokens or num_heads 0) is a no-op.
@@ -293,7 +300,7 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
                     const float *rope_sin, float k_scale, int64_t batch, int64_t num_tokens,
                     int num_heads, int head_dim, int64_t q_stride, int64_t k_stride,
                     int64_t v_stride, void *q_out, void *k_out, void *v_out,
-                    float *inflation_sq, void *stream);
+                    int64_t out_row_stride, float *inflation_sq, void *stream);
 
 #ifdef __cplusplus
 }

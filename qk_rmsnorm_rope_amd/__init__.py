@@ -85,7 +85,7 @@ def lib() -> ctypes.CDLL:
                                             P, P, P, P]
         L.qkrope_run_3d_sharded.restype = I
         L.qkrope_cam_prep.argtypes = [P, P, P, P, I, P, P, P, P, ctypes.c_float, I64, I64, I, I,
-                                      I64, I64, I64, P, P, P, P, P]
+                                      I64, I64, I64, P, P, P, I64, P, P]
         L.qkrope_cam_prep.restype = I
         runtimes = _hip_runtimes_loaded()
         if len(runtimes) > 1:
@@ -616,12 +616,29 @@ def _cam_rows(t: torch.Tensor, shape, name: str) -> int:
     return st
 
 
+def _cam_out_rows(t: torch.Tensor, shape, name: str) -> int:
+    """Row pitch of a [B, H, D, N] output view whose (b, h, d) rows are evenly spaced (contiguous,
+    or the [..., :N] slice of padded rows): the out_row_stride the C ABI takes."""
+    B, H, D, N = shape
+    if t.dim() != 4 or tuple(t.shape) != (B, H, D, N):
+        raise ValueError(f"{name} must be [batch, heads, head_dim, tokens] = {(B, H, D, N)}")
+    if t.numel() == 0:
+        return N                # nothing is written; torch's strides of an empty view vary
+    rp = t.stride(2) if D > 1 else (t.stride(1) if H > 1 else (t.stride(0) if B > 1 else N))
+    if ((N > 1 and t.stride(3) != 1) or rp < N or (H > 1 and t.stride(1) != D * rp) or
+            (B > 1 and t.stride(0) != H * D * rp)):
+        raise ValueError(f"{name} must have contiguous tokens and evenly spaced rows of at "
+                         "least tokens elements (contiguous, or a slice of padded rows)")
+    return rp
+
+
 def qkrope_cam_prep(q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, *, q_out, k_out,
                     v_out, inflation_sq=None, stream=None) -> None:
     """Camera prologue into caller-provided outputs: q, k, v [B, N, H, D] (bf16 or float16),
     proj_q / proj_kv float32 [B, N, 4, 4], rope_cos / rope_sin float32 [N, D/2]; q_out, k_out,
-    v_out contiguous [B, H, D, N] of the activation dtype; inflation_sq contiguous float32
-    [B, H, N] or None."""
+    v_out [B, H, D, N] of the activation dtype, contiguous or with one common row pitch (the
+    [..., :N] slice of padded rows; a pitch that is a multiple of 64 starts every row on a
+    128-byte line); inflation_sq contiguous float32 [B, H, N] or None."""
     if q.dim() != 4:
         raise ValueError("q must be [batch, tokens, heads, head_dim]")
     shape = tuple(q.shape)
@@ -634,10 +651,13 @@ def qkrope_cam_prep(q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, *, q_
                        (rope_cos, "rope_cos", (N, D // 2)), (rope_sin, "rope_sin", (N, D // 2))):
         if t.dtype != torch.float32 or tuple(t.shape) != want or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous float32 tensor of shape {want}")
+    pitch = []
     for t, n in ((q_out, "q_out"), (k_out, "k_out"), (v_out, "v_out")):
-        if t.dtype != q.dtype or tuple(t.shape) != (B, H, D, N) or not t.is_contiguous():
-            raise ValueError(f"{n} must be a contiguous [batch, heads, head_dim, tokens] tensor "
-                             "of the activation dtype")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{n} must have the activation dtype")
+        pitch.append(_cam_out_rows(t, (B, H, D, N), n))
+    if len(set(pitch)) != 1:
+        raise ValueError("q_out, k_out and v_out must share one row pitch")
     _same_device(q.device, k=k, v=v, proj_q=proj_q, proj_kv=proj_kv, rope_cos=rope_cos,
                  rope_sin=rope_sin, q_out=q_out, k_out=k_out, v_out=v_out,
                  inflation_sq=inflation_sq)
@@ -648,7 +668,7 @@ def qkrope_cam_prep(q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, *, q_
     s = lib().qkrope_cam_prep(_handle_for(q.device), _ptr(q), _ptr(k), _ptr(v), act,
                               _ptr(proj_q), _ptr(proj_kv), _ptr(rope_cos), _ptr(rope_sin),
                               float(k_scale), B, N, H, D, strides[0], strides[1], strides[2],
-                              _ptr(q_out), _ptr(k_out), _ptr(v_out), _ptr(inflation_sq),
+                              _ptr(q_out), _ptr(k_out), _ptr(v_out), pitch[0], _ptr(inflation_sq),
                               _stream(q.device, stream))
     _check(s, "qkrope_cam_prep")
 
@@ -675,11 +695,12 @@ class PreparedCam:
                         k_out=k_out, v_out=v_out, inflation_sq=inflation_sq, stream=stream)
         B, N, H, D = q.shape
         st = [_cam_rows(t, tuple(q.shape), "x") for t in (q, k, v)]
+        pitch = _cam_out_rows(q_out, (B, H, D, N), "q_out")
         self._fn = lib().qkrope_cam_prep
         self._args = (_handle_for(q.device), _ptr(q), _ptr(k), _ptr(v), _ACT_CODES[q.dtype],
                       _ptr(proj_q), _ptr(proj_kv), _ptr(rope_cos), _ptr(rope_sin),
                       float(k_scale), B, N, H, D, st[0], st[1], st[2], _ptr(q_out), _ptr(k_out),
-                      _ptr(v_out), _ptr(inflation_sq), _stream(q.device, stream))
+                      _ptr(v_out), pitch, _ptr(inflation_sq), _stream(q.device, stream))
         self._keep = (q, k, v, proj_q, proj_kv, rope_cos, rope_sin, q_out, k_out, v_out,
                       inflation_sq)
 

@@ -21,7 +21,7 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
                     const float *rope_sin, float k_scale, int64_t batch, int64_t num_tokens,
                     int num_heads, int head_dim, int64_t q_stride, int64_t k_stride,
                     int64_t v_stride, void *q_out, void *k_out, void *v_out,
-                    float *inflation_sq, void *stream)
+                    int64_t out_row_stride, float *inflation_sq, void *stream)
 {
     if (!h) return fail(QKROPE_ERR_INVALID, "handle is NULL");
     const int64_t B = batch, N = num_tokens;
@@ -40,6 +40,8 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
         if (strides[r] % 8 || strides[r] >= (int64_t(1) << 24))
             return fail(QKROPE_ERR_UNSUPPORTED, "token strides must be multiples of 8 elements and < 2^24");
     }
+    if (out_row_stride < N) return fail(QKROPE_ERR_INVALID, "out_row_stride smaller than num_tokens");
+    if (out_row_stride >= (int64_t(1) << 31)) return fail(QKROPE_ERR_UNSUPPORTED, "out_row_stride must be < 2^31");
     if (B * N == 0 || H == 0) return ok();
     const void *ins[3] = {q, k, v};
     void *outs[3] = {q_out, k_out, v_out};
@@ -52,10 +54,10 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
     if (!aligned(proj_q, 16) || !aligned(proj_kv, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16))
         return fail(QKROPE_ERR_UNSUPPORTED, "projections and tables must be 16-byte aligned");
     if (inflation_sq && !aligned(inflation_sq, 4)) return fail(QKROPE_ERR_INVALID, "inflation_sq must be 4-byte aligned");
-    // outputs must not overlap an input or one another (bounding intervals)
-    const int64_t out_elems = B * H * (int64_t)D * N;
-    Range ro[4] = {span_of(q_out, 1, out_elems, out_elems, 2), span_of(k_out, 1, out_elems, out_elems, 2),
-                   span_of(v_out, 1, out_elems, out_elems, 2),
+    // outputs must not overlap an input or one another (row spans of B*H*D rows)
+    const int64_t out_rows = B * H * (int64_t)D;
+    Range ro[4] = {span_of(q_out, out_rows, out_row_stride, N, 2), span_of(k_out, out_rows, out_row_stride, N, 2),
+                   span_of(v_out, out_rows, out_row_stride, N, 2),
                    span_of(inflation_sq, inflation_sq ? 1 : 0, B * H * N, B * H * N, 4)};
     Range ri[7] = {span_of(q, B * N, q_stride, (int64_t)H * D, 2), span_of(k, B * N, k_stride, (int64_t)H * D, 2),
                    span_of(v, B * N, v_stride, (int64_t)H * D, 2), span_of(proj_q, 1, B * N * 16, B * N * 16, 4),
@@ -117,7 +119,8 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
     a.div_xcd = make_fast_div(a.xcd_group ? a.xcd_group : 1u);
     // LDS rows of a power-of-two chunk count, so the per-token chunk rotation is a mask
     a.row_chunks = next_pow2(C);
-    a.vec_store = (N % 8 == 0) && aligned(q_out, 16) && aligned(k_out, 16) && aligned(v_out, 16);
+    a.out_row_stride = out_row_stride;
+    a.vec_store = (out_row_stride % 8 == 0) && aligned(q_out, 16) && aligned(k_out, 16) && aligned(v_out, 16);
     a.k_scale = k_scale;
     const int lds_bytes = 2 * kCamTile * a.row_chunks * 16;
     DeviceGuard g(h->device);

@@ -22,7 +22,8 @@ struct CamArgs {
     const float *proj[2];           // proj_q, proj_kv: [B, N, 4, 4] row-major per token
     const float *cos_table;         // [N, D/2]
     const float *sin_table;
-    uint16_t *out[3];               // [B, H, D, N]
+    uint16_t *out[3];               // [B, H, D, N]: row (b, h, d) at ((b*H + h)*D + d)*out_row_stride
+    int64_t out_row_stride;         // elements, >= N
     float *inflation;               // [B, H, N], or null
     int64_t num_tokens;             // N
     int batch, heads, head_dim;
@@ -33,7 +34,7 @@ struct CamArgs {
     uint32_t xcd_group;             // as KernelArgs::xcd_group, over tile-fastest blocks
     FastDiv div_tiles, div_groups, div_xcd;   // n / tiles_padded, n / groups, n / xcd_group
     int row_chunks;                 // LDS tile row: 16-byte chunks, next power of two >= D/8
-    int vec_store;                  // outputs take 16-byte stores (N % 8 == 0, aligned bases)
+    int vec_store;                  // outputs take 16-byte stores (row stride % 8 == 0, aligned bases)
     float k_scale;
 };
 // cpl: 16-byte chunks per lane (1 for head_dim <= 64, else ceil(head_dim / 64), with 8 lanes per

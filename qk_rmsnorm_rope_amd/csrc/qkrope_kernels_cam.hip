@@ -29,6 +29,11 @@
 //     tile is double-buffered, one barrier per tensor;
 //   * K also sums the key's squared norms before and after the projection over the token's
 //     lanes with DPP, for inflation_sq.
+// Output rows are out_row_stride elements apart (>= N): with a pitch that is a multiple of 64
+// elements every row starts on a 128-byte line, and a tile's 128-byte run of a row fills one
+// line; otherwise the runs straddle two lines, which the L2 completes from the neighbouring
+// tiles (measured on MI355X: 2 x 18432 tokens, rows on lines, 62.1% of 8 TB/s against 57.6%
+// at 2 x 18480, rows at four phases; 2 x 18480 into rows padded to 18496, 60.5%).
 // Block order: token tiles fastest, so the workgroups that run together on one XCD write
 // adjacent runs of the same output rows (measured on MI355X: 20% faster than head groups
 // fastest); each (batch, head group) has its tiles padded to a multiple of 8 and XCD x takes
@@ -95,7 +100,7 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
 
     const int D = a.head_dim, C = D >> 3, H = a.heads;
     const int CP = a.row_chunks, RS = CP * 8;    // LDS row: CP chunks, RS 16-bit elements
-    const int64_t N = a.num_tokens;
+    const int64_t N = a.num_tokens, RP = a.out_row_stride;   // RP: output row pitch, elements
     const int64_t n0 = (int64_t)tile * kCamTile;
     const int nvalid = (int)(N - n0 < kCamTile ? N - n0 : kCamTile);
     const int nl = tid / LT, dl = tid % LT;
@@ -167,11 +172,11 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
         us[j] = uu & 7;
         ud[j] = uu >> 3;
         ldsr[j] = (uint32_t)((us[j] * 8 * RS + (((ud[j] >> 3) + us[j]) & (CP - 1)) * 8 + (ud[j] & 7)) * 2);
-        st_off[j] = (ud[j] * N + n0 + us[j] * 8) * 2;
+        st_off[j] = (ud[j] * RP + n0 + us[j] * 8) * 2;
     }
-    // whole tiles of a row-aligned output: 16-byte stores, issued after the loop (measured
-    // slightly faster than storing each tensor as it is gathered); partial tiles and unaligned
-    // rows store elements as they go
+    // whole tiles of outputs with 16-byte aligned rows: 16-byte stores, issued after the loop
+    // (measured slightly faster than storing each tensor as it is gathered); the last, partial
+    // tile stores as it goes, 16 bytes per whole segment, and unaligned rows store elements
     const bool fast = a.vec_store && nvalid == kCamTile;
     // buffered outputs cost 4 * MI * CPL registers; past two chunks per lane they would cut the
     // occupancy below two workgroups per CU, so those variants store as they go
@@ -225,7 +230,7 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
         __syncthreads();
 
         uint16_t *out = a.out[r];
-        uint8_t *plane = reinterpret_cast<uint8_t *>(out + ((int64_t)b * H + h) * D * N);
+        uint8_t *plane = reinterpret_cast<uint8_t *>(out + ((int64_t)b * H + h) * D * RP);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             if (!uv[j]) continue;
@@ -233,13 +238,16 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
             uint16_t e8[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) e8[k] = src[k * RS];
+            const uint4 w = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16,
+                                       e8[4] | (uint32_t)e8[5] << 16, e8[6] | (uint32_t)e8[7] << 16);
             if (fast) {
-                const uint4 w = make_uint4(e8[0] | (uint32_t)e8[1] << 16, e8[2] | (uint32_t)e8[3] << 16,
-                                           e8[4] | (uint32_t)e8[5] << 16, e8[6] | (uint32_t)e8[7] << 16);
                 if (kEndStores) o[i][j] = w;
                 else *reinterpret_cast<uint4 *>(plane + st_off[j]) = w;
+            } else if (a.vec_store && us[j] * 8 + 8 <= nvalid) {
+                // the last, partial tile: its whole 8-token segments still take 16-byte stores
+                *reinterpret_cast<uint4 *>(plane + st_off[j]) = w;
             } else {
-                uint16_t *dst = reinterpret_cast<uint16_t *>(plane) + ud[j] * N + n0 + us[j] * 8;
+                uint16_t *dst = reinterpret_cast<uint16_t *>(plane) + ud[j] * RP + n0 + us[j] * 8;
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
                     if (us[j] * 8 + k < nvalid) dst[k] = e8[k];
@@ -251,7 +259,7 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
         for (int i = 0; i < MI; ++i) {
             if (i >= iters) continue;
             const int r = i % 3, h = h0 + i / 3;
-            uint8_t *plane = reinterpret_cast<uint8_t *>(a.out[r] + ((int64_t)b * H + h) * D * N);
+            uint8_t *plane = reinterpret_cast<uint8_t *>(a.out[r] + ((int64_t)b * H + h) * D * RP);
 #pragma unroll
             for (int j = 0; j < CPL; ++j)
                 if (uv[j]) *reinterpret_cast<uint4 *>(plane + st_off[j]) = o[i][j];

@@ -135,10 +135,15 @@ class CamWorkload:
     seed: int
     act_dtype: str = "bf16"
     base: float = 10000.0
+    out_row_stride: int = 0     # elements between output rows (b, h, d); 0: num_tokens
 
     @property
     def num_tokens(self) -> int:
         return self.ppf * self.pph * self.ppw
+
+    @property
+    def out_pitch(self) -> int:
+        return self.out_row_stride or self.num_tokens
 
     @property
     def k_scale(self) -> float:
@@ -214,12 +219,18 @@ CAM_PREP_S18480 = CamWorkload(
 CAM_PREP_S18432 = CAM_PREP_S18480.with_(
     name="cam_prep_b2_s18432_h20_d64", ppf=16, pph=32, ppw=36, seed=SEED_BASE + 110)
 
+# The 2 x 18480-token camera prologue writing into padded output rows of 18496 elements (a
+# multiple of 64: every row starts on a 128-byte line), the layout a caller that can take a row
+# pitch would choose; the same inputs and outputs as cam_prep_b2_s18480_h20_d64.
+CAM_PREP_S18480_P18496 = CAM_PREP_S18480.with_(
+    name="cam_prep_b2_s18480_h20_d64_pitch18496", out_row_stride=18496)
+
 WORKLOADS = {w.name: w for w in (TABLE_HALFSPLIT_T256, TABLE_INTERLEAVED_T4096,
                                  ROPE3D_ACROSS_S15360, ROPE3D_NEOX_FP8_S18480,
                                  ROPE3D_YARN_S122880, TABLE_INTERLEAVED_T32768,
                                  TABLE_INTERLEAVED_T32768_F16, TABLE_INTERLEAVED_T32768_E4M3,
                                  ROPE3D_ACROSS_S15360_TP4, CAM_PREP_S18480,
-                                 CAM_PREP_S18432)}
+                                 CAM_PREP_S18432, CAM_PREP_S18480_P18496)}
 
 
 # --- drawing -----------------------------------------------------------------------------------

@@ -66,7 +66,7 @@ def test_new_entry_points_reject_null_handle(lib):
                                    None, None, None, None)
     assert rc == 1 and b"handle" in lib.qkrope_last_error()
     rc = lib.qkrope_cam_prep(None, None, None, None, 0, None, None, None, None, 1.0, 1, 1, 1, 64,
-                             64, 64, 64, None, None, None, None, None)
+                             64, 64, 64, None, None, None, 1, None, None)
     assert rc == 1 and b"handle" in lib.qkrope_last_error()
 
 

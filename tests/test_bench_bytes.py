@@ -36,6 +36,9 @@ EXPECTED = {
         36960 * (12 * 20 * 64 + 2 * 64) + 18480 * 2 * 32 * 4 + 36960 * 20 * 4,
     "cam_prep_b2_s18432_h20_d64":
         36864 * (12 * 20 * 64 + 2 * 64) + 18432 * 2 * 32 * 4 + 36864 * 20 * 4,
+    # padded output rows: the padding is neither read nor written
+    "cam_prep_b2_s18480_h20_d64_pitch18496":
+        36960 * (12 * 20 * 64 + 2 * 64) + 18480 * 2 * 32 * 4 + 36960 * 20 * 4,
 }
 
 

@@ -4,8 +4,8 @@ sana_wm.ucpe", cam_prep_func) against the fp64 oracle, through the C ABI.
 Shapes cover several 64-token tiles with a ragged tail, token counts that are and are not
 multiples of 8 (16-byte and element stores), one and two chunks per lane, chunk counts that
 do not fill a power-of-two lane group, uneven head groups, a single token, binary16, padded
-token strides, no inflation output, empty problems, argument errors, graph replay, and the
-full 2 x 18480-token SANA-WM shape on sampled tokens.
+token strides, padded output rows, no inflation output, empty problems, argument errors, graph
+replay, and the full-size SANA-WM shapes at every token.
 """
 from __future__ import annotations
 
@@ -33,10 +33,18 @@ def gpu_inputs(inp):
     return {k: v.to(DEV) for k, v in inp.items()}
 
 
-def run_gpu(g, k_scale, inflation=True):
+PAD_BITS = 0x7FA5       # a NaN pattern in both 16-bit formats, written into output padding
+
+
+def run_gpu(g, k_scale, inflation=True, pitch=None):
+    """Outputs [B, H, D, N]: contiguous, or the [..., :N] views of rows of `pitch` elements whose
+    padding holds PAD_BITS (run_gpu.rows keeps the whole padded buffers)."""
     B, N, H, D = g["q"].shape
-    outs = [torch.full((B, H, D, N), float("nan"), dtype=g["q"].dtype, device=DEV)
+    P = N if pitch is None else pitch
+    rows = [torch.full((B, H, D, P), PAD_BITS, dtype=torch.int16, device=DEV).view(g["q"].dtype)
             for _ in range(3)]
+    outs = [r[..., :N] for r in rows]
+    run_gpu.rows = rows
     infl = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV) \
         if inflation else None
     qr.qkrope_cam_prep(g["q"], g["k"], g["v"], g["proj_q"], g["proj_kv"], g["rope_cos"],
@@ -146,20 +154,49 @@ def test_cam_hand_case_on_gpu():
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("w", [wl.CAM_PREP_S18480, wl.CAM_PREP_S18432], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [wl.CAM_PREP_S18480, wl.CAM_PREP_S18432, wl.CAM_PREP_S18480_P18496],
+                         ids=lambda w: w.name)
 def test_cam_full_shape_every_token(w):
-    """The SANA-WM shapes as bench.py runs them (2 x 18480 tokens, 20 heads of 64; and 2 x 18432,
-    whose output rows start on 128-byte lines): every output of one launch against the oracle."""
+    """The SANA-WM shapes as bench.py runs them (2 x 18480 tokens, 20 heads of 64; 2 x 18432,
+    whose output rows start on 128-byte lines; and 2 x 18480 into rows padded to 18496): every
+    output of one launch against the oracle."""
     print(f"\ncam full shape {w.name}", flush=True)
     inp = wl.cam_inputs(w)
     g = gpu_inputs(inp)
-    outs, infl = run_gpu(g, w.k_scale)
+    outs, infl = run_gpu(g, w.k_scale, pitch=w.out_pitch)
     torch.cuda.synchronize()
     ref = oracle.cam_prep(inp["q"], inp["k"], inp["v"], inp["proj_q"], inp["proj_kv"],
                           inp["rope_cos"], inp["rope_sin"], w.k_scale)
     check(w.name, outs, infl, ref)
     assert all(torch.isfinite(o.float()).all().item() for o in outs)
     assert torch.isfinite(infl).all().item()
+
+
+@pytest.mark.parametrize("B,N,H,D,pitch", [
+    (2, 200, 3, 64, 256),     # pitch a multiple of 64: rows on 128-byte lines
+    (2, 200, 3, 64, 203),     # odd pitch: element stores
+    (1, 130, 2, 128, 136),    # N % 8 != 0, pitch % 8 == 0: 16-byte stores on whole tiles
+    (2, 150, 3, 64, 150),     # pitch == N: the contiguous layout
+])
+def test_cam_padded_output_rows(B, N, H, D, pitch):
+    """Outputs with a row pitch above num_tokens: the same bits as contiguous outputs, the oracle's
+    values, and the padding between N and the pitch untouched."""
+    w = workload(B, N, H, D, seed=41)
+    inp = wl.cam_inputs(w)
+    g = gpu_inputs(inp)
+    dense, infl = run_gpu(g, w.k_scale)
+    padded, infl_p = run_gpu(g, w.k_scale, pitch=pitch)
+    rows = run_gpu.rows
+    torch.cuda.synchronize()
+    for a, b in zip(dense, padded):
+        assert torch.equal(a.view(torch.int16), b.contiguous().view(torch.int16))
+    assert torch.equal(infl, infl_p)
+    for r in rows:
+        pad = r.view(torch.int16)[..., N:]
+        assert bool((pad == PAD_BITS).all()), "padding written"
+    ref = oracle.cam_prep(inp["q"], inp["k"], inp["v"], inp["proj_q"], inp["proj_kv"],
+                          inp["rope_cos"], inp["rope_sin"], w.k_scale)
+    check(w.name + f"_pitch{pitch}", [p.contiguous() for p in padded], infl_p, ref)
 
 
 def test_cam_strided_rows_no_inflation_and_repeatability():
@@ -207,13 +244,13 @@ def test_cam_argument_errors():
     infl = torch.zeros(B * H * N, dtype=torch.float32, device=DEV)
     s = 0
 
-    def call(D_, xs=None, q_out=None, act=qr.QKROPE_DTYPE_BF16, stride=H * (D + 8)):
+    def call(D_, xs=None, q_out=None, act=qr.QKROPE_DTYPE_BF16, stride=H * (D + 8), pitch=N):
         xp = x.data_ptr() if xs is None else xs
         return L.qkrope_cam_prep(h, xp, x.data_ptr(), x.data_ptr(), act, P.data_ptr(),
                                  P.data_ptr(), t.data_ptr(), t.data_ptr(), 1.0, B, N, H, D_,
                                  stride, stride, stride,
                                  o[0].data_ptr() if q_out is None else q_out,
-                                 o[1].data_ptr(), o[2].data_ptr(), infl.data_ptr(), s)
+                                 o[1].data_ptr(), o[2].data_ptr(), pitch, infl.data_ptr(), s)
 
     assert call(64) == qr.QKROPE_OK
     assert call(6) == qr.QKROPE_ERR_INVALID            # not a multiple of 4
@@ -224,6 +261,8 @@ def test_cam_argument_errors():
     assert call(64, stride=H * 64 - 8) == qr.QKROPE_ERR_INVALID          # rows too short
     assert call(64, q_out=x.data_ptr()) == qr.QKROPE_ERR_INVALID         # output over q
     assert call(64, q_out=o[1].data_ptr() + 64) == qr.QKROPE_ERR_INVALID  # outputs overlap
+    assert call(64, pitch=N - 1) == qr.QKROPE_ERR_INVALID                 # rows shorter than N
+    assert call(64, pitch=1 << 31) == qr.QKROPE_ERR_UNSUPPORTED
     torch.cuda.synchronize()
 
 

@@ -129,15 +129,17 @@ hipError_t qkrope::launch_cam(const CamArgs &a, int act, int cpl, int64_t blocks
                               hipStream_t)
 {
     std::printf("launch cam act=%d cpl=%d lanes=%d hpg=%d groups=%d tiles=%d tiles_padded=%d "
-                "xcd=%u blocks=%lld lds=%d row_chunks=%d vec=%d\n",
+                "xcd=%u blocks=%lld lds=%d row_chunks=%d vec=%d pitch=%lld\n",
                 act, cpl, a.lanes_per_token, a.heads_per_group, a.groups, a.tiles, a.tiles_padded,
-                a.xcd_group, (long long)blocks, lds_bytes, a.row_chunks, a.vec_store);
+                a.xcd_group, (long long)blocks, lds_bytes, a.row_chunks, a.vec_store,
+                (long long)a.out_row_stride);
     // qkrope_kernels_cam.hip: token rows of q, k, v; one 4x4 fp32 matrix per (b, n) each; table
-    // rows [N, D/2]; output planes [B, H, D, N]; inflation [B, H, N]
+    // rows [N, D/2]; output rows (b, h, d) of N values, out_row_stride apart; inflation [B, H, N]
     const long long BN = (long long)a.batch * a.num_tokens, D = a.head_dim, H = a.heads;
+    const long long rows = (long long)a.batch * H * D;
     for (int r = 0; r < 3; ++r) {
         need(a.in[r], ((BN - 1) * a.in_stride[r] + H * D) * 2, "cam load");
-        need(a.out[r], BN * H * D * 2, "cam store");
+        need(a.out[r], ((rows - 1) * a.out_row_stride + a.num_tokens) * 2, "cam store");
     }
     need(a.proj[0], BN * 64, "proj_q");
     need(a.proj[1], BN * 64, "proj_kv");
@@ -192,20 +194,21 @@ int main(int argc, char **argv)
         st = qkrope_sumsq_3d(h, at(0), T, (int)I(1), (int)I(2), (int)I(3), D, (float *)at(6),
                              nullptr);
     } else if (!std::strcmp(form, "cam")) {
-        // B N H D act
+        // B N H D act [out_row_stride, 0: N]
         const long long B = I(0), N = I(1);
         const int H = (int)I(2), D = (int)I(3);
-        const long long s = (long long)H * D;
+        const long long s = (long long)H * D, rp = I(5) ? I(5) : N;
+        const long long out_bytes = B * s > 0 ? ((B * s - 1) * (rp > N ? rp : N) + N) * 2 : 0;
         for (int i = 0; i < 3; ++i) reg(at(i), B * N * s * 2 - (i == 0 ? shrink : 0));
         reg(at(3), B * N * 64);
         reg(at(4), B * N * 64);
         reg(at(5), N * (D / 2) * 4);
         reg(at(6), N * (D / 2) * 4);
-        for (int i = 7; i < 10; ++i) reg(at(i), B * N * s * 2);
+        for (int i = 7; i < 10; ++i) reg(at(i), out_bytes);
         reg(at(10), B * H * N * 4);
         st = qkrope_cam_prep(h, at(0), at(1), at(2), (int)I(4), (const float *)at(3),
                              (const float *)at(4), (const float *)at(5), (const float *)at(6),
-                             0.5f, B, N, H, D, s, s, s, at(7), at(8), at(9), (float *)at(10),
+                             0.5f, B, N, H, D, s, s, s, at(7), at(8), at(9), rp, (float *)at(10),
                              nullptr);
     } else {
         // T Hq Hk D R interleaved norm_mode act out tdt q_stride eps out_scale q_shift_bytes
@@ -373,6 +376,9 @@ def test_camera_prologue_launch(driver):
     assert (l["cpl"], l["lanes"], l["hpg"], l["groups"]) == (1, 8, 2, 10)
     assert (l["tiles"], l["tiles_padded"], l["xcd"]) == (289, 296, 37)
     assert (l["blocks"], l["lds"], l["row_chunks"], l["vec"]) == (2 * 296 * 10, 16384, 8, 1)
+    # 288 tiles: eighths without padding
+    (l,), st = run(driver, "cam", 2, 18432, 20, 64, 0)
+    assert st == 0 and (l["tiles_padded"], l["xcd"], l["blocks"]) == (288, 36, 2 * 10 * 288)
     # head_dim 128: two chunks per lane, one head per group; odd heads split as evenly as can be
     (l,), st = run(driver, "cam", 1, 1000, 3, 128, 2)
     assert st == 0 and (l["cpl"], l["hpg"], l["groups"], l["row_chunks"]) == (2, 1, 3, 16)
@@ -384,6 +390,22 @@ def test_camera_prologue_launch(driver):
     # fewer than 8 tiles: plain block order
     (l,), st = run(driver, "cam", 3, 200, 4, 64, 0)
     assert st == 0 and (l["tiles"], l["tiles_padded"], l["xcd"]) == (4, 4, 0)
+    # padded output rows: the pitch reaches the kernel; 16-byte stores need a multiple of 8, and
+    # every store stays inside the B*H*D rows of N values (run() checks the ranges)
+    (l,), st = run(driver, "cam", 2, 18480, 20, 64, 0, 18496)
+    assert st == 0 and (l["pitch"], l["vec"]) == (18496, 1)
+    (l,), st = run(driver, "cam", 2, 200, 3, 64, 0, 203)
+    assert st == 0 and (l["pitch"], l["vec"]) == (203, 0)
+    (l,), st = run(driver, "cam", 1, 301, 2, 40, 0, 304)
+    assert st == 0 and (l["pitch"], l["vec"]) == (304, 1)     # N % 8 != 0, rows still aligned
+
+
+@pytest.mark.parametrize("pitch,status", [(199, 1), (1, 1), (1 << 31, 2), (200, 0), (256, 0)])
+def test_camera_prologue_row_pitch_rules(driver, pitch, status):
+    """out_row_stride: below num_tokens is invalid, 2^31 and past unsupported; nothing launches
+    unless the call is accepted."""
+    ls, st = run(driver, "cam", 2, 200, 3, 64, 0, pitch)
+    assert st == status and len(ls) == (1 if status == 0 else 0)
 
 
 def test_camera_prologue_grid_limit(driver):
