@@ -172,16 +172,18 @@ def test_cam_full_shape_every_token(w):
     assert torch.isfinite(infl).all().item()
 
 
-@pytest.mark.parametrize("B,N,H,D,pitch", [
-    (2, 200, 3, 64, 256),     # pitch a multiple of 64: rows on 128-byte lines
-    (2, 200, 3, 64, 203),     # odd pitch: element stores
-    (1, 130, 2, 128, 136),    # N % 8 != 0, pitch % 8 == 0: 16-byte stores on whole tiles
-    (2, 150, 3, 64, 150),     # pitch == N: the contiguous layout
+@pytest.mark.parametrize("B,N,H,D,pitch,act", [
+    (2, 200, 3, 64, 256, "bf16"),     # pitch a multiple of 64: rows on 128-byte lines
+    (2, 200, 3, 64, 203, "bf16"),     # odd pitch: element stores
+    (1, 130, 2, 128, 136, "bf16"),    # N % 8 != 0, pitch % 8 == 0: 16-byte stores on whole tiles
+    (2, 150, 3, 64, 150, "bf16"),     # pitch == N: the contiguous layout
+    (1, 100, 2, 256, 128, "bf16"),    # four chunks per lane: stores as each tensor is gathered
+    (2, 136, 4, 64, 192, "f16"),      # binary16 activations and outputs
 ])
-def test_cam_padded_output_rows(B, N, H, D, pitch):
+def test_cam_padded_output_rows(B, N, H, D, pitch, act):
     """Outputs with a row pitch above num_tokens: the same bits as contiguous outputs, the oracle's
     values, and the padding between N and the pitch untouched."""
-    w = workload(B, N, H, D, seed=41)
+    w = workload(B, N, H, D, act=act, seed=41)
     inp = wl.cam_inputs(w)
     g = gpu_inputs(inp)
     dense, infl = run_gpu(g, w.k_scale)
