@@ -35,6 +35,7 @@ struct CamArgs {
     FastDiv div_tiles, div_groups, div_xcd;   // n / tiles_padded, n / groups, n / xcd_group
     int row_chunks;                 // LDS tile row: 16-byte chunks, next power of two >= D/8
     int vec_store;                  // outputs take 16-byte stores (row stride % 8 == 0, aligned bases)
+    int nt_store;                   // every output row starts on a 128-byte line: whole tiles store non-temporally
     float k_scale;
 };
 // cpl: 16-byte chunks per lane (1 for head_dim <= 64, else ceil(head_dim / 64), with 8 lanes per

@@ -30,10 +30,11 @@
 //   * K also sums the key's squared norms before and after the projection over the token's
 //     lanes with DPP, for inflation_sq.
 // Output rows are out_row_stride elements apart (>= N): with a pitch that is a multiple of 64
-// elements every row starts on a 128-byte line, and a tile's 128-byte run of a row fills one
-// line; otherwise the runs straddle two lines, which the L2 completes from the neighbouring
-// tiles (measured on MI355X: 2 x 18432 tokens, rows on lines, 62.1% of 8 TB/s against 57.6%
-// at 2 x 18480, rows at four phases; 2 x 18480 into rows padded to 18496, 60.5%).
+// elements every row starts on a 128-byte line, a tile's 128-byte run of a row fills one line,
+// and the whole tiles store non-temporally; otherwise the runs straddle two lines, which the L2
+// completes from the neighbouring tiles, so the stores stay normal (measured on MI355X: 2 x
+// 18432 tokens, rows on lines, 65.9% of 8 TB/s; 2 x 18480 into rows padded to 18496, 64.8%;
+// 2 x 18480 contiguous, rows at four phases, 57%).
 // Block order: token tiles fastest, so the workgroups that run together on one XCD write
 // adjacent runs of the same output rows (measured on MI355X: 20% faster than head groups
 // fastest); each (batch, head group) has its tiles padded to a multiple of 8 and XCD x takes
@@ -261,8 +262,16 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
             const int r = i % 3, h = h0 + i / 3;
             uint8_t *plane = reinterpret_cast<uint8_t *>(a.out[r] + ((int64_t)b * H + h) * D * RP);
 #pragma unroll
-            for (int j = 0; j < CPL; ++j)
-                if (uv[j]) *reinterpret_cast<uint4 *>(plane + st_off[j]) = o[i][j];
+            for (int j = 0; j < CPL; ++j) {
+                if (!uv[j]) continue;
+                if (a.nt_store) {           // uniform: every row starts on a line
+                    const uint4 ov = o[i][j];
+                    const u32x4 w4 = {ov.x, ov.y, ov.z, ov.w};
+                    __builtin_nontemporal_store(w4, reinterpret_cast<u32x4 *>(plane + st_off[j]));
+                } else {
+                    *reinterpret_cast<uint4 *>(plane + st_off[j]) = o[i][j];
+                }
+            }
         }
     }
 }
