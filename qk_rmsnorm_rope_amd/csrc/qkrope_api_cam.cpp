@@ -124,7 +124,7 @@ int qkrope_cam_prep(qkrope_handle h, const void *q, const void *k, const void *v
     // Rows that all start on a 128-byte line (a pitch that is a multiple of 64 elements, bases on
     // lines): each tile's run of a row is one whole line, written by one store instruction, and
     // non-temporal stores are faster (measured on MI355X, 2 x 18480 x 20 x 64 into rows of 18496:
-    // 120.2 -> 111.9 us; 2 x 18432 contiguous: 117.2 -> 109.8 us). Rows at other phases keep
+    // 119.8 -> 113.8 us; 2 x 18432 contiguous: 116.4 -> 111.8 us). Rows at other phases keep
     // normal stores: the L2 completes the lines that their runs split between neighbouring tiles,
     // and non-temporal stores there ran 39% slower.
     a.nt_store = a.vec_store && out_row_stride % 64 == 0 && aligned(q_out, 128) && aligned(k_out, 128) &&

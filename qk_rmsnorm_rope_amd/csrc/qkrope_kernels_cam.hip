@@ -33,8 +33,8 @@
 // elements every row starts on a 128-byte line, a tile's 128-byte run of a row fills one line,
 // and the whole tiles store non-temporally; otherwise the runs straddle two lines, which the L2
 // completes from the neighbouring tiles, so the stores stay normal (measured on MI355X: 2 x
-// 18432 tokens, rows on lines, 65.9% of 8 TB/s; 2 x 18480 into rows padded to 18496, 64.8%;
-// 2 x 18480 contiguous, rows at four phases, 57%).
+// 18432 tokens, rows on lines, 64.7% of 8 TB/s; 2 x 18480 into rows padded to 18496, 63.7%;
+// 2 x 18480 contiguous, rows at four phases, 57.3%).
 // Block order: token tiles fastest, so the workgroups that run together on one XCD write
 // adjacent runs of the same output rows (measured on MI355X: 20% faster than head groups
 // fastest); each (batch, head group) has its tiles padded to a multiple of 8 and XCD x takes
