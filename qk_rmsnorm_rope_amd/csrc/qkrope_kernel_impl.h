@@ -184,18 +184,41 @@ __device__ __forceinline__ uint4 ld16_stream(const void *base, uint32_t byte_off
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Streamed 16- and 8-byte stores at a (usually uniform) base plus a 32-bit byte offset, like
-// the loads: the saddr+voffset form, with no 64-bit address arithmetic per lane.
+// Streamed 16- and 8-byte stores at a base plus a 32-bit byte offset, like the loads: no 64-bit
+// address arithmetic per lane. With a uniform base (UNI) the store goes through a buffer
+// resource spanning the 4 GiB above the base, whose instruction takes device scope (sc1) besides
+// the non-temporal hint, so each XCD's L2 passes the written lines on to memory at once instead
+// of holding them dirty. Measured on MI355X: a plain 16-byte copy of 3 GB runs at 79-81% of
+// 8 TB/s so, against 77% with the non-temporal hint alone; the 122880-token YaRN workload went
+// from 948 to 928 us per launch, the others moved by less than 1%. (The same policy on the
+// camera prologue's line-aligned rows was 1.3% slower; it keeps its own stores.) A per-lane base
+// (the mixed slot layout) keeps the global form, which carries the non-temporal hint only.
+constexpr int kStorePolicy = 2 | 16;        // nt | sc1 in the buffer instruction's aux field
+constexpr int kBufferFlags = 0x00020000;    // raw (untyped) buffer: word 3 of the resource
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(void *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, -1, kBufferFlags);
+}
+
+template <bool UNI>
 __device__ __forceinline__ void st16_stream(void *base, uint32_t byte_off, uint4 v)
 {
     const u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(static_cast<uint8_t *>(base) + byte_off));
+    if (UNI)
+        __builtin_amdgcn_raw_buffer_store_b128(w, stream_rsrc(base), (int)byte_off, 0, kStorePolicy);
+    else
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(static_cast<uint8_t *>(base) + byte_off));
 }
 
+template <bool UNI>
 __device__ __forceinline__ void st8_stream(void *base, uint32_t byte_off, uint2 v)
 {
     const u32x2 w = {v.x, v.y};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(base) + byte_off));
+    if (UNI)
+        __builtin_amdgcn_raw_buffer_store_b64(w, stream_rsrc(base), (int)byte_off, 0, kStorePolicy);
+    else
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(base) + byte_off));
 }
 
 // n / d for n < 2^31 with a host-computed magic pair (m, l): q = (mulhi(n, m) + n) >> l.
@@ -791,8 +814,9 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             const int r = reg[j] < 3 ? reg[j] : 0;
             const uint32_t in_row = (hoff[j] + off0) * ESIZE;
             const uint32_t off = TPW == 2 ? __umul24(ts_st, (uint32_t)(a.out_stride[r] * ESIZE)) + in_row : in_row;
-            if (FP8) st8_stream(sel3(reg[j], out_q, out_k, out_v), off, make_uint2(pk[j].x, pk[j].y));
-            else st16_stream(sel3(reg[j], out_q, out_k, out_v), off, pk[j]);
+            // region-major slots: the region, so the base, is compile-time; mixed: per lane
+            if (FP8) st8_stream<SU>(sel3(reg[j], out_q, out_k, out_v), off, make_uint2(pk[j].x, pk[j].y));
+            else st16_stream<SU>(sel3(reg[j], out_q, out_k, out_v), off, pk[j]);
         }
     }
 }
