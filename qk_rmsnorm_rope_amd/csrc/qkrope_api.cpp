@@ -139,11 +139,16 @@ bool split_regions(const LaunchShape &s, const KernelKey &k)
 // XCDs. Runs of 16 consecutive blocks per XCD, measured on MI355X (graph replay, G in
 // {0, 1, 4, 16, 32, 64, 256}): 122880 tokens x 3x16 x 256 (6 GB per launch) 73.5% -> 77.3% of
 // 8 TB/s, 15360 x 3x32 x 128 76.2% -> 77.2%, the 4096- and 32768-token tables +0.7-1.2 points,
-// the FP8 NeoX workload within noise; larger runs lose again. Grids under 128 blocks keep the
-// plain order (the remap leaves blocks past the last whole 8G run in place).
-uint32_t xcd_group_for(int64_t blocks)
+// the FP8 NeoX workload within noise; larger runs lose again. With the stores at device scope
+// the region-split launch (8 KB workgroups that only stream) gains from longer runs: 64 blocks
+// (512 KB of input per run) took the 122880-token workload from 945 to 934 us per launch, while
+// the 32768-token table lost 1% at 64 and 2.4% at 128 and the 15360-token and FP8 NeoX
+// workloads stayed within noise. Grids under 128 blocks keep the plain order (the remap leaves
+// blocks past the last whole 8G run in place).
+uint32_t xcd_group_for(int64_t blocks, bool split)
 {
-    return blocks >= 128 ? 16u : 0u;    // a power of two (the kernel shifts by its log)
+    if (blocks < 128) return 0u;
+    return split ? 64u : 16u;    // a power of two (the kernel shifts by its log)
 }
 
 hipError_t launch(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
@@ -208,7 +213,7 @@ int do_launch(qkrope_handle h, const KernelKey &key, const LaunchShape &shape,
         LaunchShape s = shape;
         KernelArgs a = n == T ? args : token_range(args, key, t0, n);
         s.blocks = (n + s.tpw - 1) / s.tpw * per_block;
-        a.xcd_group = xcd_group_for(s.blocks);
+        a.xcd_group = xcd_group_for(s.blocks, s.split);
         const hipError_t e = launch(key, s, a, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     }

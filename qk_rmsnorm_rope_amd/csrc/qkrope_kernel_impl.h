@@ -17,8 +17,9 @@
 //     per region of a token in the 3D form without norm, see RS). On MI355X the hardware's own
 //     workgroup scheduling hides memory latency better than a software-pipelined walk over
 //     several tokens per workgroup, which measured slower at every depth tried. Large grids
-//     deal runs of 16 consecutive token blocks to each XCD (KernelArgs::xcd_group); a call
-//     whose grid would exceed one dispatch runs as several launches over token ranges (host).
+//     deal runs of 16 consecutive token blocks (64 with the region split) to each XCD
+//     (KernelArgs::xcd_group); a call whose grid would exceed one dispatch runs as several
+//     launches over token ranges (host).
 //   * A token's Q, K (and V) rows are cut into units of one 16-byte chunk (8 bf16), so every
 //     load and store instruction of a wave covers whole contiguous cache lines. Interleaved
 //     pairs never leave a chunk. Half-split/NeoX pairs (d, d + R/2) join chunk c with chunk
@@ -273,6 +274,24 @@ __device__ __forceinline__ float group_sum(float v, int width)
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
 
+// Two sums through one tree. v_permlane16_swap exchanges the second 16-lane row of its first
+// operand with the first row of its second (and rows 3 and 2 likewise), so with (a, b) the first
+// row of each 32-lane group ends with a of lanes i and i + 16, the second with b of lanes i - 16
+// and i: the first row then carries a's pair sums, the second b's, for a 16-lane tree to finish.
+__device__ __forceinline__ float pair_rows_add(float a, float b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// The same swap with v in both operands gives every lane of a 32-lane group its first row's
+// value (.x) and its second row's (.y).
+__device__ __forceinline__ f32x2 rows_to_all(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return f32x2{__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+
 // Sum of squares of the 8 activations of a chunk, from the packed pairs (v_dot2c_f32_bf16 or
 // v_dot2_f32_f16: products of 16-bit values are exact in fp32, the sums are fp32).
 template <int ACT>
@@ -332,7 +351,8 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     constexpr int CSR = kMaxPairs / NPAIR + 1;  // row stride of a plane, f32x2
     constexpr int CSP = NPAIR * CSR;            // one plane
     __shared__ f32x2 s_cs[IS3D ? TPW * 2 * CSP : 1];
-    __shared__ f32x2 s_red[32];
+    __shared__ f32x2 s_red[32];                 // across-heads partials (Q, K) per wave or group
+    float *const s_redf = reinterpret_cast<float *>(s_red);
     // kPairHalfAny: one area of 64 lanes x 8 floats per wave (launched with threads * 32 bytes)
     extern __shared__ float s_xch[];
 
@@ -649,16 +669,14 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                 sq += reg[j] == kQ ? ss[j] : 0.0f;
                 sk += reg[j] == kK ? ss[j] : 0.0f;
             }
-            if (TPW == 1) {
-                sq = wave_sum(sq);
-                sk = wave_sum(sk);
-                if ((tid & 63) == 0) s_red[tid >> 6] = f32x2{sq, sk};
-            } else {
-                // per 32-lane group (each belongs to one token)
-                sq = group_sum(sq, 32);
-                sk = group_sum(sk, 32);
-                if ((tid & 31) == 0) s_red[tid >> 5] = f32x2{sq, sk};
-            }
+            // Q's and K's sums through one tree: after the row pairing the first row of each
+            // 32-lane group carries Q, the second K. Per 32-lane group with two tokens (each
+            // group belongs to one), per wave with one.
+            float v = group_sum(pair_rows_add(sq, sk), 16);
+            if (TPW == 1) v = swap32_add(v);
+            // lane 0 of the group (or wave) holds Q's sum, lane 16 K's: s_red[g] = (Q, K)
+            if ((tid & 15) == 0 && (TPW == 2 || (tid & 32) == 0))
+                s_redf[2 * (tid >> (TPW == 1 ? 6 : 5)) + ((tid >> 4) & 1)] = v;
         }
 
         if (NEED_BARRIER && !v_wg) __syncthreads();   // v_wg is uniform
@@ -672,22 +690,16 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             rq = __builtin_amdgcn_rsqf(p.x * a.inv_count[0] + a.eps);
             rk = __builtin_amdgcn_rsqf(p.y * a.inv_count[1] + a.eps);
         } else if (NORM == kNormAcross) {
-            // every wave sums its token's partials: one token, lane w of each 16-lane row reads
-            // wave w's; two tokens, lane w of each 32-lane group reads its token's group w
-            float sq, sk;
-            if (TPW == 1) {
-                const int w = tid & 15;
-                const f32x2 p = w < (nth >> 6) ? s_red[w] : f32x2{0.0f, 0.0f};
-                sq = group_sum(p.x, 16);
-                sk = group_sum(p.y, 16);
-            } else {
-                const int ng = LT >> 5, w = tid & 31;
-                const f32x2 p = w < ng ? s_red[ts * ng + w] : f32x2{0.0f, 0.0f};
-                sq = group_sum(p.x, 32);
-                sk = group_sum(p.y, 32);
-            }
-            rq = __builtin_amdgcn_rsqf(sq * a.inv_count[0] + a.eps);
-            rk = __builtin_amdgcn_rsqf(sk * a.inv_count[1] + a.eps);
+            // every wave sums its token's partials (its waves', or its 32-lane groups' with two
+            // tokens; at most 16 either way): lane w of a group's first row reads partial w's Q
+            // sum, of its second row the K sum; one 16-lane tree, then both to every lane
+            const int np = TPW == 1 ? (nth >> 6) : (LT >> 5);
+            const int g0 = TPW == 1 ? 0 : ts * np;
+            const int w = tid & 15;
+            const float p = w < np ? s_redf[2 * (g0 + w) + ((tid >> 4) & 1)] : 0.0f;
+            const f32x2 s = rows_to_all(group_sum(p, 16));
+            rq = __builtin_amdgcn_rsqf(s.x * a.inv_count[0] + a.eps);
+            rk = __builtin_amdgcn_rsqf(s.y * a.inv_count[1] + a.eps);
         }
         if (IS3D && unit_ok && !v_wg) {
             // interleaved and second-half lanes read (cos, sin), first-half lanes (cos, -sin);

@@ -298,11 +298,11 @@ def test_named_3d_workloads_get_their_tuned_shapes(driver):
     (l,), st = run_3d(driver, 36960, (20, 33, 28), (16, 24, 24), (20, 20, 20), 64, interleave=0,
                       fp8=1)
     assert st == 0 and (l["threads"], l["tpw"], l["split"], l["fp8"]) == (320, 2, 0, 1)
-    assert l["blocks"] == 36960 // 2
+    assert l["blocks"] == 36960 // 2 and l["xcd"] == 16
     # 122880 x 3x16 x 256, no norm: one region of one token per workgroup (three per token)
     (l,), st = run_3d(driver, 122880, (32, 48, 80), (64, 96, 96), (16, 16, 16), 256, norm=0)
     assert st == 0 and (l["threads"], l["split"], l["norm"]) == (512, 1, 0)
-    assert l["blocks"] == 3 * 122880
+    assert l["blocks"] == 3 * 122880 and l["xcd"] == 64
 
 
 @pytest.mark.parametrize("norm,fp8,heads", [(1, 0, (16, 16, 16)), (0, 1, (16, 16, 16)),
