@@ -151,6 +151,19 @@ uint32_t xcd_group_for(int64_t blocks, bool split)
     return split ? 64u : 16u;    // a power of two (the kernel shifts by its log)
 }
 
+// Store scope of a launch (KernelArgs::store_device): device scope once it writes at least
+// 128 MiB. Measured on MI355X (graph replay, A/B on one box, against non-temporal stores only):
+// the 122880-token YaRN workload (3 GB written) 2% faster, the 32768-token tables (403 MB)
+// 0.4-1%, the 15360-token across-heads (377 MB) and FP8 NeoX (142 MB) workloads within noise;
+// the 4-way head-sharded rank (94 MB) 4% slower and the 4096-token table (50 MB) 2-3% slower.
+constexpr int64_t kStoreDeviceBytes = int64_t(1) << 27;
+
+uint32_t store_device_for(const KernelKey &k, const KernelArgs &a)
+{
+    const int64_t elems = int64_t(a.heads[0] + a.heads[1] + a.heads[2]) * a.head_dim;
+    return a.num_tokens * elems * (k.fp8 ? 1 : 2) >= kStoreDeviceBytes ? 1u : 0u;
+}
+
 hipError_t launch(const KernelKey &k, const LaunchShape &s, const KernelArgs &a, hipStream_t st)
 {
     if (k.src == kSrc3D) {
@@ -214,6 +227,7 @@ int do_launch(qkrope_handle h, const KernelKey &key, const LaunchShape &shape,
         KernelArgs a = n == T ? args : token_range(args, key, t0, n);
         s.blocks = (n + s.tpw - 1) / s.tpw * per_block;
         a.xcd_group = xcd_group_for(s.blocks, s.split);
+        a.store_device = store_device_for(key, a);
         const hipError_t e = launch(key, s, a, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     }

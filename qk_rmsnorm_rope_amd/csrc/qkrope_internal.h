@@ -45,6 +45,7 @@ struct KernelArgs {
 
     int64_t num_tokens;        // tokens; the grid has one workgroup per token (per 2 with TPW 2)
     uint32_t xcd_group;        // 0: block b takes token block b; G > 0 (a power of two): XCD runs
+    uint32_t store_device;     // 1: streamed stores at device scope (large launches), 0: nt only
     int head_dim;              // D
     int rotary_dim;            // R (== D for the 3D form)
     int lanes_per_head;        // L: power of two >= head_dim / 8 (16-byte chunks per head)

@@ -186,15 +186,17 @@ __device__ __forceinline__ uint4 ld16_stream(const void *base, uint32_t byte_off
 }
 
 // Streamed 16- and 8-byte stores at a base plus a 32-bit byte offset, like the loads: no 64-bit
-// address arithmetic per lane. With a uniform base (UNI) the store goes through a buffer
-// resource spanning the 4 GiB above the base, whose instruction takes device scope (sc1) besides
-// the non-temporal hint, so each XCD's L2 passes the written lines on to memory at once instead
-// of holding them dirty. Measured on MI355X: a plain 16-byte copy of 3 GB runs at 79-81% of
-// 8 TB/s so, against 77% with the non-temporal hint alone; the 122880-token YaRN workload went
-// from 948 to 928 us per launch, the others moved by less than 1%. (The same policy on the
-// camera prologue's line-aligned rows was 1.3% slower; it keeps its own stores.) A per-lane base
-// (the mixed slot layout) keeps the global form, which carries the non-temporal hint only.
-constexpr int kStorePolicy = 2 | 16;        // nt | sc1 in the buffer instruction's aux field
+// address arithmetic per lane; all carry the non-temporal hint. Large launches (DEV, a uniform
+// flag the host sets from the bytes a launch writes) with a uniform base (UNI) store through a
+// buffer resource spanning the 4 GiB above the base instead, whose instruction also takes
+// device scope (sc1), so each XCD's L2 passes the written lines on to memory at once instead of
+// holding them dirty. Measured on MI355X: a plain 16-byte copy of 3 GB runs at 79-81% of
+// 8 TB/s with device scope against 77% without; the 122880-token YaRN workload went from 955 to
+// 934 us per launch and the 32768-token tables gained 0.4-1%, but launches writing under 100 MB
+// lost (the 4-way head-sharded rank's apply kernel 31.1 -> 32.4 us, the 4096-token table
+// 19.55 -> 19.9 us): there the lines a write-back L2 would hold past the kernel's end are
+// written inside it. A per-lane base (the mixed slot layout) always takes the global form.
+constexpr int kStoreNTDevice = 2 | 16;      // nt | sc1 in the buffer instruction's aux field
 constexpr int kBufferFlags = 0x00020000;    // raw (untyped) buffer: word 3 of the resource
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(void *base)
@@ -203,21 +205,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(void *base)
 }
 
 template <bool UNI>
-__device__ __forceinline__ void st16_stream(void *base, uint32_t byte_off, uint4 v)
+__device__ __forceinline__ void st16_stream(void *base, uint32_t byte_off, uint4 v, bool dev)
 {
     const u32x4 w = {v.x, v.y, v.z, v.w};
-    if (UNI)
-        __builtin_amdgcn_raw_buffer_store_b128(w, stream_rsrc(base), (int)byte_off, 0, kStorePolicy);
+    if (UNI && dev)
+        __builtin_amdgcn_raw_buffer_store_b128(w, stream_rsrc(base), (int)byte_off, 0, kStoreNTDevice);
     else
         __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(static_cast<uint8_t *>(base) + byte_off));
 }
 
 template <bool UNI>
-__device__ __forceinline__ void st8_stream(void *base, uint32_t byte_off, uint2 v)
+__device__ __forceinline__ void st8_stream(void *base, uint32_t byte_off, uint2 v, bool dev)
 {
     const u32x2 w = {v.x, v.y};
-    if (UNI)
-        __builtin_amdgcn_raw_buffer_store_b64(w, stream_rsrc(base), (int)byte_off, 0, kStorePolicy);
+    if (UNI && dev)
+        __builtin_amdgcn_raw_buffer_store_b64(w, stream_rsrc(base), (int)byte_off, 0, kStoreNTDevice);
     else
         __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(base) + byte_off));
 }
@@ -827,8 +829,8 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
             const uint32_t in_row = (hoff[j] + off0) * ESIZE;
             const uint32_t off = TPW == 2 ? __umul24(ts_st, (uint32_t)(a.out_stride[r] * ESIZE)) + in_row : in_row;
             // region-major slots: the region, so the base, is compile-time; mixed: per lane
-            if (FP8) st8_stream<SU>(sel3(reg[j], out_q, out_k, out_v), off, make_uint2(pk[j].x, pk[j].y));
-            else st16_stream<SU>(sel3(reg[j], out_q, out_k, out_v), off, pk[j]);
+            if (FP8) st8_stream<SU>(sel3(reg[j], out_q, out_k, out_v), off, make_uint2(pk[j].x, pk[j].y), a.store_device);
+            else st16_stream<SU>(sel3(reg[j], out_q, out_k, out_v), off, pk[j], a.store_device);
         }
     }
 }

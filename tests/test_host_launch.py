@@ -101,11 +101,12 @@ static hipError_t rec(const char *kind, const qkrope::KernelKey &k, const qkrope
                       const qkrope::KernelArgs &a)
 {
     std::printf("launch %s threads=%d slots=%d su=%d tpw=%d split=%d blocks=%lld tpl=%d "
-                "pairing=%d norm=%d fp8=%d ntok=%lld toff=%u in0=%llu xcd=%u\n",
+                "pairing=%d norm=%d fp8=%d ntok=%lld toff=%u in0=%llu xcd=%u dev=%u\n",
                 kind, s.threads, s.slots, (int)s.slot_uniform, s.tpw, (int)s.split,
                 (long long)s.blocks, k.head_dim_tpl, k.pairing, k.norm, (int)k.fp8,
                 (long long)a.num_tokens, a.token_offset,
-                (unsigned long long)(reinterpret_cast<uintptr_t>(a.in[0]) - g_base), a.xcd_group);
+                (unsigned long long)(reinterpret_cast<uintptr_t>(a.in[0]) - g_base), a.xcd_group,
+                a.store_device);
     check_prologue(k, a);
     return hipSuccess;
 }
@@ -311,6 +312,27 @@ def test_region_split_only_without_norm_for_16_bit_outputs_and_wide_rows(driver,
                                                                          heads):
     (l,), st = run_3d(driver, 1536, (4, 4, 96), (64, 96, 96), heads, 256, norm=norm, fp8=fp8)
     assert st == 0 and l["split"] == 0 and l["blocks"] == 1536 // l["tpw"]
+
+
+def test_store_scope_follows_the_bytes_a_launch_writes(driver):
+    # device-scope stores once a launch writes at least 2^27 bytes
+    cases_3d = [((32, 32, 32), 128, 15360, 0, 1),     # 15360 x 3x32 x 128: 377 MB
+                ((8, 8, 8), 128, 15360, 0, 0),        # one rank of 4 head shards: 94 MB
+                ((20, 20, 20), 64, 36960, 1, 1)]      # 2 x 18480 x 3x20 x 64, E4M3: 142 MB
+    for heads, D, T, fp8, dev in cases_3d:
+        grid = (20, 33, 28) if T == 36960 else (16, 24, 40)
+        ch = (16, 24, 24) if D == 64 else (16, 56, 56)
+        (l,), st = run_3d(driver, T, grid, ch, heads, D, interleave=1 - fp8, fp8=fp8)
+        assert st == 0 and l["dev"] == dev, (heads, D, T)
+    for T, dev in [(4096, 0), (32768, 1)]:                  # 2x24 x 128 tables: 50 / 403 MB
+        (l,), st = run_table(driver, T, 24, 24, 128, 128, tdt=0)
+        assert st == 0 and l["dev"] == dev, T
+    # the threshold itself: 4096 bytes a token (2x8 x 128 bf16), 2^15 tokens write 2^27 bytes
+    for T, dev in [(32767, 0), (32768, 1)]:
+        (l,), st = run_table(driver, T, 8, 8, 128, 128, tdt=0)
+        assert st == 0 and l["dev"] == dev, T
+    (l,), st = run_table(driver, 2 * 32768, 8, 8, 128, 128, tdt=0, out=3)   # E4M3: a byte each
+    assert st == 0 and l["dev"] == 1 and l["fp8"] == 1
 
 
 def test_named_table_workloads_get_their_tuned_shapes(driver):
