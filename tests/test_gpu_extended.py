@@ -55,6 +55,55 @@ def split_views(tab, R, pad_c=8, pad_s=24):
     return cbuf[:, : R // 2], sbuf[:, : R // 2]
 
 
+# --- launches that write 2^27 bytes or more (stores at device scope through buffer resources) ---
+
+def _run_table_full(w, inp):
+    g = {k: _gpu(v) for k, v in inp.items()}
+    odt = torch.float8_e4m3fn if w.out_dtype == "e4m3" else g["q"].dtype
+    qo = torch.empty(g["q"].shape, dtype=odt, device=DEV)
+    ko = torch.empty(g["k"].shape, dtype=odt, device=DEV)
+    R = w.rotary_dim
+    qr.qkrope_run_table_ex(g["q"], g["k"], g["q_weight"], g["k_weight"],
+                           g["rope_table"][:, : R // 2], g["rope_table"][:, R // 2: R], w.eps,
+                           q_out=qo, k_out=ko, rotary_dim=R, interleaved=w.interleaved,
+                           norm_mode=w.norm_mode, out_scale=w.out_scale)
+    torch.cuda.synchronize()
+    return qo, ko
+
+
+def _check_table(w, qo, ko, rq, rk):
+    if w.out_dtype == "e4m3":
+        assert_e4m3_within_one(qo, oracle.e4m3_encode(rq, w.out_scale), f"{w.name} q")
+        assert_e4m3_within_one(ko, oracle.e4m3_encode(rk, w.out_scale), f"{w.name} k")
+    elif w.act_dtype == "f16":
+        assert_f16_close(qo, rq, f"{w.name} q")
+        assert_f16_close(ko, rk, f"{w.name} k")
+    else:
+        assert_bf16_close(qo, rq, f"{w.name} q")
+        assert_bf16_close(ko, rk, f"{w.name} k")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w", [wl.TABLE_INTERLEAVED_T32768, wl.TABLE_INTERLEAVED_T32768_F16,
+                               wl.TABLE_INTERLEAVED_T32768_E4M3], ids=lambda w: w.name)
+def test_table_workload_full_size_every_token(w):
+    """The 32768-token table workloads (403 MB, or 201 MB of E4M3 codes, written per launch:
+    16- and 8-byte stores at device scope), every output element against the oracle."""
+    inp = wl.table_inputs(w)
+    qo, ko = _run_table_full(w, inp)
+    _check_table(w, qo, ko, *oracle_table(w, inp))
+
+
+@pytest.mark.parametrize("T", [32767, 32768])
+def test_table_store_scope_threshold(T):
+    """2 x 8 heads x 128 bf16 write 4096 bytes a token: 32767 tokens keep the global
+    non-temporal stores, 32768 (2^27 bytes) store at device scope; both match the oracle."""
+    w = table_workload(T, 8, 8, 128, 128, True, "per_head", "bf16", "bf16", seed=4700)
+    inp = wl.table_inputs(w)
+    qo, ko = _run_table_full(w, inp)
+    _check_table(w, qo, ko, *oracle_table(w, inp))
+
+
 # --- float16 activations -----------------------------------------------------------------------
 
 F16_CASES = [
