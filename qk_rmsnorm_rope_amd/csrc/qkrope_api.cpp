@@ -227,6 +227,8 @@ int do_launch(qkrope_handle h, const KernelKey &key, const LaunchShape &shape,
         KernelArgs a = n == T ? args : token_range(args, key, t0, n);
         s.blocks = (n + s.tpw - 1) / s.tpw * per_block;
         a.xcd_group = xcd_group_for(s.blocks, s.split);
+        a.xcd_lg = a.xcd_group ? (uint32_t)__builtin_ctz(a.xcd_group) : 0u;
+        a.xcd_full = a.xcd_group ? (uint32_t)(s.blocks >> (a.xcd_lg + 3) << (a.xcd_lg + 3)) : 0u;
         a.store_device = store_device_for(key, a);
         const hipError_t e = launch(key, s, a, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return fail(QKROPE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));

@@ -45,6 +45,8 @@ struct KernelArgs {
 
     int64_t num_tokens;        // tokens; the grid has one workgroup per token (per 2 with TPW 2)
     uint32_t xcd_group;        // 0: block b takes token block b; G > 0 (a power of two): XCD runs
+    uint32_t xcd_lg;           // log2 G (0 when off)
+    uint32_t xcd_full;         // blocks below this (whole runs of 8G) are renumbered; 0 when off
     uint32_t store_device;     // 1: streamed stores at device scope (large launches), 0: nt only
     int head_dim;              // D
     int rotary_dim;            // R (== D for the 3D form)

@@ -404,14 +404,22 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     // Workgroups are dealt to the 8 XCDs round-robin (block b to XCD b % 8). With xcd_group G
     // (a power of two), XCD x takes runs of G consecutive blocks instead of every 8th block, so a
     // page of the streams is touched by one XCD's translation caches, not all eight; blocks past
-    // the last whole run of 8G keep their own index. Uniform, so scalar shifts and masks.
+    // the last whole run of 8G (xcd_full, 0 when off) keep their own index. Uniform, so scalar
+    // shifts and masks, and branch-free, so the scalar loads of every argument the first data
+    // loads need issue together at the start instead of one round trip after another.
+    // Every argument the first data loads depend on, taken by an empty asm statement at the
+    // start: the compiler then fetches them in one batch of scalar loads, one round trip, where
+    // it otherwise spread them over two or three dependent ones between the block renumbering
+    // and the first data load.
+    asm volatile("" ::"s"(a.xcd_lg), "s"(a.xcd_full), "s"(a.heads[0]), "s"(a.heads[1]),
+                 "s"(a.heads[2]), "s"(a.in[0]), "s"(a.in[1]), "s"(a.in[2]), "s"(a.in_stride[0]),
+                 "s"(a.in_stride[1]), "s"(a.in_stride[2]), "s"(a.weight[0]), "s"(a.weight[1]),
+                 "s"(a.num_tokens));
     uint32_t blk = blockIdx.x;
-    if (a.xcd_group) {
-        const uint32_t lg = __builtin_ctz(a.xcd_group), full = gridDim.x >> (lg + 3) << (lg + 3);
-        if (blk < full) {
-            const uint32_t j = blk >> 3, x = blk & 7u;
-            blk = ((j >> lg) << (lg + 3)) + (x << lg) + (j & (a.xcd_group - 1));
-        }
+    {
+        const uint32_t lg = a.xcd_lg, j = blk >> 3, x = blk & 7u;
+        const uint32_t r = ((j >> lg) << (lg + 3)) + (x << lg) + (j & ((1u << lg) - 1u));
+        blk = blk < a.xcd_full ? r : blk;
     }
     // RS: this workgroup's region (uniform); blk becomes its token
     const int rs = RS ? (int)(blk % (uint32_t)NREG) : 0;
@@ -457,10 +465,16 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
         wk = ld16(a.weight[1], wo);
     }
 
-    // 3D: this lane's pair (tid < D/2) frequency in revolutions and its position axis.
+    // 3D: this lane's pair (tl < D/2) frequency in revolutions and its position axis. Vector
+    // loads complete in order, so read before the data loads the angle lanes start their sin/cos
+    // while the data is still on its way; read after them, the angles wait for every data load.
+    // Measured on MI355X: before is better where a lane loads several chunks (the 4-way
+    // head-sharded rank's apply kernel 1% slower the other way), after is better for the region
+    // split, one chunk a lane and a third of its workgroups without angles (the 122880-token
+    // YaRN workload 0.7% faster).
     float omega_rev = 0.0f;
     int axis = 0;
-    if (IS3D && tl < D / 2 && !v_wg) {
+    if (!RS && IS3D && tl < D / 2 && !v_wg) {
         omega_rev = a.omega_rev[tl];
         axis = a.axis[tl];
     }
@@ -503,6 +517,11 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
                     wa[j] = ld16(w, (ok[j] && r < 2) ? oh : 0u);
                 }
             }
+        }
+
+        if (RS && IS3D && tl < D / 2 && !v_wg) {   // the region split: after the data loads
+            omega_rev = a.omega_rev[tl];
+            axis = a.axis[tl];
         }
 
         // -- cos/sin: the table row, or the 3D angle of pair `tid` into LDS

@@ -101,12 +101,12 @@ static hipError_t rec(const char *kind, const qkrope::KernelKey &k, const qkrope
                       const qkrope::KernelArgs &a)
 {
     std::printf("launch %s threads=%d slots=%d su=%d tpw=%d split=%d blocks=%lld tpl=%d "
-                "pairing=%d norm=%d fp8=%d ntok=%lld toff=%u in0=%llu xcd=%u dev=%u\n",
+                "pairing=%d norm=%d fp8=%d ntok=%lld toff=%u in0=%llu xcd=%u xlg=%u xfull=%u dev=%u\n",
                 kind, s.threads, s.slots, (int)s.slot_uniform, s.tpw, (int)s.split,
                 (long long)s.blocks, k.head_dim_tpl, k.pairing, k.norm, (int)k.fp8,
                 (long long)a.num_tokens, a.token_offset,
                 (unsigned long long)(reinterpret_cast<uintptr_t>(a.in[0]) - g_base), a.xcd_group,
-                a.store_device);
+                a.xcd_lg, a.xcd_full, a.store_device);
     check_prologue(k, a);
     return hipSuccess;
 }
