@@ -86,12 +86,24 @@ __global__ void __launch_bounds__(64 * LT) qkrope_cam_kernel(const CamArgs a)
     const int tid = threadIdx.x;
     constexpr int NTH = 64 * LT;
 
-    // block -> (batch, head group, tile); uniform, with host-computed magic divisors
+    // Every argument the first data loads depend on, taken by an empty asm statement at the
+    // start: the compiler then fetches them in one batch of scalar loads, where it otherwise
+    // spread them over five dependent round trips between the block decomposition's steps.
+    asm volatile("" ::"s"(a.xcd_group), "s"(a.div_xcd.m), "s"(a.div_xcd.l), "s"(a.div_tiles.m),
+                 "s"(a.div_tiles.l), "s"(a.tiles_padded), "s"(a.tiles), "s"(a.div_groups.m),
+                 "s"(a.div_groups.l), "s"(a.groups), "s"(a.heads_per_group), "s"(a.heads),
+                 "s"(a.head_dim), "s"(a.num_tokens), "s"(a.in[0]), "s"(a.in[1]), "s"(a.in[2]),
+                 "s"(a.in_stride[0]), "s"(a.in_stride[1]), "s"(a.in_stride[2]), "s"(a.proj[0]),
+                 "s"(a.proj[1]), "s"(a.cos_table), "s"(a.sin_table));
+    // block -> (batch, head group, tile); uniform, with host-computed magic divisors; with
+    // xcd_group G the grid is a whole number of 8*G runs and every block is renumbered
+    // (branch-free: a select)
     uint32_t blk = blockIdx.x;
-    if (a.xcd_group) {       // the grid is a whole number of 8*G runs: every block is remapped
+    {
         const uint32_t G = a.xcd_group, j = blk >> 3, x = blk & 7u;
         const uint32_t q = fast_div(j, a.div_xcd.m, a.div_xcd.l);
-        blk = q * (8u * G) + x * G + (j - q * G);
+        const uint32_t r = q * (8u * G) + x * G + (j - q * G);
+        blk = G ? r : blk;
     }
     const uint32_t bg = fast_div(blk, a.div_tiles.m, a.div_tiles.l);
     const uint32_t tile = blk - bg * (uint32_t)a.tiles_padded;
