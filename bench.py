@@ -670,7 +670,7 @@ steps captured in a HIP graph, replayed once to warm up and once timed); the cou
 launch on the stream (per-dispatch counters do not depend on how the launch was submitted).
 
 Kernel: `{k0['Kernel_Name']}`
-(workgroup {k0['Workgroup_Size_X']}, grid {k0['Grid_Size_X']} work-items, LDS {k0['LDS_Block_Size']} B, scratch {k0['Scratch_Size']} B, {k0['VGPR_Count']} VGPRs)
+(workgroup {k0['Workgroup_Size_X']}, grid {k0['Grid_Size_X']} work-items, LDS {k0['LDS_Block_Size']} B, scratch {k0['Scratch_Size']} B)
 
 | kernel trace | value |
 |---|---|
