@@ -22,6 +22,7 @@ import os
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -312,6 +313,37 @@ def test_region_split_only_without_norm_for_16_bit_outputs_and_wide_rows(driver,
                                                                          heads):
     (l,), st = run_3d(driver, 1536, (4, 4, 96), (64, 96, 96), heads, 256, norm=norm, fp8=fp8)
     assert st == 0 and l["split"] == 0 and l["blocks"] == 1536 // l["tpw"]
+
+
+def test_xcd_renumbering_parameters_match_the_run_length(driver):
+    # the kernel renumbers blocks below xfull (whole runs of 8 * 2^xlg blocks) branch-free;
+    # the host derives both from the run length G = xcd and the launch's grid
+    launches = [run_3d(driver, 15360, (16, 24, 40), (16, 56, 56), (32, 32, 32), 128)[0][0],
+                run_3d(driver, 36960, (20, 33, 28), (16, 24, 24), (20, 20, 20), 64, interleave=0,
+                       fp8=1)[0][0],
+                run_3d(driver, 122880, (32, 48, 80), (64, 96, 96), (16, 16, 16), 256,
+                       norm=0)[0][0],
+                run_table(driver, 4096, 24, 24, 128, 128, tdt=0)[0][0],
+                run_table(driver, 100, 2, 2, 128, 128, tdt=0)[0][0]]     # 100 blocks: plain order
+    for l in launches:
+        G = l["xcd"]
+        if G == 0:
+            assert l["xlg"] == 0 and l["xfull"] == 0 and l["blocks"] < 128
+            continue
+        assert 1 << l["xlg"] == G
+        assert l["xfull"] == l["blocks"] // (8 * G) * (8 * G) and l["xfull"] > 0
+        # the renumbering (the kernel's shifts and masks): a permutation of the grid in which
+        # the hardware's XCD b % 8 gets runs of G consecutive blocks
+        lg, full = l["xlg"], l["xfull"]
+        b = np.arange(l["blocks"], dtype=np.int64)
+        j, x = b >> 3, b & 7
+        r = ((j >> lg) << (lg + 3)) + (x << lg) + (j & ((1 << lg) - 1))
+        r = np.where(b < full, r, b)
+        assert np.array_equal(np.sort(r), b)
+        # hardware block 8j + x goes to XCD x: [run][position j in the run][XCD x]
+        runs = r[: full].reshape(-1, G, 8)
+        assert (np.diff(runs, axis=1) == 1).all()
+    assert [l["xcd"] for l in launches] == [16, 16, 64, 16, 0]
 
 
 def test_store_scope_follows_the_bytes_a_launch_writes(driver):
