@@ -587,7 +587,8 @@ into another: 1 GiB read and 1 GiB written per launch.
 
 A plain streaming kernel (torch's vectorized elementwise kernel, 8-element vectors, normal loads
 and stores) on this box: a reference point for the prologue kernels, which stream with
-non-temporal loads and stores.
+non-temporal loads and stores (the stores at device scope in launches that write 128 MiB or
+more).
 
 | counter | per launch (median of {len(f['FETCH_SIZE'])}) | true | scale applied to kernel counters |
 |---|---|---|---|
