@@ -597,6 +597,41 @@ def test_graph_replay_sharded_step_and_e4m3_outputs():
             assert torch.equal(got, r), f"replay {rep}"
 
 
+@pytest.mark.timeout(600)
+def test_graph_replay_full_size_named_3d_workloads():
+    """The three large 3D workloads at full size, launched as bench.py times them: marshalled
+    once (Prepared3D, on the capture stream) and replayed from one HIP graph. Every output is
+    stored at device scope there (each launch writes 142 MB to 3 GB). Every replay, with the
+    outputs cleared eagerly in between, matches the eager launch bit for bit; the eager launch
+    itself matches the oracle at every token (tests/test_gpu_parity.py)."""
+    ws = [wl.ROPE3D_ACROSS_S15360, wl.ROPE3D_NEOX_FP8_S18480, wl.ROPE3D_YARN_S122880]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    preps, outs = [], []
+    with torch.cuda.stream(s):
+        for w in ws:
+            x = {k: _gpu(v) for k, v in wl.rope3d_inputs(w).items()}
+            o = qr.run_workload_3d(w, x["qkv"], x["q_weight"], x["k_weight"])
+            preps.append(qr.Prepared3D(w, x["qkv"], x["q_weight"], x["k_weight"], *o))
+            outs.extend(o)
+    torch.cuda.synchronize()
+    raw = [t.view(torch.uint8) for t in outs]
+    ref = [t.clone() for t in raw]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for prep in preps:
+                prep()
+    for rep in range(3):
+        for t in raw:
+            t.zero_()                             # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for w, t, r in zip([w for w in ws for _ in range(3)], raw, ref):
+            assert torch.equal(t, r), f"{w.name}, replay {rep}"
+
+
 def test_host_tensor_arguments_are_refused():
     """A host tensor among GPU ones (weights, tables, outputs, matrices) raises before launch."""
     wt = wl.TABLE_INTERLEAVED_T4096.with_(num_tokens=64)
