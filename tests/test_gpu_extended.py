@@ -632,6 +632,56 @@ def test_graph_replay_full_size_named_3d_workloads():
             assert torch.equal(t, r), f"{w.name}, replay {rep}"
 
 
+@pytest.mark.timeout(600)
+def test_graph_replay_full_size_tables_and_camera():
+    """The 32768-token table workloads and the three camera-prologue workloads at full size,
+    marshalled once (PreparedTable, PreparedCam) and replayed from one HIP graph, as bench.py
+    times them: every replay, with the outputs cleared eagerly in between, matches the eager
+    launch bit for bit (whose outputs match the oracle at every element elsewhere)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    preps, outs, names = [], [], []
+    with torch.cuda.stream(s):
+        for w in (wl.TABLE_INTERLEAVED_T32768, wl.TABLE_INTERLEAVED_T32768_F16,
+                  wl.TABLE_INTERLEAVED_T32768_E4M3):
+            g = {k: _gpu(v) for k, v in wl.table_inputs(w).items()}
+            odt = torch.float8_e4m3fn if w.out_dtype == "e4m3" else g["q"].dtype
+            qo = torch.empty(g["q"].shape, dtype=odt, device=DEV)
+            ko = torch.empty(g["k"].shape, dtype=odt, device=DEV)
+            preps.append(qr.PreparedTable(g["q"], g["k"], g["q_weight"], g["k_weight"],
+                                          g["rope_table"], w.eps, q_out=qo, k_out=ko,
+                                          rotary_dim=w.rotary_dim, interleaved=w.interleaved,
+                                          norm_mode=w.norm_mode, out_scale=w.out_scale))
+            outs += [qo, ko]
+            names += [w.name] * 2
+        for w in (wl.CAM_PREP_S18480, wl.CAM_PREP_S18432, wl.CAM_PREP_S18480_P18496):
+            g = {k: _gpu(v) for k, v in wl.cam_inputs(w).items()}
+            B, N, H, D = w.batch, w.num_tokens, w.num_heads, w.head_dim
+            o = [torch.empty((B, H, D, w.out_pitch), dtype=g["q"].dtype, device=DEV)[..., :N]
+                 for _ in range(3)]
+            infl = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+            preps.append(qr.PreparedCam(g["q"], g["k"], g["v"], g["proj_q"], g["proj_kv"],
+                                        g["rope_cos"], g["rope_sin"], w.k_scale, *o, infl))
+            outs += [*o, infl]
+            names += [w.name] * 4
+    torch.cuda.synchronize()
+    raw = [t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t for t in outs]
+    ref = [t.clone() for t in raw]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for prep in preps:
+                prep()
+    for rep in range(3):
+        for t in raw:
+            t.zero_()                             # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(names, raw, ref):
+            assert torch.equal(t, r), f"{name}, replay {rep}"
+
+
 def test_host_tensor_arguments_are_refused():
     """A host tensor among GPU ones (weights, tables, outputs, matrices) raises before launch."""
     wt = wl.TABLE_INTERLEAVED_T4096.with_(num_tokens=64)
