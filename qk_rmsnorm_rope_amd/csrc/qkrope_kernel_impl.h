@@ -411,12 +411,13 @@ __global__ void __launch_bounds__(1024) qkrope_kernel(const KernelArgs a)
     // start: the compiler then fetches them in one batch of scalar loads, one round trip, where
     // it otherwise spread them over two or three dependent ones between the block renumbering
     // and the first data load.
-    // One token per workgroup under the across-heads norm (16-bit outputs): the wave raises its
-    // issue priority until its data loads are out, so a newly started workgroup's loads go ahead
-    // of the arithmetic of workgroups past their barrier. Measured on MI355X: the 15360-token
-    // across-heads workload 122.1 -> 120.5 us per launch; the same in the FP8 NeoX (two tokens
-    // per workgroup), YaRN (region split) and E4M3 table kernels cost 2%, 1.8% and 8%.
-    constexpr bool PRIO = NORM == kNormAcross && TPW == 1 && !FP8 && !RS;
+    // 3D form, one token per workgroup under the across-heads norm (16-bit outputs): the wave
+    // raises its issue priority until its data loads are out, so a newly started workgroup's
+    // loads go ahead of the arithmetic of workgroups past their barrier. Measured on MI355X: the
+    // 15360-token across-heads workload 122.1 -> 120.5 us per launch; the same in the FP8 NeoX
+    // (two tokens per workgroup), YaRN (region split) and E4M3 table kernels cost 2%, 1.8% and
+    // 8%, and in the table form with the across-heads norm (32768 tokens) 0.5%.
+    constexpr bool PRIO = IS3D && NORM == kNormAcross && TPW == 1 && !FP8 && !RS;
     if (PRIO) __builtin_amdgcn_s_setprio(3);
     asm volatile("" ::"s"(a.xcd_lg), "s"(a.xcd_full), "s"(a.heads[0]), "s"(a.heads[1]),
                  "s"(a.heads[2]), "s"(a.in[0]), "s"(a.in[1]), "s"(a.in[2]), "s"(a.in_stride[0]),
