@@ -395,6 +395,11 @@ def test_region_split_past_one_grid_runs_as_two_launches(driver):
     assert (a["toff"], b["toff"]) == (11, 11 + per)
     assert (a["in0"], b["in0"]) == (0, per * row * 2)
     assert a["blocks"] * a["threads"] <= (1 << 32) - 1
+    # store scope and XCD runs are chosen per launch: the first writes far more than 2^27
+    # bytes, the second 3001 tokens x 80 heads x 128 x 2 bytes (61 MB)
+    assert (a["dev"], b["dev"]) == (1, 0)
+    assert a["xcd"] == b["xcd"] == 64
+    assert (a["xfull"], b["xfull"]) == (a["blocks"] // 512 * 512, b["blocks"] // 512 * 512)
 
 
 @pytest.mark.parametrize("with_table", [False, True])
