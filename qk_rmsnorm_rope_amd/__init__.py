@@ -164,6 +164,17 @@ def _same_device(device: torch.device, **tensors) -> None:
             raise ValueError(f"{name} must be a GPU tensor on {device}, got {t.device}")
 
 
+_C_INT_MIN, _C_INT_MAX = -(1 << 31), (1 << 31) - 1
+
+
+def _c_ints(**values) -> None:
+    """Arguments the C ABI takes as `int`: ctypes would truncate a larger value to its low 32
+    bits without a word (2**32 + 20 passed as 20), so each must fit before the call."""
+    for name, v in values.items():
+        if not _C_INT_MIN <= v <= _C_INT_MAX:
+            raise ValueError(f"{name} = {v} does not fit the C ABI's 32-bit int")
+
+
 def _check_weight(w, need: int, dtype, name: str) -> None:
     """A norm weight: contiguous, of `dtype`, holding at least the `need` elements the kernels
     read (the C ABI takes a bare pointer, so its length is checked here). A region that reads
@@ -324,6 +335,10 @@ def qkrope_run_3d_sharded(qkv, q_weight, k_weight, *, token_offset=0, sumsq=None
     """3D form on one shard: tokens from global index token_offset on, and (with sumsq, a
     float32 [tokens, 2] tensor of sums over every head) the across-heads norm of the whole
     row."""
+    _c_ints(ppf=ppf, pph=pph, ppw=ppw, num_frame_channels=num_frame_channels,
+            num_height_channels=num_height_channels, num_width_channels=num_width_channels,
+            num_heads_q=num_heads_q, num_heads_k=num_heads_k, num_heads_v=num_heads_v,
+            head_dim=head_dim)
     if qkv.dtype != torch.bfloat16 or not qkv.is_cuda or not qkv.is_contiguous():
         raise ValueError("qkv must be a contiguous bfloat16 GPU tensor")
     row = (num_heads_q + num_heads_k + num_heads_v) * head_dim
@@ -366,6 +381,10 @@ def qkrope_run_3d(qkv, q_weight, k_weight, *, ppf, pph, ppw, num_frame_channels,
     """3D form into caller-provided contiguous outputs. qkv is [tokens, row] with tokens a
     multiple of ppf*pph*ppw, or [batch, seq_len, row] with seq_len == ppf*pph*ppw (FlashInfer's
     parameter list: seq_len = ppf * pph * ppw)."""
+    _c_ints(ppf=ppf, pph=pph, ppw=ppw, num_frame_channels=num_frame_channels,
+            num_height_channels=num_height_channels, num_width_channels=num_width_channels,
+            num_heads_q=num_heads_q, num_heads_k=num_heads_k, num_heads_v=num_heads_v,
+            head_dim=head_dim)
     row = (num_heads_q + num_heads_k + num_heads_v) * head_dim
     if qkv.dim() not in (2, 3) or qkv.shape[-1] != row:
         raise ValueError(f"qkv must be [tokens, {row}] or [batch, seq_len, {row}]")
@@ -434,8 +453,8 @@ def fused_qk_norm_rope(q, k, q_weight, k_weight, rope_table, eps, *, head_dim=No
     try:
         return (_native_mod or native()).table(
             q, k, q_weight, k_weight, rope_table, float(eps),
-            -1 if head_dim is None else int(head_dim), -1 if rotary_dim is None else int(rotary_dim),
-            bool(interleaved))
+            None if head_dim is None else int(head_dim),
+            None if rotary_dim is None else int(rotary_dim), bool(interleaved))
     except RuntimeError as e:
         raise _device_error(e) from None
 
@@ -643,6 +662,7 @@ def qkrope_cam_prep(q, k, v, proj_q, proj_kv, rope_cos, rope_sin, k_scale, *, q_
         raise ValueError("q must be [batch, tokens, heads, head_dim]")
     shape = tuple(q.shape)
     B, N, H, D = shape
+    _c_ints(heads=H, head_dim=D)
     act = _ACT_CODES.get(q.dtype)
     if act is None or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share a bfloat16 or float16 dtype")

@@ -109,24 +109,42 @@ int64_t rows(const at::Tensor &t, int64_t heads, int64_t D, const char *name)
 
 void *ptr(const std::optional<at::Tensor> &t) { return t ? t->data_ptr() : nullptr; }
 
+std::string i128_str(__int128 v)
+{
+    if (v >= INT64_MIN && v <= INT64_MAX) return std::to_string((int64_t)v);
+    return std::to_string((double)v);
+}
+
+// An argument the C ABI takes as `int`: a larger value would reach it as its low 32 bits.
+int c_int(int64_t v, const char *name)
+{
+    if (v < INT32_MIN || v > INT32_MAX)
+        throw py::value_error(std::string(name) + " = " + std::to_string(v) +
+                              " does not fit the C ABI's 32-bit int");
+    return (int)v;
+}
+
 // fused_qk_norm_rope: per-head RMSNorm with [head_dim] weights, then RoPE from the packed
 // [tokens, rotary_dim] = [cos | sin] table (its two halves are passed as the split tables).
 py::tuple table(const at::Tensor &q, const at::Tensor &k, const std::optional<at::Tensor> &q_weight,
                 const std::optional<at::Tensor> &k_weight, const at::Tensor &rope_table,
-                double eps, int64_t head_dim, int64_t rotary_dim, bool interleaved)
+                double eps, std::optional<int64_t> head_dim, std::optional<int64_t> rotary_dim,
+                bool interleaved)
 {
+    if (head_dim) c_int(*head_dim, "head_dim");
+    if (rotary_dim) c_int(*rotary_dim, "rotary_dim");
     const int act = dtype_code(q.scalar_type());
     if ((act != QKROPE_DTYPE_BF16 && act != QKROPE_DTYPE_F16) || k.scalar_type() != q.scalar_type())
         throw py::value_error("q and k must both be bfloat16 or both float16");
     if (!q.is_cuda()) throw py::value_error("q must be a GPU tensor");
     if (!k.is_cuda()) throw py::value_error("k must be a GPU tensor");
-    const int64_t D = head_dim >= 0 ? head_dim : q.size(-1);
+    const int64_t D = head_dim ? *head_dim : q.size(-1);
     if (D <= 0) throw py::value_error("head_dim must be positive");
     const int64_t Hq = q.dim() == 3 ? q.size(1) : q.size(1) / D;
     const int64_t Hk = k.dim() == 3 ? k.size(1) : k.size(1) / D;
     const int64_t T = q.size(0);
     if (k.size(0) != T) throw py::value_error("q, k and outputs must have the same number of tokens");
-    const int64_t R = rotary_dim >= 0 ? rotary_dim : rope_table.size(-1);
+    const int64_t R = rotary_dim ? *rotary_dim : rope_table.size(-1);
     const int tdt = dtype_code(rope_table.scalar_type());
     if (tdt != QKROPE_DTYPE_F32 && tdt != act)
         throw py::value_error("cos and sin tables must both be float32 or both the activation dtype");
@@ -150,7 +168,8 @@ py::tuple table(const at::Tensor &q, const at::Tensor &k, const std::optional<at
     const void *sin = tab ? tab + (R / 2) * rope_table.element_size() : nullptr;
     const int st = qkrope_run_table_ex(
         handle_for(idx), q.data_ptr(), k.data_ptr(), ptr(q_weight), ptr(k_weight), tab, sin, tdt,
-        act, act, 1.0, eps, T, (int)Hq, (int)Hk, (int)D, (int)R, interleaved ? 1 : 0,
+        act, act, 1.0, eps, T, c_int(Hq, "num_heads_q"), c_int(Hk, "num_heads_k"),
+        c_int(D, "head_dim"), c_int(R, "rotary_dim"), interleaved ? 1 : 0,
         QKROPE_NORM_PER_HEAD, qs, ks, ts, ts, q_out.data_ptr(), k_out.data_ptr(),
         rows(q_out, Hq, D, "q_out"), rows(k_out, Hk, D, "k_out"),
         c10::hip::getCurrentHIPStream(idx).stream());
@@ -169,13 +188,21 @@ py::tuple rope3d(const at::Tensor &qkv, const std::optional<at::Tensor> &q_weigh
                  std::optional<at::Tensor> q_out, std::optional<at::Tensor> k_out,
                  std::optional<at::Tensor> v_out)
 {
-    const int64_t row = (Hq + Hk + Hv) * D;
-    if ((qkv.dim() != 2 && qkv.dim() != 3) || qkv.size(-1) != row)
-        throw py::value_error("qkv must be [tokens, " + std::to_string(row) + "] or [batch, seq_len, " +
-                              std::to_string(row) + "]");
-    if (qkv.dim() == 3 && qkv.size(1) != ppf * pph * ppw)
+    const int ippf = c_int(ppf, "ppf"), ipph = c_int(pph, "pph"), ippw = c_int(ppw, "ppw");
+    const int icf = c_int(cf, "num_frame_channels"), ich = c_int(ch, "num_height_channels"),
+              icw = c_int(cw, "num_width_channels");
+    const int iHq = c_int(Hq, "num_heads_q"), iHk = c_int(Hk, "num_heads_k"),
+              iHv = c_int(Hv, "num_heads_v"), iD = c_int(D, "head_dim");
+    // products of 32-bit values, formed in 128 bits (no overflow for any of them)
+    const __int128 row128 = (__int128)(Hq + Hk + Hv) * D;
+    const __int128 seq128 = (__int128)ppf * pph * ppw;
+    if ((qkv.dim() != 2 && qkv.dim() != 3) || (__int128)qkv.size(-1) != row128)
+        throw py::value_error("qkv must be [tokens, " + i128_str(row128) + "] or [batch, seq_len, " +
+                              i128_str(row128) + "]");
+    if (qkv.dim() == 3 && (__int128)qkv.size(1) != seq128)
         throw py::value_error("a [batch, seq_len, row] qkv needs seq_len == ppf*pph*ppw = " +
-                              std::to_string(ppf * pph * ppw) + ", got " + std::to_string(qkv.size(1)));
+                              i128_str(seq128) + ", got " + std::to_string(qkv.size(1)));
+    const int64_t row = qkv.size(-1);
     if (qkv.scalar_type() != at::kBFloat16 || !qkv.is_cuda() || !qkv.is_contiguous())
         throw py::value_error("qkv must be a contiguous bfloat16 GPU tensor");
     const int64_t T = row > 0 ? qkv.numel() / row : 0;
@@ -213,8 +240,8 @@ py::tuple rope3d(const at::Tensor &qkv, const std::optional<at::Tensor> &q_weigh
     const int idx = dev.index();
     const int st = qkrope_run_3d(
         handle_for(idx), qkv.data_ptr(), is_qk_norm ? ptr(q_weight) : nullptr,
-        is_qk_norm ? ptr(k_weight) : nullptr, T, (int)ppf, (int)pph, (int)ppw, (int)cf, (int)ch,
-        (int)cw, (int)Hq, (int)Hk, (int)Hv, (int)D, eps, base, interleave ? 1 : 0, factor, low,
+        is_qk_norm ? ptr(k_weight) : nullptr, T, ippf, ipph, ippw, icf, ich, icw, iHq, iHk, iHv,
+        iD, eps, base, interleave ? 1 : 0, factor, low,
         high, attention_factor, is_qk_norm ? 1 : 0, output_fp8 ? 1 : 0, output_quant_scale,
         v_quant_scale, q_out->data_ptr(), k_out->data_ptr(), v_out->data_ptr(),
         c10::hip::getCurrentHIPStream(idx).stream());

@@ -173,3 +173,44 @@ def test_native_marshaller_loads_and_checks_arguments_on_the_host():
                                  pph=1, ppw=4, num_frame_channels=0, num_height_channels=0,
                                  num_width_channels=64, num_heads_q=1, num_heads_k=1,
                                  num_heads_v=1, head_dim=64)
+
+
+def test_binding_refuses_ints_past_the_c_int():
+    """The C ABI takes counts and sizes as 32-bit `int`; ctypes and a C++ cast would pass only
+    the low 32 bits of a larger Python int (2**32 + 2 as 2), so every such argument is checked
+    first, in the Python functions and in the C++ marshaller of the page signatures."""
+    import torch
+    import qk_rmsnorm_rope_amd as qr
+    H, D = 2, 64
+    kw = dict(ppf=2, pph=3, ppw=4, num_frame_channels=16, num_height_channels=24,
+              num_width_channels=24, num_heads_q=H, num_heads_k=H, num_heads_v=H, head_dim=D)
+    qkv = torch.zeros((24, 3 * H * D), dtype=torch.bfloat16)
+    for name, bad in (("ppf", (1 << 32) + 2), ("pph", (1 << 32) + 3), ("ppw", -(1 << 32) + 4),
+                      ("num_frame_channels", (1 << 32) + 16), ("num_heads_v", (1 << 31))):
+        args = {**kw, name: bad}
+        with pytest.raises(ValueError, match=f"{name} = {bad} does not fit"):
+            qr.fused_qk_rmsnorm_rope(qkv, None, None, **args)
+        with pytest.raises(ValueError, match=f"{name} = {bad} does not fit"):
+            qr.qkrope_run_3d(qkv, None, None, q_out=None, k_out=None, v_out=None, **args)
+        with pytest.raises(ValueError, match=f"{name} = {bad} does not fit"):
+            qr.qkrope_run_3d_sharded(qkv, None, None, q_out=None, k_out=None, v_out=None, **args)
+    # 32-bit values whose products pass int64: refused by the shape rules, no overflow
+    big = (1 << 31) - 1
+    with pytest.raises(ValueError, match="qkv must be"):
+        qr.fused_qk_rmsnorm_rope(qkv, None, None, **{**kw, "num_heads_q": big, "num_heads_k": big,
+                                                     "num_heads_v": big, "head_dim": big})
+    with pytest.raises(ValueError, match="seq_len == ppf\\*pph\\*ppw"):
+        qr.fused_qk_rmsnorm_rope(qkv.view(1, 24, -1), None, None,
+                                 **{**kw, "ppf": big, "pph": big, "ppw": big})
+    # table form: head_dim and rotary_dim
+    q = torch.zeros((4, H, D), dtype=torch.bfloat16)
+    tab = torch.zeros((4, D), dtype=torch.float32)
+    with pytest.raises(ValueError, match="rotary_dim = 4294967360 does not fit"):
+        qr.fused_qk_norm_rope(q, q, None, None, tab, 1e-6, rotary_dim=(1 << 32) + 64)
+    with pytest.raises(ValueError, match="head_dim = -4294967232 does not fit"):
+        qr.fused_qk_norm_rope(q, q, None, None, tab, 1e-6, head_dim=-(1 << 32) + 64)
+    # camera prologue: head_dim from the tensor's shape (a zero-stride view, no storage)
+    x = torch.zeros(1, dtype=torch.bfloat16).as_strided((1, 1, 1, (1 << 31) + 64), (0, 0, 0, 0))
+    with pytest.raises(ValueError, match="head_dim = 2147483712 does not fit"):
+        qr.qkrope_cam_prep(x, x, x, proj_q=None, proj_kv=None, rope_cos=None, rope_sin=None,
+                           k_scale=1.0, q_out=None, k_out=None, v_out=None)
