@@ -8,6 +8,8 @@ inflation_sq present or not; every output element is compared at the criteria in
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,7 +23,8 @@ qr = pytest.importorskip("qk_rmsnorm_rope_amd")
 from qk_rmsnorm_rope_amd import workloads as wl  # noqa: E402
 
 DEV = "cuda"
-NCASES = 32
+# QKROPE_SWEEP_CASES runs that many cases instead (same draws, more indices)
+NCASES = int(os.environ.get("QKROPE_SWEEP_CASES", "200"))
 
 
 def draw(i):

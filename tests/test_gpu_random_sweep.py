@@ -11,6 +11,7 @@ scalar and vector table reads).
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -26,7 +27,25 @@ qr = pytest.importorskip("qk_rmsnorm_rope_amd")
 from qk_rmsnorm_rope_amd import workloads as wl  # noqa: E402
 
 DEV = "cuda"
-N3D, NTAB = 80, 96
+# cases per form; QKROPE_SWEEP_CASES runs that many of each instead (same draws, more indices)
+N3D = NTAB = int(os.environ.get("QKROPE_SWEEP_CASES", "400"))
+# 3D cases (every fourth below this) that also run as two sequence shards, checked bit for bit
+N_SHARD = 80
+
+
+def describe_mismatch(got, want, t0, label):
+    """Where two [tokens, heads, head_dim] outputs differ (tokens offset by t0), and whether
+    the difference is still there when compared again."""
+    g, wv = got.view(torch.uint8), want.view(torch.uint8)
+    d = (g != wv).nonzero().cpu()
+    toks = sorted({int(x) + t0 for x in d[:, 0]})
+    heads = sorted({int(x) for x in d[:, 1]})
+    t, h, e = (int(x) for x in d[0])
+    torch.cuda.synchronize()
+    again = torch.equal(g, wv)
+    return (f"{label}: {len(d)} bytes differ at tokens {toks[:16]} heads {heads[:24]}; first at "
+            f"token {t + t0} head {h} byte {e}: {int(g[t, h, e])} vs {int(wv[t, h, e])}; "
+            f"equal when compared again: {again}")
 
 
 def pow2_on_even(i, v):
@@ -75,7 +94,7 @@ def test_random_3d(i):
     ref = oracle.run_3d_workload(w, inp["qkv"].reshape(-1, w.row_elems), inp["q_weight"],
                                  inp["k_weight"])
     check_3d_outputs(w, outs, ref)
-    if i % 4 == 0 and w.num_tokens > 2:
+    if i % 4 == 0 and i < N_SHARD and w.num_tokens > 2:
         # the same tokens as two sequence shards give the same bits
         rng = np.random.default_rng(9200 + i)
         cut = int(rng.integers(1, w.num_tokens))
@@ -97,7 +116,8 @@ def test_random_3d(i):
             torch.cuda.synchronize()
             for r in range(3):
                 full = outs[r].reshape(w.num_tokens, -1, w.head_dim)[a:b]
-                assert torch.equal(o[r].view(torch.uint8), full.view(torch.uint8)), (a, b, r)
+                assert torch.equal(o[r].view(torch.uint8), full.view(torch.uint8)), \
+                    describe_mismatch(o[r], full, a, (a, b, r))
 
 
 def draw_table(i):
