@@ -6,7 +6,8 @@ any difference between two launches would mean a race, a read of memory no lane 
 missing wait; the parity tests compare against the oracle within a tolerance and would not see a
 difference of an ulp between launches. Shapes: the two large across-heads 3D workloads at full
 size (one and two tokens per workgroup, bf16 and E4M3 outputs), a 13-wave mixed-slot 3D shape
-with NeoX pairs (10/17/22 heads of 128), and the 4096-token table form.
+with NeoX pairs (10/17/22 heads of 128), the 4096-token table form, the camera prologue at full
+size, and one rank's two-kernel step of a head-sharded run.
 """
 from __future__ import annotations
 
@@ -63,3 +64,26 @@ def test_table_launches_repeat_bit_for_bit():
                             interleaved=w.interleaved, norm_mode=w.norm_mode,
                             out_scale=w.out_scale)
     _repeat(call, [qo, ko], 1000)
+
+
+def test_camera_prologue_launches_repeat_bit_for_bit():
+    w = wl.WORKLOADS["cam_prep_b2_s18480_h20_d64"]
+    g = {k: v.to(DEV) for k, v in wl.cam_inputs(w).items()}
+    B, N, H, D = w.batch, w.num_tokens, w.num_heads, w.head_dim
+    outs = [torch.empty((B, H, D, N), dtype=g["q"].dtype, device=DEV) for _ in range(3)]
+    infl = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    call = qr.PreparedCam(g["q"], g["k"], g["v"], g["proj_q"], g["proj_kv"], g["rope_cos"],
+                          g["rope_sin"], w.k_scale, *outs, infl)
+    _repeat(call, outs + [infl], 300)
+
+
+def test_head_sharded_step_repeats_bit_for_bit():
+    """The two-kernel step of one head shard: per-token sums of squares, then the apply kernel
+    normalising with them (sums and outputs both compared)."""
+    w = wl.WORKLOADS["rope3d_across_interleaved_s15360_h32_d128_tp4rank"]
+    g = {k: v.to(DEV) for k, v in wl.rope3d_inputs(w).items()}
+    outs = [torch.empty((w.num_tokens, h, w.head_dim), dtype=torch.bfloat16, device=DEV)
+            for h in (w.num_heads_q, w.num_heads_k, w.num_heads_v)]
+    ss = torch.empty((w.num_tokens, 2), dtype=torch.float32, device=DEV)
+    call = qr.PreparedSharded3D(w, g["qkv"], g["q_weight"], g["k_weight"], *outs, ss, ss)
+    _repeat(call, outs + [ss], 300)
