@@ -12,7 +12,9 @@ The default workload is the largest one that fits one GPU: 122880 tokens of pack
 and in the same JSON line under "also_timed", the two other workloads held to the bandwidth
 target are timed the same way: the 15360-token, 32-head, head_dim-128 3D problem with
 across-heads norm (LTX-2's video self-attention shape) and the 2 x 18480-token, 20-head,
-head_dim-64 NeoX problem with E4M3 outputs (SANA-WM's grid). Inputs are seeded synthetic bf16
+head_dim-64 NeoX problem with E4M3 outputs (SANA-WM's grid); so is the SANA-WM camera prologue
+on that grid (2 x 18480 tokens, 20 heads of 64, outputs transposed to [B, H, D, N]). Inputs are
+seeded synthetic bf16
 drawn by qk_rmsnorm_rope_amd.workloads, resident in HBM before timing.
 Prints one JSON line with tokens/s, the HBM roofline of the kernel and a CPU baseline (the fp64
 oracle on a bounded sample of the headline workload).
@@ -44,8 +46,10 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 COLD_BYTES = 512 << 20         # --cold: rotating buffer sets total at least twice the MALL
 DEFAULT_WORKLOAD = "rope3d_yarn_nonorm_s122880_h16_d256"
-# timed after the default workload, in the same run, as sub-records of its JSON line
-ALSO_TIMED = ("rope3d_across_interleaved_s15360_h32_d128", "rope3d_neox_fp8_b2_s18480_h20_d64")
+# timed after the default workload, in the same run, as sub-records of its JSON line: the two
+# other 3D workloads held to the bandwidth target, and the SANA-WM camera prologue
+ALSO_TIMED = ("rope3d_across_interleaved_s15360_h32_d128", "rope3d_neox_fp8_b2_s18480_h20_d64",
+              "cam_prep_b2_s18480_h20_d64")
 _CSRC = "qk_rmsnorm_rope_amd/csrc/"
 # build.py holds the compile flags; the per-variant .hip files choose the instantiations
 COMMON_SOURCES = [_CSRC + "qkrope_kernel_impl.h", _CSRC + "qkrope_internal.h",

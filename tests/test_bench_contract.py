@@ -24,13 +24,14 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in r.stdout + r.stderr
 
 
-def test_headline_is_the_largest_single_gpu_3d_workload_with_configs_3_and_4_beside_it():
+def test_headline_is_the_largest_single_gpu_3d_workload_with_configs_3_and_4_and_the_camera_beside_it():
     named_3d = [w for w in wl.WORKLOADS.values()
                 if bench.is_3d(w) and not bench.is_sharded(w) and not bench.is_cam(w)]
     largest = max(named_3d, key=bench.algorithmic_bytes)
     assert bench.DEFAULT_WORKLOAD == largest.name == "rope3d_yarn_nonorm_s122880_h16_d256"
     assert set(bench.ALSO_TIMED) == {"rope3d_across_interleaved_s15360_h32_d128",
-                                     "rope3d_neox_fp8_b2_s18480_h20_d64"}
+                                     "rope3d_neox_fp8_b2_s18480_h20_d64",
+                                     "cam_prep_b2_s18480_h20_d64"}
 
 
 @pytest.mark.parametrize("name", [bench.DEFAULT_WORKLOAD, *bench.ALSO_TIMED])
@@ -46,4 +47,6 @@ def test_roofline_fields_and_arithmetic(name):
     text = open(os.path.join(ROOT, "profiles", f"counters_{name}.md"), encoding="utf-8").read()
     rec = json.loads(re.search(r"<!-- traffic (\{.*\}) -->", text).group(1))
     assert r["traffic"] == rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
-    assert abs(r["traffic"] / r["algorithmic_bytes"] - 1) < 0.01
+    # the camera prologue's head groups re-read their tokens' matrices and table rows: 2% more
+    # reads than its algorithmic bytes (one pass) on the contiguous layout
+    assert abs(r["traffic"] / r["algorithmic_bytes"] - 1) < (0.03 if bench.is_cam(w) else 0.01)
